@@ -1,0 +1,73 @@
+"""The QLoRA linear layer, forward and backward, in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Pages: Mathematical Formulation and Figure 1 of "DL0087 QLoRA" (output and
+input stay 16-bit; the frozen base is dequantized to a bf16 tile for the
+matmul; trainable bf16 adapters of rank r, scaled; the adapter that starts at
+zero makes the layer reproduce the quantized base), list item (4) of the same
+page and "The Efficient Symphony of the QLoRA Workflow" of "QLoRA (Quantized
+Low-Rank Adaptation)" (gradients pass through the frozen 4-bit weights into
+the adapters; the base is never updated).
+
+The formula itself was lost from the Mathematical Formulation when the page
+was extracted; the reading rebuilt from its bullets is
+
+    Y = X . W_hat_lin^T + s . (X . A) . B
+
+with X [M, K], W_hat_lin [N, K] (the dequantized bf16 base, out x in),
+A [K, r], B [r, N], s the LoRA scale (alpha / r), Y [M, N].  The backward of
+L with dL/dY = dY is
+
+    G  = dY . B^T                       [M, r]
+    dX = dY . W_hat_lin + s . G . A^T   [M, K]
+    dA = s . X^T . G                    [K, r]
+    dB = s . (X . A)^T . dY             [r, N]
+
+and there is no gradient for the base weight or its constants.
+Products are exact-input float64 matmuls; no intermediate is rounded.
+"""
+import numpy as np
+
+from .nf4 import bf16_bits_to_f64
+
+
+def linear_fwd_f64(X, W, A, B, s):
+    """Forward on float64 operands. Returns (Y, T) with T = X . A."""
+    X, W, A, B = (np.asarray(a, dtype=np.float64) for a in (X, W, A, B))
+    T = X @ A
+    Y = X @ W.T + float(s) * (T @ B)
+    return Y, T
+
+
+def linear_bwd_f64(dY, X, W, A, B, s):
+    """Backward on float64 operands. Returns (dX, dA, dB)."""
+    dY, X, W, A, B = (np.asarray(a, dtype=np.float64) for a in (dY, X, W, A, B))
+    s = float(s)
+    G = dY @ B.T
+    dX = dY @ W + s * (G @ A.T)
+    dA = s * (X.T @ G)
+    dB = s * ((X @ A).T @ dY)
+    return dX, dA, dB
+
+
+def linear_fwd(X_bits, W_bits, A_bits, B_bits, s):
+    """Forward from bf16 bit patterns (uint16 arrays); float64 results."""
+    return linear_fwd_f64(bf16_bits_to_f64(X_bits), bf16_bits_to_f64(W_bits),
+                          bf16_bits_to_f64(A_bits), bf16_bits_to_f64(B_bits), s)
+
+
+def linear_bwd(dY_bits, X_bits, W_bits, A_bits, B_bits, s):
+    """Backward from bf16 bit patterns (uint16 arrays); float64 results."""
+    return linear_bwd_f64(bf16_bits_to_f64(dY_bits), bf16_bits_to_f64(X_bits),
+                          bf16_bits_to_f64(W_bits), bf16_bits_to_f64(A_bits),
+                          bf16_bits_to_f64(B_bits), s)
+
+
+def linear_flops(M, N, K, r):
+    """Algorithmic flops of one forward + backward: 4MKN + 6Mr(K+N).
+
+    Forward: X.W^T (2MKN), X.A (2MKr), T.B (2MrN).  Backward: dY.W (2MKN),
+    dY.B^T (2MNr), G.A^T (2MrK), X^T.G (2MKr), T^T.dY (2MrN).
+    """
+    return 4 * M * K * N + 6 * M * r * (K + N)

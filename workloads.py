@@ -1,0 +1,127 @@
+"""Seeded synthetic workloads for the QLoRA NF4 linear layer.
+
+This module only draws random inputs; it holds none of the method's
+arithmetic.  Both the oracle-side tests and the GPU-side tests and benchmark
+take their inputs from here, so both sides see the same bytes.
+
+Recipe (stated once, used everywhere):
+  * config i draws from numpy.random.default_rng(seed) with seed = i unless
+    a test picks another seed;
+  * per linear, in the order q, k, v, o, gate, up, down, the draws are:
+      W   float32 [N, K], standard normal x 0.02
+      an outlier mask, uniform(0,1) < 0.001, and W *= 10 on the mask
+      X   [M, K] standard normal, rounded to bf16
+      A   [K, r] normal with standard deviation 1/r, rounded to bf16
+      B   [r, N] normal with standard deviation b_std (0.01), rounded to bf16
+      dY  [M, N] standard normal, rounded to bf16
+  * bf16 rounding is torch's float32 -> bfloat16 conversion on the CPU
+    (round to nearest even); tensors travel as uint16 bit patterns.
+
+The shapes stand in for LLaMA-7B, -33B and -65B linear layers (the pages'
+models), with token counts from the batch and sequence sizes the pages quote.
+"""
+from dataclasses import dataclass, field
+from typing import List, Tuple
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Linear:
+    name: str
+    N: int   # out features (rows of W_lin)
+    K: int   # in features
+
+
+@dataclass(frozen=True)
+class Config:
+    idx: int
+    name: str
+    linears: Tuple[Linear, ...]
+    M: Tuple[int, ...]
+    r: int
+    alpha: float
+    note: str = ""
+
+    @property
+    def s(self) -> float:
+        return self.alpha / self.r if self.r else 0.0
+
+
+def _llama_layer(hidden: int, ffn: int) -> Tuple[Linear, ...]:
+    return (Linear("q", hidden, hidden), Linear("k", hidden, hidden),
+            Linear("v", hidden, hidden), Linear("o", hidden, hidden),
+            Linear("gate", ffn, hidden), Linear("up", ffn, hidden),
+            Linear("down", hidden, ffn))
+
+
+CONFIGS = {
+    0: Config(0, "single linear 1024x1024, M=16, r=16 (parity case)",
+              (Linear("w", 1024, 1024),), (16,), 16, 16.0),
+    1: Config(1, "LLaMA-7B layer linears, M=2048 tokens, r=64",
+              _llama_layer(4096, 11008), (2048,), 64, 16.0),
+    2: Config(2, "65B-shaped decode sweep, M in {1,4,16}, r=64",
+              (Linear("qkvo", 8192, 8192), Linear("up", 22016, 8192),
+               Linear("down", 8192, 22016)), (1, 4, 16), 64, 16.0,
+              "alpha not given for this sweep; alpha=16 assumed (s=0.25)"),
+    3: Config(3, "33B-shaped layer linears, M=4096 tokens, r=64, recompute bwd",
+              _llama_layer(6656, 17920), (4096,), 64, 16.0),
+    4: Config(4, "65B-shaped stack, 80 layers x 7 linears, M=2048, r=64",
+              _llama_layer(8192, 22016) * 80, (2048,), 64, 16.0),
+}
+
+
+def to_bf16_bits(a) -> np.ndarray:
+    """float32 -> bf16 bit patterns via torch's CPU conversion (RNE)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def draw_weight(rng, N: int, K: int) -> np.ndarray:
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    mask = rng.random((N, K)) < 0.001
+    W[mask] *= np.float32(10.0)
+    return W
+
+
+@dataclass
+class LinearInputs:
+    W: np.ndarray            # float32 [N, K]
+    X: np.ndarray            # bf16 bits [M, K]
+    A: np.ndarray            # bf16 bits [K, r]
+    B: np.ndarray            # bf16 bits [r, N]
+    dY: np.ndarray = None    # bf16 bits [M, N]
+    extra: dict = field(default_factory=dict)
+
+
+def draw_linear(rng, N: int, K: int, M: int, r: int, b_std: float = 0.01,
+                with_grad: bool = True) -> LinearInputs:
+    W = draw_weight(rng, N, K)
+    X = to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    a_std = np.float32(1.0 / r) if r else np.float32(0.0)
+    A = to_bf16_bits(rng.standard_normal((K, r), dtype=np.float32) * a_std)
+    B = to_bf16_bits(rng.standard_normal((r, N), dtype=np.float32) * np.float32(b_std))
+    dY = (to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32))
+          if with_grad else None)
+    return LinearInputs(W, X, A, B, dY)
+
+
+def config_inputs(cfg_idx: int, M: int = None, seed: int = None,
+                  linears: List[int] = None, with_grad: bool = True):
+    """Yield (Linear, LinearInputs) for the linears of a config, in order.
+
+    All linears are drawn in sequence from one generator, so asking for a
+    subset still yields the same bytes as the full config for those linears.
+    """
+    cfg = CONFIGS[cfg_idx]
+    rng = np.random.default_rng(cfg_idx if seed is None else seed)
+    m = cfg.M[0] if M is None else M
+    want = set(range(len(cfg.linears))) if linears is None else set(linears)
+    last = max(want) if want else -1
+    for i, lin in enumerate(cfg.linears):
+        if i > last:
+            break
+        inp = draw_linear(rng, lin.N, lin.K, m, cfg.r, with_grad=with_grad)
+        if i in want:
+            yield lin, inp
