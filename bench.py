@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA NF4 linear layer on one MI355X.
+
+Headline: fwd+bwd TFLOP/s of the seven LLaMA-7B-shaped linears (q, k, v, o
+[4096x4096], gate, up [11008x4096], down [4096x11008]) at M = 2048 tokens,
+rank 64, s = 0.25.  One step = forward (Y, T) and backward (dX, dA, dB) of
+all seven on one batch; the NF4 base is quantized once at load, outside the
+step, because the base is frozen.  Algorithmic flops per linear:
+4MKN + 6Mr(K+N); dequantization and recomputation are not counted.
+
+Second figure: decode (M = 1) effective HBM GB/s on the 65B shapes, with a
+pool of weight copies over 1 GB per shape so the 256 MB last-level cache
+cannot serve them.
+
+Prints one JSON line (the last line of stdout).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA linear fwd+bwd TFLOP/s at M=2048; decode (M=1) effective HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+FAMILIES = {0: "k_fwd_gemm", 1: "k_dx_gemm", 2: "k_fwd_decode", 3: "k_quantize", 4: "rank"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_quantized_fine_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, src_hash):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("src_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def bf16_dev(bits, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def run_training(q, torch, steps, warmup, dev):
+    import numpy as np
+
+    import workloads
+    import oracle
+    cfg = workloads.CONFIGS[1]
+    M, r, s = cfg.M[0], cfg.r, cfg.s
+    layers = []
+    t0 = time.time()
+    for lin, inp in workloads.config_inputs(1):
+        w = q.qlora_nf4_quantize(torch.from_numpy(inp.W).to(dev))
+        L = dict(lin=lin, w=w, X=bf16_dev(inp.X, dev), A=bf16_dev(inp.A, dev),
+                 B=bf16_dev(inp.B, dev), dY=bf16_dev(inp.dY, dev))
+        L["Y"] = torch.empty((M, lin.N), dtype=torch.bfloat16, device=dev)
+        L["T"] = torch.empty((M, r), dtype=torch.float32, device=dev)
+        L["dX"] = torch.empty((M, lin.K), dtype=torch.bfloat16, device=dev)
+        L["dA"] = torch.empty((lin.K, r), dtype=torch.bfloat16, device=dev)
+        L["dB"] = torch.empty((r, lin.N), dtype=torch.bfloat16, device=dev)
+        L["wsf"] = torch.empty(q.lib().qlora_linear_fwd_workspace_bytes(M, lin.N, lin.K, r),
+                               dtype=torch.uint8, device=dev)
+        L["wsb"] = torch.empty(q.lib().qlora_linear_bwd_workspace_bytes(M, lin.N, lin.K, r),
+                               dtype=torch.uint8, device=dev)
+        layers.append(L)
+    torch.cuda.synchronize()
+    log(f"setup (draw + upload + quantize 7 linears): {time.time() - t0:.1f}s")
+
+    def step():
+        for L in layers:
+            q.qlora_linear_fwd(L["X"], L["w"], L["A"], L["B"], s, Y=L["Y"], T=L["T"],
+                               workspace=L["wsf"])
+            q.qlora_linear_bwd(L["dY"], L["X"], L["w"], L["A"], L["B"], s, T=L["T"],
+                               dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["wsb"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    q.qlora_profile_reset()
+    q.qlora_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    q.qlora_profile_enable(False)
+    ms_step = (t1 - t0) * 1e3 / steps
+    fam = {FAMILIES[f]: q.qlora_profile_read(f) for f in FAMILIES}
+
+    flops_step = sum(oracle.linear_flops(M, L["lin"].N, L["lin"].K, r) for L in layers)
+    fwd_flops = sum(2 * M * L["lin"].K * L["lin"].N + 2 * M * r * L["lin"].N for L in layers)
+    dx_flops = sum(2 * M * L["lin"].K * L["lin"].N + 2 * M * r * L["lin"].K for L in layers)
+    return dict(layers=layers, M=M, r=r, s=s, ms_step=ms_step, flops_step=flops_step,
+                fam=fam, fwd_flops=fwd_flops, dx_flops=dx_flops, cfg=cfg)
+
+
+def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
+    """Decode GB/s on the 65B shapes, rotating over >1 GB of weight copies."""
+    import workloads
+    cfg = workloads.CONFIGS[2]
+    r, s = cfg.r, cfg.s
+    g = torch.Generator(device=dev)
+    g.manual_seed(2000)
+    out = {}
+    for M in cfg.M:
+        tot_bytes, tot_ms, kern_ms, kern_n = 0.0, 0.0, 0.0, 0
+        per_shape = {}
+        for lin in cfg.linears:
+            N, K = lin.N, lin.K
+            nf4_bytes = N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256)
+            copies = max(2, int(pool_bytes // nf4_bytes) + 1)
+            pool = []
+            for _ in range(copies):
+                W = torch.randn((N, K), generator=g, device=dev) * 0.02
+                W = torch.where(torch.rand((N, K), generator=g, device=dev) < 0.001, W * 10, W)
+                pool.append(q.qlora_nf4_quantize(W))
+                del W
+            X = (torch.randn((M, K), generator=g, device=dev)).to(torch.bfloat16)
+            A = (torch.randn((K, r), generator=g, device=dev) / r).to(torch.bfloat16)
+            B = (torch.randn((r, N), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            T = torch.empty((M, r), dtype=torch.float32, device=dev)
+            ws = torch.empty(q.lib().qlora_linear_fwd_workspace_bytes(M, N, K, r),
+                             dtype=torch.uint8, device=dev)
+            for w in pool[:2]:
+                q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
+            torch.cuda.synchronize()
+            q.qlora_profile_reset()
+            q.qlora_profile_enable(True)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            calls = 0
+            for _ in range(reps):
+                for w in pool:
+                    q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
+                    calls += 1
+            ev1.record()
+            torch.cuda.synchronize()
+            q.qlora_profile_enable(False)
+            ms = ev0.elapsed_time(ev1)
+            kms, kn = q.qlora_profile_read(2)
+            alg = nf4_bytes + 2 * (M * K + M * N + K * r + r * N)
+            per_shape[f"{N}x{K}"] = dict(us_per_call=1e3 * ms / calls,
+                                         gbs_call=alg * calls / (ms * 1e-3) / 1e9,
+                                         us_decode_kernel=1e3 * kms / max(1, kn),
+                                         gbs_decode_kernel=alg * kn / (kms * 1e-3) / 1e9,
+                                         copies=copies)
+            tot_bytes += alg * calls
+            tot_ms += ms
+            kern_ms += kms
+            kern_n += kn
+            del pool
+            torch.cuda.empty_cache()
+        out[f"M={M}"] = dict(gbs_call=tot_bytes / (tot_ms * 1e-3) / 1e9,
+                             gbs_decode_kernel=tot_bytes / (kern_ms * 1e-3) / 1e9,
+                             shapes=per_shape)
+        log(f"decode M={M}: {out[f'M={M}']['gbs_call']:.0f} GB/s per call, "
+            f"{out[f'M={M}']['gbs_decode_kernel']:.0f} GB/s decode kernel")
+    return out
+
+
+def run_cpu_baseline(train):
+    """The oracle (dequantize + forward + backward, float64 products) on a
+    bounded sample of the same workload: the q and gate linears of the seven,
+    full M, on this host's cores."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_info = threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    cfg = workloads.CONFIGS[1]
+    flops, secs = 0, 0.0
+    ctx = threadpool_limits(cores) if threadpool_limits else None
+    try:
+        for idx in (0, 4):
+            (lin, inp), = list(workloads.config_inputs(1, linears=[idx]))
+            codes, e, d, _ = oracle.quantize(inp.W)       # load-time, untimed
+            t0 = time.perf_counter()
+            What = oracle.dequantize(codes, e, d, lin.N, lin.K)
+            oracle.linear_fwd(inp.X, What, inp.A, inp.B, cfg.s)
+            oracle.linear_bwd(inp.dY, inp.X, What, inp.A, inp.B, cfg.s)
+            secs += time.perf_counter() - t0
+            flops += oracle.linear_flops(cfg.M[0], lin.N, lin.K, cfg.r)
+        threads = cores
+        if threadpool_info:
+            nums = [p.get("num_threads", 0) for p in threadpool_info()
+                    if p.get("user_api") == "blas"]
+            threads = max(nums) if nums else cores
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return dict(value=flops / secs / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                seconds=secs,
+                sample="linears q [4096x4096] and gate [11008x4096] of the seven, M=2048, "
+                       "r=64: oracle dequantize + fwd + bwd (float64 products), "
+                       "quantization untimed")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_fine_amd as q
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    q.lib()
+
+    tr = run_training(q, torch, args.steps, args.warmup, dev)
+    value = tr["flops_step"] / (tr["ms_step"] * 1e-3) / 1e12
+    log(f"train step: {tr['ms_step']:.3f} ms, {value:.1f} TFLOP/s; kernels: {tr['fam']}")
+
+    fwd_ms, fwd_n = tr["fam"]["k_fwd_gemm"]
+    dx_ms, dx_n = tr["fam"]["k_dx_gemm"]
+    if fwd_ms >= dx_ms:
+        kern, kms, kn, kflops = "k_fwd_gemm", fwd_ms, fwd_n, tr["fwd_flops"]
+    else:
+        kern, kms, kn, kflops = "k_dx_gemm", dx_ms, dx_n, tr["dx_flops"]
+    steps_timed = args.steps
+    achieved = kflops * steps_timed / (kms * 1e-3) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = stored_traffic(kern, src_hash)
+    roofline = dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic, kernel=kern,
+                    avg_launch_us=1e3 * kms / max(1, kn),
+                    flops_per_launch=kflops / len(tr["layers"]), src_hash=src_hash)
+
+    kernels = {}
+    for name, (ms, n) in tr["fam"].items():
+        if n:
+            kernels[name] = dict(ms_per_step=ms / steps_timed, launches_per_step=n / steps_timed,
+                                 avg_launch_us=1e3 * ms / n)
+
+    decode = None
+    if not args.no_decode:
+        decode = run_decode(q, torch, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_baseline(tr)
+        log(f"cpu baseline: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
+
+    cfg = tr["cfg"]
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": tr["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "LLaMA-7B-shaped QLoRA linears q,k,v,o [4096x4096], gate,up "
+                        "[11008x4096], down [4096x11008]; NF4 base (block 64, DQ 256); "
+                        "fwd + bwd (dX, dA, dB)",
+            "global_batch": cfg.M[0], "seq_len": 512, "batch": 4, "tokens": cfg.M[0],
+            "rank": cfg.r, "lora_scale": cfg.s, "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode_m1_gbs": None if decode is None else decode["M=1"]["gbs_call"],
+        "decode": decode,
+        "kernels": kernels,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

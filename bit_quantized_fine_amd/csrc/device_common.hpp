@@ -1,0 +1,132 @@
+// Device-side building blocks shared by the gfx950 kernels of the QLoRA NF4
+// linear layer: vector types, bf16 packing, the NF4 byte-pair lookup table
+// and the 16x16x32 bf16 MFMA wrapper.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qnf4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// The 16 NF4 levels and the 15 nearest-level decision thresholds, passed to
+// kernels by value (they land in scalar registers / the kernarg segment).
+struct Nf4Tables {
+  float q[16];
+  float t[15];
+};
+
+constexpr int kBlock = 64;    // weights per absmax constant
+constexpr int kGroup = 256;   // constants per fp32 second-level scale
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+// `a` lands in the low half (the lower-addressed element).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 h = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t packed) {
+  return __builtin_bit_cast(float, packed << 16);
+}
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t packed) {
+  return __builtin_bit_cast(float, packed & 0xFFFF0000u);
+}
+
+// Split fp32 values a, b into bf16 hi parts and bf16 lo parts (v - hi),
+// so that hi + lo carries ~16 significant bits of v.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi,
+                                             uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - bf16_lo_to_f32(hi), b - bf16_hi_to_f32(hi));
+}
+
+// Byte-pair lookup table of NF4 levels in LDS: entry b holds
+// (level[b & 15], level[b >> 4]), i.e. the two weights a packed code byte
+// encodes, even element first.  256 entries x 8 bytes = 2 KB.
+__device__ __forceinline__ void build_pair_table(float2* tab, const Nf4Tables& tb,
+                                                 int tid, int nthreads) {
+  for (int b = tid; b < 256; b += nthreads) {
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      lo = ((b & 15) == j) ? tb.q[j] : lo;
+      hi = ((b >> 4) == j) ? tb.q[j] : hi;
+    }
+    tab[b] = make_float2(lo, hi);
+  }
+}
+
+// Dequantize the 8 codes of one 32-bit word (4 bytes, elements in order) with
+// block constant c_hat: bf16_rne(fl32(level[code] * c_hat)), packed as 8
+// consecutive bf16 (4 dwords).
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, float c_hat,
+                                          const float2* tab) {
+  const float2 p0 = tab[w & 0xFFu];
+  const float2 p1 = tab[(w >> 8) & 0xFFu];
+  const float2 p2 = tab[(w >> 16) & 0xFFu];
+  const float2 p3 = tab[w >> 24];
+  u32x4 o;
+  o.x = pack_bf16x2(p0.x * c_hat, p0.y * c_hat);
+  o.y = pack_bf16x2(p1.x * c_hat, p1.y * c_hat);
+  o.z = pack_bf16x2(p2.x * c_hat, p2.y * c_hat);
+  o.w = pack_bf16x2(p3.x * c_hat, p3.y * c_hat);
+  return o;
+}
+
+// Same, but keeps the fp32 products (used by the transposing loader, which
+// packs pairs across rows instead of along the row).
+__device__ __forceinline__ void dequant8_f32(uint32_t w, float c_hat,
+                                             const float2* tab, float* v) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float2 p = tab[(w >> (8 * b)) & 0xFFu];
+    v[2 * b] = p.x * c_hat;
+    v[2 * b + 1] = p.y * c_hat;
+  }
+}
+
+// Block constant c_hat = fl32(e * d).
+__device__ __forceinline__ float block_scale(const uint8_t* absmax_q,
+                                             const float* absmax_scale,
+                                             int64_t block) {
+  return static_cast<float>(absmax_q[block]) * absmax_scale[block >> 8];
+}
+
+// D += A . B for one 16x16x32 bf16 MFMA.  Lane l supplies row (l % 16) of A
+// and column (l % 16) of B, each with the 8 reduction elements 8*(l/16)..+7;
+// lane l receives D rows 4*(l/16)..+3 of column l % 16.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// v_perm_b32 selector patterns for building bf16 pairs from two dwords.
+// perm(hi_src, lo_src, sel): bytes 0-3 index lo_src, 4-7 index hi_src.
+constexpr uint32_t kSelLoHalves = 0x05040100u;   // lo16(lo_src) | lo16(hi_src)<<16
+constexpr uint32_t kSelHiHalves = 0x07060302u;   // hi16(lo_src) | hi16(hi_src)<<16
+
+// Transpose an 8x8 tile of 16-bit elements held as 8 rows of 4 dwords.
+// in[i] = row i (elements (i,0..7)); out[j] = column j (elements (0..7,j)).
+__device__ __forceinline__ void transpose8x8_b16(const u32x4* in, u32x4* out) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = j >> 1;
+    const uint32_t sel = (j & 1) ? kSelHiHalves : kSelLoHalves;
+    uint32_t d[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      d[q] = __builtin_amdgcn_perm(in[2 * q + 1][p], in[2 * q][p], sel);
+    }
+    out[j] = u32x4{d[0], d[1], d[2], d[3]};
+  }
+}
+
+}  // namespace qnf4

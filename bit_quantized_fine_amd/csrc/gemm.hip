@@ -1,0 +1,664 @@
+// MFMA GEMMs of the QLoRA NF4 linear layer on gfx950.
+//
+// Every product here has the form C[q, p] = sum_k P[p, k] . Q[q, k]: the
+// workgroup stages a P tile [BP x 64] and a Q tile [BQ x 64] in LDS, both
+// laid out reduction-contiguous ("MFMA ready": a lane's 8 reduction elements
+// are one 16-byte LDS read), and four waves (2 x 2) accumulate their
+// (BP/2 x BQ/2) share with v_mfma_f32_16x16x32_bf16.  Loaders bring each
+// operand into that layout whatever its layout in HBM:
+//   Bf16Nat  bf16 rows, reduction contiguous          (X, dY, B as [r,N], A as [K,r])
+//   Bf16Tr   bf16 with the reduction as the row index (X^T, dY^T, B^T)
+//   F32Nat / F32Tr  fp32 (T, G) split into bf16 hi and lo passes
+//   Nf4Nat   the NF4 weight with rows n, reduction k (forward): dequantized
+//            in registers from 16-byte code loads, written to LDS as bf16
+//   Nf4Tr    the NF4 weight with rows k, reduction n (backward dX): 8 x 8
+//            patches dequantized and packed across rows
+// The dequantization (Mathematical Formulation of "DL0087 QLoRA": a bf16 tile
+// is rebuilt just before the matmul and discarded) happens once per
+// workgroup tile; no bf16 copy of the weight ever reaches HBM.
+//
+// The fused LoRA terms are extra reduction steps over the rank dimension
+// appended to the main loop (forward: s.T.B; dX: s.G.A^T), with the fp32
+// factor split into bf16 hi + lo so the adapter term keeps ~16 bits.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace qnf4 {
+
+constexpr int BK = 64;              // reduction elements per tile
+constexpr int LDS_STRIDE = BK + 8;  // bf16 per LDS row: 144 B, spreads rows over banks
+constexpr int NT = 256;             // threads per workgroup (4 waves)
+
+struct OpParams {
+  const void* ptr;
+  int64_t ld;      // leading dimension of the source array (elements)
+  int64_t nrows;   // extent of the tile-row index
+  int64_t nred;    // extent of the reduction index
+  float scale;     // fp32 sources: value = scale * src
+  // NF4 sources
+  const uint8_t* absmax_q;
+  const float* absmax_scale;
+  int64_t N, K;
+};
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st_lds16(uint16_t* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ---------------------------------------------------------------------------
+// Loaders.  load(kt) fetches reduction tile kt into registers; store(lds)
+// writes the tile [ROWS][LDS_STRIDE] to LDS; elements outside the operand
+// are zero.
+// ---------------------------------------------------------------------------
+
+template <int ROWS>
+struct Bf16Nat {   // element (row, k) = src[row * ld + k]
+  static constexpr int CH = ROWS * BK / 8;              // 16-byte chunks
+  static constexpr int CPT = (CH + NT - 1) / NT;
+  OpParams o;
+  int64_t row0;
+  u32x4 r[CPT];
+  __device__ void load(int kt, int tid) {
+    const uint16_t* src = static_cast<const uint16_t*>(o.ptr);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      const int row = idx >> 3, kc = idx & 7;
+      const int64_t gr = row0 + row, gk = (int64_t)kt * BK + kc * 8;
+      r[c] = (idx < CH && gr < o.nrows && gk < o.nred) ? ld16(src + gr * o.ld + gk)
+                                                        : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ void store(uint16_t* lds, int tid) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      if (idx < CH) st_lds16(lds + (idx >> 3) * LDS_STRIDE + (idx & 7) * 8, r[c]);
+    }
+  }
+};
+
+template <int ROWS>
+struct Bf16Tr {    // element (row, k) = src[k * ld + row]; rows come in 8s
+  static constexpr int NP = ROWS;                 // 8x8 patches per tile
+  static constexpr int PPT = (NP + NT - 1) / NT;
+  static constexpr int RS = ROWS / 8;             // row slabs
+  OpParams o;
+  int64_t row0;
+  u32x4 r[PPT][8];
+  __device__ void load(int kt, int tid) {
+    const uint16_t* src = static_cast<const uint16_t*>(o.ptr);
+#pragma unroll
+    for (int c = 0; c < PPT; ++c) {
+      const int p = tid + c * NT;
+      const int rp = p % RS, kp = p / RS;
+      const int64_t gr = row0 + rp * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t gk = (int64_t)kt * BK + kp * 8 + i;
+        r[c][i] = (p < NP && gr < o.nrows && gk < o.nred) ? ld16(src + gk * o.ld + gr)
+                                                          : u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  __device__ void store(uint16_t* lds, int tid) {
+#pragma unroll
+    for (int c = 0; c < PPT; ++c) {
+      const int p = tid + c * NT;
+      if (p < NP) {
+        const int rp = p % RS, kp = p / RS;
+        u32x4 t[8];
+        transpose8x8_b16(r[c], t);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st_lds16(lds + (rp * 8 + j) * LDS_STRIDE + kp * 8, t[j]);
+      }
+    }
+  }
+};
+
+// fp32 -> bf16 conversion of 8 values, hi part (pass 0) or lo part (pass 1).
+__device__ __forceinline__ u32x4 f32x8_to_bf16(const f32x4& a, const f32x4& b,
+                                               float scale, int pass) {
+  const float v[8] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale,
+                      b.x * scale, b.y * scale, b.z * scale, b.w * scale};
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t hi, lo;
+    split_bf16x2(v[2 * i], v[2 * i + 1], hi, lo);
+    out[i] = pass ? lo : hi;
+  }
+  return u32x4{out[0], out[1], out[2], out[3]};
+}
+
+template <int ROWS>
+struct F32Nat {    // element (row, k) = scale * src[row * ld + k], fp32 source
+  static constexpr int CH = ROWS * BK / 8;
+  static constexpr int CPT = (CH + NT - 1) / NT;
+  OpParams o;
+  int64_t row0;
+  int pass;
+  f32x4 r[CPT][2];
+  __device__ void load(int kt, int tid) {
+    const float* src = static_cast<const float*>(o.ptr);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      const int row = idx >> 3, kc = idx & 7;
+      const int64_t gr = row0 + row, gk = (int64_t)kt * BK + kc * 8;
+      const bool ok = idx < CH && gr < o.nrows && gk < o.nred;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      r[c][0] = ok ? *reinterpret_cast<const f32x4*>(src + gr * o.ld + gk) : z;
+      r[c][1] = ok ? *reinterpret_cast<const f32x4*>(src + gr * o.ld + gk + 4) : z;
+    }
+  }
+  __device__ void store(uint16_t* lds, int tid) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      if (idx < CH)
+        st_lds16(lds + (idx >> 3) * LDS_STRIDE + (idx & 7) * 8,
+                 f32x8_to_bf16(r[c][0], r[c][1], o.scale, pass));
+    }
+  }
+};
+
+template <int ROWS>
+struct F32Tr {     // element (row, k) = scale * src[k * ld + row], fp32 source
+  static constexpr int NP = ROWS;
+  static constexpr int PPT = (NP + NT - 1) / NT;
+  static constexpr int RS = ROWS / 8;
+  OpParams o;
+  int64_t row0;
+  int pass;
+  f32x4 r[PPT][8][2];
+  __device__ void load(int kt, int tid) {
+    const float* src = static_cast<const float*>(o.ptr);
+#pragma unroll
+    for (int c = 0; c < PPT; ++c) {
+      const int p = tid + c * NT;
+      const int rp = p % RS, kp = p / RS;
+      const int64_t gr = row0 + rp * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t gk = (int64_t)kt * BK + kp * 8 + i;
+        const bool ok = p < NP && gr < o.nrows && gk < o.nred;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        r[c][i][0] = ok ? *reinterpret_cast<const f32x4*>(src + gk * o.ld + gr) : z;
+        r[c][i][1] = ok ? *reinterpret_cast<const f32x4*>(src + gk * o.ld + gr + 4) : z;
+      }
+    }
+  }
+  __device__ void store(uint16_t* lds, int tid) {
+#pragma unroll
+    for (int c = 0; c < PPT; ++c) {
+      const int p = tid + c * NT;
+      if (p < NP) {
+        const int rp = p % RS, kp = p / RS;
+        u32x4 rows[8], t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rows[i] = f32x8_to_bf16(r[c][i][0], r[c][i][1], o.scale, pass);
+        transpose8x8_b16(rows, t);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st_lds16(lds + (rp * 8 + j) * LDS_STRIDE + kp * 8, t[j]);
+      }
+    }
+  }
+};
+
+template <int ROWS>
+struct Nf4Nat {    // element (n, k) = deq(W)[n, k]; one thread = half a block
+  static constexpr int CH = ROWS * 2;
+  static constexpr int CPT = (CH + NT - 1) / NT;
+  OpParams o;
+  int64_t row0;
+  const float2* tab;
+  u32x4 r[CPT];
+  float chat[CPT];
+  __device__ void load(int kt, int tid) {
+    const uint8_t* codes = static_cast<const uint8_t*>(o.ptr);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      const int64_t n = row0 + (idx >> 1);
+      const int half = idx & 1;
+      if (idx < CH && n < o.N) {
+        r[c] = ld16(codes + n * (o.K / 2) + (int64_t)kt * 32 + half * 16);
+        chat[c] = block_scale(o.absmax_q, o.absmax_scale, n * (o.K / kBlock) + kt);
+      } else {
+        r[c] = u32x4{0, 0, 0, 0};
+        chat[c] = 0.f;
+      }
+    }
+  }
+  __device__ void store(uint16_t* lds, int tid) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      if (idx < CH) {
+        uint16_t* dst = lds + (idx >> 1) * LDS_STRIDE + (idx & 1) * 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st_lds16(dst + 8 * i, dequant8(r[c][i], chat[c], tab));
+      }
+    }
+  }
+};
+
+template <int ROWS>
+struct Nf4Tr {     // element (k, n) = deq(W)[n, k]: rows k, reduction n
+  static constexpr int NP = ROWS;                 // 8 (n) x 8 (k) patches
+  static constexpr int PPT = (NP + NT - 1) / NT;
+  static constexpr int KS = ROWS / 8;
+  OpParams o;
+  int64_t row0;
+  const float2* tab;
+  uint32_t r[PPT][8];
+  float chat[PPT][8];
+  __device__ void load(int kt, int tid) {
+    const uint8_t* codes = static_cast<const uint8_t*>(o.ptr);
+#pragma unroll
+    for (int c = 0; c < PPT; ++c) {
+      const int p = tid + c * NT;
+      const int kp = p % KS, np = p / KS;
+      const int64_t k = row0 + kp * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t n = (int64_t)kt * BK + np * 8 + i;
+        if (p < NP && n < o.N && k < o.K) {
+          r[c][i] = *reinterpret_cast<const uint32_t*>(codes + n * (o.K / 2) + k / 2);
+          chat[c][i] = block_scale(o.absmax_q, o.absmax_scale, n * (o.K / kBlock) + k / kBlock);
+        } else {
+          r[c][i] = 0;
+          chat[c][i] = 0.f;
+        }
+      }
+    }
+  }
+  __device__ void store(uint16_t* lds, int tid) {
+#pragma unroll
+    for (int c = 0; c < PPT; ++c) {
+      const int p = tid + c * NT;
+      if (p < NP) {
+        const int kp = p % KS, np = p / KS;
+        float v[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dequant8_f32(r[c][i], chat[c][i], tab, v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x4 o4 = {pack_bf16x2(v[0][j], v[1][j]), pack_bf16x2(v[2][j], v[3][j]),
+                            pack_bf16x2(v[4][j], v[5][j]), pack_bf16x2(v[6][j], v[7][j])};
+          st_lds16(lds + (kp * 8 + j) * LDS_STRIDE + np * 8, o4);
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA tile step and the double-buffered tile loop
+// ---------------------------------------------------------------------------
+
+template <int BP, int BQ>
+struct Mma {
+  static constexpr int TP = BP / 32, TQ = BQ / 32;   // 16x16 tiles per wave
+  f32x4 acc[TP][TQ];
+  __device__ void zero() {
+#pragma unroll
+    for (int i = 0; i < TP; ++i)
+#pragma unroll
+      for (int j = 0; j < TQ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ void step(const uint16_t* ldsP, const uint16_t* ldsQ, int wave, int lane) {
+    const int wp = (wave & 1) * (BP / 2), wq = (wave >> 1) * (BQ / 2);
+    const int lr = lane & 15, lk = 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      u32x4 a[TP], b[TQ];
+#pragma unroll
+      for (int i = 0; i < TP; ++i)
+        a[i] = *reinterpret_cast<const u32x4*>(ldsP + (wp + 16 * i + lr) * LDS_STRIDE + ks * 32 + lk);
+#pragma unroll
+      for (int j = 0; j < TQ; ++j)
+        b[j] = *reinterpret_cast<const u32x4*>(ldsQ + (wq + 16 * j + lr) * LDS_STRIDE + ks * 32 + lk);
+#pragma unroll
+      for (int i = 0; i < TP; ++i)
+#pragma unroll
+        for (int j = 0; j < TQ; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+    }
+  }
+};
+
+// Runs reduction tiles [kt0, kt1) through the two LDS buffers:
+// prefetch tile t+1 into registers, multiply tile t, store t+1, barrier.
+template <int BP, int BQ, class LP, class LQ>
+__device__ void run_tiles(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mma,
+                          uint16_t* lds, int tid) {
+  if (kt0 >= kt1) return;
+  uint16_t* bufP[2] = {lds, lds + (BP + BQ) * LDS_STRIDE};
+  uint16_t* bufQ[2] = {lds + BP * LDS_STRIDE, lds + (2 * BP + BQ) * LDS_STRIDE};
+  const int wave = tid >> 6, lane = tid & 63;
+  lp.load(kt0, tid);
+  lq.load(kt0, tid);
+  __syncthreads();
+  lp.store(bufP[0], tid);
+  lq.store(bufQ[0], tid);
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) {
+      lp.load(kt + 1, tid);
+      lq.load(kt + 1, tid);
+    }
+    mma.step(bufP[cur], bufQ[cur], wave, lane);
+    if (more) {
+      lp.store(bufP[cur ^ 1], tid);
+      lq.store(bufQ[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+}
+
+// Stores C[q, p] as bf16 (lane holds 4 consecutive p of one q per tile).
+template <int BP, int BQ>
+__device__ void store_bf16(const Mma<BP, BQ>& mma, uint16_t* out, int64_t ldo,
+                           int64_t p0, int64_t q0, int64_t P, int64_t Q, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const int64_t wp = p0 + (wave & 1) * (BP / 2) + 4 * (lane >> 4);
+  const int64_t wq = q0 + (wave >> 1) * (BQ / 2) + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < Mma<BP, BQ>::TP; ++i)
+#pragma unroll
+    for (int j = 0; j < Mma<BP, BQ>::TQ; ++j) {
+      const int64_t p = wp + 16 * i, q = wq + 16 * j;
+      if (p < P && q < Q) {   // P % 4 == 0, so the 4 values are all in range
+        const f32x4 v = mma.acc[i][j];
+        *reinterpret_cast<u32x2*>(out + q * ldo + p) =
+            u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+      }
+    }
+}
+
+template <int BP, int BQ>
+__device__ void store_f32(const Mma<BP, BQ>& mma, float* out, int64_t ldo,
+                          int64_t p0, int64_t q0, int64_t P, int64_t Q, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  const int64_t wp = p0 + (wave & 1) * (BP / 2) + 4 * (lane >> 4);
+  const int64_t wq = q0 + (wave >> 1) * (BQ / 2) + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < Mma<BP, BQ>::TP; ++i)
+#pragma unroll
+    for (int j = 0; j < Mma<BP, BQ>::TQ; ++j) {
+      const int64_t p = wp + 16 * i, q = wq + 16 * j;
+      if (p < P && q < Q) *reinterpret_cast<f32x4*>(out + q * ldo + p) = mma.acc[i][j];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward, large M: Y = X . deq(W)^T + s . T . B.  P = n, Q = m.
+// ---------------------------------------------------------------------------
+
+constexpr int FBP = 128, FBQ = 128;
+
+__global__ __launch_bounds__(NT) void k_fwd_gemm(OpParams w, OpParams x, OpParams bl,
+                                                 OpParams tl, int r, uint16_t* Y,
+                                                 int64_t M, int64_t N, Nf4Tables tb) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (FBP + FBQ) * LDS_STRIDE];
+  __shared__ float2 tab[256];
+  const int tid = threadIdx.x;
+  build_pair_table(tab, tb, tid, NT);
+  const int64_t p0 = (int64_t)blockIdx.x * FBP, q0 = (int64_t)blockIdx.y * FBQ;
+  Mma<FBP, FBQ> mma;
+  mma.zero();
+  {
+    Nf4Nat<FBP> lp{w, p0, tab};
+    Bf16Nat<FBQ> lq{x, q0};
+    run_tiles<FBP, FBQ>(lp, lq, 0, (int)(w.K / BK), mma, lds, tid);
+  }
+  if (r > 0) {
+    const int nt = (r + BK - 1) / BK;
+    Bf16Tr<FBP> lp{bl, p0};
+    for (int pass = 0; pass < 2; ++pass) {
+      F32Nat<FBQ> lq{tl, q0, pass};
+      run_tiles<FBP, FBQ>(lp, lq, 0, nt, mma, lds, tid);
+    }
+  }
+  store_bf16(mma, Y, N, p0, q0, N, M, tid);
+}
+
+// ---------------------------------------------------------------------------
+// Backward dX = dY . deq(W) + s . G . A^T.  P = k, Q = m.
+// ---------------------------------------------------------------------------
+
+constexpr int DBP = 128, DBQ = 128;
+
+__global__ __launch_bounds__(NT) void k_dx_gemm(OpParams w, OpParams dy, OpParams al,
+                                                OpParams gl, int r, uint16_t* dX,
+                                                int64_t M, int64_t K, Nf4Tables tb) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (DBP + DBQ) * LDS_STRIDE];
+  __shared__ float2 tab[256];
+  const int tid = threadIdx.x;
+  build_pair_table(tab, tb, tid, NT);
+  const int64_t p0 = (int64_t)blockIdx.x * DBP, q0 = (int64_t)blockIdx.y * DBQ;
+  Mma<DBP, DBQ> mma;
+  mma.zero();
+  {
+    Nf4Tr<DBP> lp{w, p0, tab};
+    Bf16Nat<DBQ> lq{dy, q0};
+    run_tiles<DBP, DBQ>(lp, lq, 0, (int)((w.N + BK - 1) / BK), mma, lds, tid);
+  }
+  if (r > 0) {
+    const int nt = (r + BK - 1) / BK;
+    Bf16Nat<DBP> lp{al, p0};
+    for (int pass = 0; pass < 2; ++pass) {
+      F32Nat<DBQ> lq{gl, q0, pass};
+      run_tiles<DBP, DBQ>(lp, lq, 0, nt, mma, lds, tid);
+    }
+  }
+  store_bf16(mma, dX, K, p0, q0, K, M, tid);
+}
+
+// ---------------------------------------------------------------------------
+// Rank-r products with a split reduction: partial sums of C[q, p] for
+// reduction tiles [z*tps, (z+1)*tps) go to ws[z][q][p]; a second kernel sums
+// the partials in split order (deterministic) and writes the result.
+// PASSES = 2 runs the tiles twice with the fp32 operand's hi and lo parts.
+// ---------------------------------------------------------------------------
+
+template <int BP, int BQ, class LP, class LQ, int PASSES>
+__global__ __launch_bounds__(NT) void k_rank(OpParams po, OpParams qo, int ntiles,
+                                             int tps, float* ws, int64_t P, int64_t Q) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BP + BQ) * LDS_STRIDE];
+  const int tid = threadIdx.x;
+  const int64_t p0 = (int64_t)blockIdx.x * BP, q0 = (int64_t)blockIdx.y * BQ;
+  const int z = blockIdx.z;
+  const int kt0 = z * tps, kt1 = min(ntiles, kt0 + tps);
+  Mma<BP, BQ> mma;
+  mma.zero();
+  for (int pass = 0; pass < PASSES; ++pass) {
+    LP lp{po, p0};
+    LQ lq{qo, q0};
+    if constexpr (PASSES == 2) {
+      // exactly one of the two operands is an fp32 hi/lo source
+      if constexpr (requires { lp.pass; }) lp.pass = pass;
+      if constexpr (requires { lq.pass; }) lq.pass = pass;
+    }
+    run_tiles<BP, BQ>(lp, lq, kt0, kt1, mma, lds, tid);
+  }
+  store_f32(mma, ws + (int64_t)z * P * Q, P, p0, q0, P, Q, tid);
+}
+
+// out[i] = scale * sum_z ws[z][i]; fp32 or bf16 output; 4 elements a thread.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void k_split_reduce(const float* ws, int splits,
+                                                      int64_t count, float scale,
+                                                      void* out) {
+  const int64_t i = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (i >= count) return;
+  f32x4 s = *reinterpret_cast<const f32x4*>(ws + i);
+  for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(ws + (int64_t)z * count + i);
+  s *= scale;
+  if constexpr (BF16_OUT) {
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + i) =
+        u32x2{pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w)};
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + i) = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+
+namespace {
+
+OpParams op(const void* p, int64_t ld, int64_t nrows, int64_t nred, float scale = 1.f) {
+  OpParams o{};
+  o.ptr = p;
+  o.ld = ld;
+  o.nrows = nrows;
+  o.nred = nred;
+  o.scale = scale;
+  return o;
+}
+
+OpParams nf4op(const Nf4View& w) {
+  OpParams o{};
+  o.ptr = w.codes;
+  o.absmax_q = w.absmax_q;
+  o.absmax_scale = w.absmax_scale;
+  o.N = w.N;
+  o.K = w.K;
+  return o;
+}
+
+unsigned cdiv(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
+
+struct Split {
+  int ntiles, tps, splits;
+};
+
+// Split the reduction so that the grid has about 512 workgroups, at least two
+// tiles per split.
+Split choose_split(int64_t nred, int64_t ptiles, int64_t qtiles) {
+  Split s;
+  s.ntiles = static_cast<int>((nred + BK - 1) / BK);
+  int64_t want = 512 / std::max<int64_t>(1, ptiles * qtiles);
+  want = std::max<int64_t>(1, std::min<int64_t>(want, (s.ntiles + 1) / 2));
+  s.tps = static_cast<int>((s.ntiles + want - 1) / want);
+  s.splits = (s.ntiles + s.tps - 1) / s.tps;
+  return s;
+}
+
+template <bool BF16>
+hipError_t reduce(const float* ws, int splits, int64_t count, float scale, void* out,
+                  hipStream_t stream) {
+  const unsigned grid = cdiv(count / 4, 256);
+  hipLaunchKernelGGL(k_split_reduce<BF16>, dim3(grid), dim3(256), 0, stream, ws, splits,
+                     count, scale, out);
+  return hipGetLastError();
+}
+
+constexpr int RB_R = 64;     // tile of the rank dimension
+constexpr int RB_X = 128;    // tile of the long dimension
+
+}  // namespace
+
+size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r) {
+  if (r <= 0) return 0;
+  const int64_t rt = (r + RB_R - 1) / RB_R;
+  const Split t = choose_split(K, rt, (M + RB_X - 1) / RB_X);
+  const Split g = choose_split(N, rt, (M + RB_X - 1) / RB_X);
+  const Split a = choose_split(M, rt, (K + RB_X - 1) / RB_X);
+  const Split b = choose_split(M, (N + RB_X - 1) / RB_X, rt);
+  size_t m = 0;
+  m = std::max<size_t>(m, (size_t)t.splits * M * r);
+  m = std::max<size_t>(m, (size_t)g.splits * M * r);
+  m = std::max<size_t>(m, (size_t)a.splits * K * r);
+  m = std::max<size_t>(m, (size_t)b.splits * r * N);
+  return m;
+}
+
+hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
+                           const float* T, const uint16_t* B, int r, float s,
+                           uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
+  dim3 grid(cdiv(w.N, FBP), cdiv(M, FBQ));
+  prof_begin(0, stream);
+  hipLaunchKernelGGL(k_fwd_gemm, grid, dim3(NT), 0, stream, nf4op(w), op(X, w.K, M, w.K),
+                     op(B, w.N, w.N, r), op(T, r, M, r, s), r, Y, M, w.N, tb);
+  prof_end(0, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
+                          const float* G, const uint16_t* A, int r, float s,
+                          uint16_t* dX, const Nf4Tables& tb, hipStream_t stream) {
+  dim3 grid(cdiv(w.K, DBP), cdiv(M, DBQ));
+  prof_begin(1, stream);
+  hipLaunchKernelGGL(k_dx_gemm, grid, dim3(NT), 0, stream, nf4op(w), op(dY, w.N, M, w.N),
+                     op(A, r, w.K, r), op(G, r, M, r, s), r, dX, M, w.K, tb);
+  prof_end(1, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A,
+                            int r, float* T, float* ws, hipStream_t stream) {
+  const int64_t pt = (r + RB_R - 1) / RB_R, qt = (M + RB_X - 1) / RB_X;
+  const Split sp = choose_split(K, pt, qt);
+  prof_begin(4, stream);
+  hipLaunchKernelGGL((k_rank<RB_R, RB_X, Bf16Tr<RB_R>, Bf16Nat<RB_X>, 1>),
+                     dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(A, r, r, K),
+                     op(X, K, M, K), sp.ntiles, sp.tps, ws, (int64_t)r, M);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = reduce<false>(ws, sp.splits, M * r, 1.f, T, stream);
+  prof_end(4, stream);
+  return e;
+}
+
+hipError_t launch_lora_grad_in(const uint16_t* dY, int64_t M, int64_t N,
+                               const uint16_t* B, int r, float* G, float* ws,
+                               hipStream_t stream) {
+  const int64_t pt = (r + RB_R - 1) / RB_R, qt = (M + RB_X - 1) / RB_X;
+  const Split sp = choose_split(N, pt, qt);
+  prof_begin(4, stream);
+  hipLaunchKernelGGL((k_rank<RB_R, RB_X, Bf16Nat<RB_R>, Bf16Nat<RB_X>, 1>),
+                     dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(B, N, r, N),
+                     op(dY, N, M, N), sp.ntiles, sp.tps, ws, (int64_t)r, M);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = reduce<false>(ws, sp.splits, M * r, 1.f, G, stream);
+  prof_end(4, stream);
+  return e;
+}
+
+hipError_t launch_grad_a(const uint16_t* X, int64_t M, int64_t K, const float* G,
+                         int r, float s, uint16_t* dA, float* ws, hipStream_t stream) {
+  const int64_t pt = (r + RB_R - 1) / RB_R, qt = (K + RB_X - 1) / RB_X;
+  const Split sp = choose_split(M, pt, qt);
+  prof_begin(4, stream);
+  hipLaunchKernelGGL((k_rank<RB_R, RB_X, F32Tr<RB_R>, Bf16Tr<RB_X>, 2>),
+                     dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(G, r, r, M),
+                     op(X, K, K, M), sp.ntiles, sp.tps, ws, (int64_t)r, K);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = reduce<true>(ws, sp.splits, K * r, s, dA, stream);
+  prof_end(4, stream);
+  return e;
+}
+
+hipError_t launch_grad_b(const uint16_t* dY, int64_t M, int64_t N, const float* T,
+                         int r, float s, uint16_t* dB, float* ws, hipStream_t stream) {
+  const int64_t pt = (N + RB_X - 1) / RB_X, qt = (r + RB_R - 1) / RB_R;
+  const Split sp = choose_split(M, pt, qt);
+  prof_begin(4, stream);
+  hipLaunchKernelGGL((k_rank<RB_X, RB_R, Bf16Tr<RB_X>, F32Tr<RB_R>, 2>),
+                     dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(dY, N, N, M),
+                     op(T, r, r, M), sp.ntiles, sp.tps, ws, N, (int64_t)r);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = reduce<true>(ws, sp.splits, r * N, s, dB, stream);
+  prof_end(4, stream);
+  return e;
+}
+
+}  // namespace qnf4

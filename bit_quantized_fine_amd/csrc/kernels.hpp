@@ -1,0 +1,67 @@
+// Host-callable launchers of the gfx950 kernels.  Every launcher enqueues on
+// `stream`, allocates nothing and returns hipGetLastError() of its launches.
+// Shapes are validated by the caller (the C ABI layer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qnf4 {
+
+struct Nf4Tables;
+
+hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
+                           uint8_t* absmax_q, float* absmax_scale,
+                           const Nf4Tables& tb, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
+                             const float* absmax_scale, int64_t N, int64_t K,
+                             uint16_t* out, const Nf4Tables& tb, hipStream_t stream);
+
+struct Nf4View {
+  const uint8_t* codes;
+  const uint8_t* absmax_q;
+  const float* absmax_scale;
+  int64_t N, K;
+};
+
+// Profiling hook: the launchers call these around the launches of one
+// kernel family (no-ops unless profiling is enabled).
+void prof_begin(int family, hipStream_t stream);
+void prof_end(int family, hipStream_t stream);
+
+// Y[M,N] = bf16( X . deq(W)^T + s . T . B ), large-M MFMA path.
+// T [M, r] fp32 (may be null when r == 0).
+hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
+                           const float* T, const uint16_t* B, int r, float s,
+                           uint16_t* Y, const Nf4Tables& tb, hipStream_t stream);
+
+// Same result, small-M (M <= 16) streaming path.
+hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
+                             const float* T, const uint16_t* B, int r, float s,
+                             uint16_t* Y, const Nf4Tables& tb, hipStream_t stream);
+
+// dX[M,K] = bf16( dY . deq(W) + s . G . A^T ).
+hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
+                          const float* G, const uint16_t* A, int r, float s,
+                          uint16_t* dX, const Nf4Tables& tb, hipStream_t stream);
+
+// Rank-r products with a split reduction; partials go to `ws`.
+size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r);
+
+// T[M,r] = X . A (fp32 out).
+hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K,
+                            const uint16_t* A, int r, float* T, float* ws,
+                            hipStream_t stream);
+// G[M,r] = dY . B^T (fp32 out).
+hipError_t launch_lora_grad_in(const uint16_t* dY, int64_t M, int64_t N,
+                               const uint16_t* B, int r, float* G, float* ws,
+                               hipStream_t stream);
+// dA[K,r] = bf16( s . X^T . G ).
+hipError_t launch_grad_a(const uint16_t* X, int64_t M, int64_t K, const float* G,
+                         int r, float s, uint16_t* dA, float* ws, hipStream_t stream);
+// dB[r,N] = bf16( s . T^T . dY ).
+hipError_t launch_grad_b(const uint16_t* dY, int64_t M, int64_t N, const float* T,
+                         int r, float s, uint16_t* dB, float* ws, hipStream_t stream);
+
+}  // namespace qnf4

@@ -40,12 +40,13 @@ def linear_fwd_f64(X, W, A, B, s):
     return Y, T
 
 
-def linear_bwd_f64(dY, X, W, A, B, s):
-    """Backward on float64 operands. Returns (dX, dA, dB)."""
-    dY, X, W, A, B = (np.asarray(a, dtype=np.float64) for a in (dY, X, W, A, B))
+def linear_bwd_f64(dY, X, W, A, B, s, need_dx=True):
+    """Backward on float64 operands. Returns (dX, dA, dB); dX is None when
+    need_dx is False (W is then not read)."""
+    dY, X, A, B = (np.asarray(a, dtype=np.float64) for a in (dY, X, A, B))
     s = float(s)
     G = dY @ B.T
-    dX = dY @ W + s * (G @ A.T)
+    dX = dY @ np.asarray(W, dtype=np.float64) + s * (G @ A.T) if need_dx else None
     dA = s * (X.T @ G)
     dB = s * ((X @ A).T @ dY)
     return dX, dA, dB
@@ -57,11 +58,12 @@ def linear_fwd(X_bits, W_bits, A_bits, B_bits, s):
                           bf16_bits_to_f64(A_bits), bf16_bits_to_f64(B_bits), s)
 
 
-def linear_bwd(dY_bits, X_bits, W_bits, A_bits, B_bits, s):
+def linear_bwd(dY_bits, X_bits, W_bits, A_bits, B_bits, s, need_dx=True):
     """Backward from bf16 bit patterns (uint16 arrays); float64 results."""
-    return linear_bwd_f64(bf16_bits_to_f64(dY_bits), bf16_bits_to_f64(X_bits),
-                          bf16_bits_to_f64(W_bits), bf16_bits_to_f64(A_bits),
-                          bf16_bits_to_f64(B_bits), s)
+    W = bf16_bits_to_f64(W_bits) if need_dx else None
+    return linear_bwd_f64(bf16_bits_to_f64(dY_bits), bf16_bits_to_f64(X_bits), W,
+                          bf16_bits_to_f64(A_bits), bf16_bits_to_f64(B_bits), s,
+                          need_dx=need_dx)
 
 
 def linear_flops(M, N, K, r):

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function include/qlora_nf4.h declares,
+compute the same NF4 level table as the oracle (independently: Newton's method
+on erfc in long double vs. the oracle's bisection), give thresholds whose
+crossings are exactly the oracle's code boundaries, and reject bad arguments
+with the documented status before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_quantized_fine_amd as q
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(q.LIB_PATH),
+                                reason="libqlora_nf4.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = q.lib()
+    names = _declared_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(q.EXPORTED)
+
+
+def test_level_table_matches_oracle_bitwise():
+    got = np.array(q.qlora_nf4_levels(), dtype=np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), oracle.nf4_levels().view(np.uint32))
+
+
+def test_thresholds_are_oracle_boundaries():
+    """x > t_j  <=>  x >= boundary_{j+1}: the first float above t_j is the
+    oracle's boundary, so counting thresholds reproduces nearest-level
+    encoding on every float32 in [-1, 1]."""
+    t = np.array(q.qlora_nf4_thresholds(), dtype=np.float32)
+    nxt = np.nextafter(t, np.float32(2), dtype=np.float32)
+    np.testing.assert_array_equal(nxt.view(np.uint32), oracle.code_boundaries().view(np.uint32))
+
+
+def test_size_helpers():
+    L = q.lib()
+    for N, K in [(1, 64), (1024, 1024), (11008, 4096), (3, 64 * 257)]:
+        assert L.qlora_nf4_codes_bytes(N, K) == N * K // 2
+        assert L.qlora_nf4_absmax_q_bytes(N, K) == N * K // 64
+        assert L.qlora_nf4_scale_count(N, K) == -(-(N * K // 64) // 256)
+        total = (L.qlora_nf4_codes_bytes(N, K) + L.qlora_nf4_absmax_q_bytes(N, K)
+                 + 4 * L.qlora_nf4_scale_count(N, K))
+        assert total == oracle.storage_bytes(N, K)
+    assert L.qlora_nf4_codes_bytes(4, 100) == 0
+
+
+def test_status_strings_and_version():
+    L = q.lib()
+    for s in range(7):
+        assert L.qlora_status_string(s)
+    assert L.qlora_status_string(99) == b"unknown status"
+    assert L.qlora_version().decode().count(".") == 2
+
+
+def _w(codes=16, aq=16, sc=16, N=64, K=64):
+    return q._Nf4Weight(codes, aq, sc, N, K)
+
+
+def test_quantize_validation_before_launch():
+    L = q.lib()
+    p = ctypes.c_void_p(4096)
+    assert L.qlora_nf4_quantize(None, 4, 64, p, p, p, None) == 1
+    assert L.qlora_nf4_quantize(p, 4, 100, p, p, p, None) == 2
+    assert L.qlora_nf4_quantize(p, 0, 64, p, p, p, None) == 2
+    assert L.qlora_nf4_quantize(ctypes.c_void_p(4100), 4, 64, p, p, p, None) == 4
+
+
+def test_linear_validation_before_launch():
+    L = q.lib()
+    p = ctypes.c_void_p(4096)
+    w = _w(4096, 4096, 4096, 64, 128)
+    ws_need = L.qlora_linear_fwd_workspace_bytes(16, 64, 128, 16)
+    assert ws_need > 0
+    # null X
+    assert L.qlora_linear_fwd(None, 16, ctypes.byref(w), p, p, 16, 1.0, p, p, p, ws_need, None) == 1
+    # rank not a multiple of 8 / too large
+    assert L.qlora_linear_fwd(p, 16, ctypes.byref(w), p, p, 7, 1.0, p, p, p, ws_need, None) == 3
+    assert L.qlora_linear_fwd(p, 16, ctypes.byref(w), p, p, 264, 1.0, p, p, p, ws_need, None) == 3
+    # r > 0 needs A, B and T
+    assert L.qlora_linear_fwd(p, 16, ctypes.byref(w), None, p, 16, 1.0, p, p, p, ws_need, None) == 1
+    assert L.qlora_linear_fwd(p, 16, ctypes.byref(w), p, p, 16, 1.0, p, None, p, ws_need, None) == 1
+    # shapes
+    assert L.qlora_linear_fwd(p, 0, ctypes.byref(w), p, p, 16, 1.0, p, p, p, ws_need, None) == 2
+    bad_k = _w(4096, 4096, 4096, 64, 96)
+    assert L.qlora_linear_fwd(p, 16, ctypes.byref(bad_k), p, p, 16, 1.0, p, p, p, ws_need, None) == 2
+    bad_n = _w(4096, 4096, 4096, 60, 128)
+    assert L.qlora_linear_fwd(p, 16, ctypes.byref(bad_n), p, p, 16, 1.0, p, p, p, ws_need, None) == 2
+    # alignment
+    assert L.qlora_linear_fwd(ctypes.c_void_p(4098), 16, ctypes.byref(w), p, p, 16, 1.0, p, p, p,
+                              ws_need, None) == 4
+    # workspace
+    assert L.qlora_linear_fwd(p, 16, ctypes.byref(w), p, p, 16, 1.0, p, p, p, ws_need - 1, None) == 6
+    assert L.qlora_linear_fwd(p, 16, ctypes.byref(w), p, p, 16, 1.0, p, p, None, ws_need, None) == 6
+    # null weight struct / fields
+    assert L.qlora_linear_fwd(p, 16, None, p, p, 16, 1.0, p, p, p, ws_need, None) == 1
+    nw = _w(0, 4096, 4096, 64, 128)
+    assert L.qlora_linear_fwd(p, 16, ctypes.byref(nw), p, p, 16, 1.0, p, p, p, ws_need, None) == 1
+
+
+def test_bwd_validation_before_launch():
+    L = q.lib()
+    p = ctypes.c_void_p(4096)
+    w = _w(4096, 4096, 4096, 64, 128)
+    need = L.qlora_linear_bwd_workspace_bytes(16, 64, 128, 16)
+    assert need > 0
+    assert L.qlora_linear_bwd(None, p, 16, ctypes.byref(w), p, p, 16, 1.0, None, p, p, p, p,
+                              need, None) == 1
+    assert L.qlora_linear_bwd(p, p, 16, ctypes.byref(w), p, p, 16, 1.0, None, p, None, p, p,
+                              need, None) == 1
+    assert L.qlora_linear_bwd(p, p, 16, ctypes.byref(w), p, p, 12, 1.0, None, p, p, p, p,
+                              need, None) == 3
+    assert L.qlora_linear_bwd(p, p, 16, ctypes.byref(w), p, p, 16, 1.0, None, p, p, p, p,
+                              need - 1, None) == 6
+    assert L.qlora_linear_bwd(p, p, 16, ctypes.byref(w), p, p, 16, 1.0, None,
+                              ctypes.c_void_p(4104), p, p, p, need, None) == 4
+    # r = 0 needs no workspace and no adapters
+    assert L.qlora_linear_bwd_workspace_bytes(16, 64, 128, 0) == 0
+
+
+def test_profile_api_host_only():
+    L = q.lib()
+    assert L.qlora_profile_reset() == 0
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert L.qlora_profile_read(0, ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert n.value == 0 and ms.value == 0.0
+    assert L.qlora_profile_read(9, None, None) == 2

@@ -1,0 +1,248 @@
+"""GPU parity of the QLoRA linear forward and backward against the oracle.
+
+The oracle quantizes the same seeded float32 weight itself, dequantizes it,
+and computes Y, dX, dA, dB in float64 from the exact bf16 inputs.  The GPU
+outputs (bf16, fp32 accumulation) must be within relative Frobenius error
+5e-3 and max error 1e-2 * max|ref|.  Cases span both forward paths (M <= 16
+streams the weight; larger M runs the MFMA GEMM), several tiles with ragged
+tails in every dimension, ranks 8..256, B = 0 and r = 0.
+"""
+import numpy as np
+import pytest
+
+import bit_quantized_fine_amd as q
+import oracle
+import workloads
+from gpu_util import (assert_close, bf16, bits, dev, errors, f32, need_gpu, say,
+                      torch)
+
+pytestmark = pytest.mark.gpu
+
+
+class Case:
+    """One linear: seeded inputs, GPU tensors, oracle reference."""
+
+    def __init__(self, M, N, K, r, s, seed, b_std=0.01, b_zero=False):
+        rng = np.random.default_rng(seed)
+        inp = workloads.draw_linear(rng, N, K, M, r, b_std=b_std)
+        if b_zero:
+            inp.B[:] = 0
+        self.M, self.N, self.K, self.r, self.s = M, N, K, r, s
+        self.inp = inp
+        self.w = q.qlora_nf4_quantize(f32(inp.W))
+        self.X, self.A, self.B, self.dY = (bf16(inp.X), bf16(inp.A), bf16(inp.B),
+                                           bf16(inp.dY))
+        codes, e, d, _ = oracle.quantize(inp.W)
+        self.What = oracle.dequantize(codes, e, d, N, K)
+
+    def gpu_fwd(self, r=None):
+        if (self.r if r is None else r) == 0:
+            return q.qlora_linear_fwd(self.X, self.w)
+        return q.qlora_linear_fwd(self.X, self.w, self.A, self.B, self.s)
+
+    def ref_fwd(self):
+        return oracle.linear_fwd(self.inp.X, self.What, self.inp.A, self.inp.B, self.s)
+
+    def ref_bwd(self):
+        return oracle.linear_bwd(self.inp.dY, self.inp.X, self.What, self.inp.A,
+                                 self.inp.B, self.s)
+
+
+FWD_CASES = [
+    # (M, N, K, r, s)   decode path M <= 16, GEMM path above
+    (1, 1024, 1024, 16, 1.0),
+    (4, 1024, 1024, 16, 1.0),
+    (16, 1024, 1024, 16, 1.0),
+    (7, 200, 320, 8, 0.5),           # ragged N (not a multiple of 16), K = 5 * 64
+    (16, 1000, 64 * 33, 64, 0.25),   # K with a half chunk
+    (17, 1024, 1024, 16, 1.0),       # first GEMM size
+    (300, 520, 448, 64, 0.25),       # ragged M, N, K over several tiles
+    (256, 384, 1024, 256, 0.0625),   # maximum rank
+    (129, 136, 64, 8, 2.0),          # single reduction tile
+]
+
+
+@pytest.mark.parametrize("M,N,K,r,s", FWD_CASES)
+def test_fwd_parity(M, N, K, r, s):
+    need_gpu()
+    say(f"fwd M={M} N={N} K={K} r={r}")
+    c = Case(M, N, K, r, s, seed=M * 7 + N + K + r)
+    Y, T = c.gpu_fwd()
+    torch.cuda.synchronize()
+    Yref, Tref = c.ref_fwd()
+    assert_close("Y", Y.float().cpu().numpy(), Yref)
+    assert_close("T", T.cpu().numpy(), Tref)
+
+
+@pytest.mark.parametrize("M,N,K,r,s", [
+    (16, 1024, 1024, 16, 1.0),
+    (1, 200, 320, 8, 0.5),
+    (300, 520, 448, 64, 0.25),
+    (256, 384, 1024, 256, 0.0625),
+    (33, 1000, 64 * 33, 64, 0.25),
+])
+def test_bwd_parity(M, N, K, r, s):
+    need_gpu()
+    say(f"bwd M={M} N={N} K={K} r={r}")
+    c = Case(M, N, K, r, s, seed=M * 5 + N + K + r)
+    Y, T = c.gpu_fwd()
+    dX, dA, dB = q.qlora_linear_bwd(c.dY, c.X, c.w, c.A, c.B, c.s, T=T)
+    # gradient-checkpointing form: T recomputed inside the backward
+    dX2, dA2, dB2 = q.qlora_linear_bwd(c.dY, c.X, c.w, c.A, c.B, c.s, T=None)
+    torch.cuda.synchronize()
+    dXr, dAr, dBr = c.ref_bwd()
+    assert_close("dX", dX.float().cpu().numpy(), dXr)
+    assert_close("dA", dA.float().cpu().numpy(), dAr)
+    assert_close("dB", dB.float().cpu().numpy(), dBr)
+    assert_close("dA(recompute)", dA2.float().cpu().numpy(), dAr)
+    assert_close("dB(recompute)", dB2.float().cpu().numpy(), dBr)
+    np.testing.assert_array_equal(bits(dX2), bits(dX))
+
+
+def test_lora_heavy_case():
+    """B with standard deviation 1: the adapter term dominates, so a dropped or
+    mis-scaled LoRA term (or a wrong hi/lo split) cannot hide in the tolerance."""
+    need_gpu()
+    for M in (8, 200):
+        say(f"lora-heavy M={M}")
+        c = Case(M, 256, 512, 32, 0.5, seed=99 + M, b_std=1.0)
+        Y, T = c.gpu_fwd()
+        dX, dA, dB = q.qlora_linear_bwd(c.dY, c.X, c.w, c.A, c.B, c.s, T=T)
+        torch.cuda.synchronize()
+        Yr, _ = c.ref_fwd()
+        dXr, dAr, dBr = c.ref_bwd()
+        assert_close("Y", Y.float().cpu().numpy(), Yr)
+        assert_close("dX", dX.float().cpu().numpy(), dXr)
+        assert_close("dA", dA.float().cpu().numpy(), dAr)
+        assert_close("dB", dB.float().cpu().numpy(), dBr)
+
+
+@pytest.mark.parametrize("M", [16, 160])
+def test_b_zero_reproduces_base(M):
+    """B = 0: Y equals the base-only (r = 0) GPU output bit for bit, equals
+    the oracle's X . deq(W)^T, and dA is exactly zero (the adapter that starts
+    at zero: Mathematical Formulation of "DL0087 QLoRA")."""
+    need_gpu()
+    say(f"B=0 M={M}")
+    c = Case(M, 1024, 1024, 16, 1.0, seed=5 + M, b_zero=True)
+    Y, T = c.gpu_fwd()
+    Y0, _ = c.gpu_fwd(r=0)
+    dX, dA, dB = q.qlora_linear_bwd(c.dY, c.X, c.w, c.A, c.B, c.s, T=T)
+    dX0, _, _ = q.qlora_linear_bwd(c.dY, c.X, c.w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y), bits(Y0))
+    np.testing.assert_array_equal(bits(dX), bits(dX0))
+    assert torch.count_nonzero(dA.float()).item() == 0
+    base = oracle.bf16_bits_to_f64(c.inp.X) @ oracle.bf16_bits_to_f64(c.What).T
+    assert_close("Y(B=0)", Y.float().cpu().numpy(), base)
+    _, _, dBr = c.ref_bwd()
+    assert_close("dB(B=0)", dB.float().cpu().numpy(), dBr)
+
+
+def test_frozen_base_untouched_and_deterministic():
+    """The NF4 buffers are bytewise unchanged by fwd and bwd, and repeated
+    calls give bitwise-identical outputs."""
+    need_gpu()
+    for M in (4, 192):
+        say(f"frozen/determinism M={M}")
+        c = Case(M, 512, 512, 16, 1.0, seed=M)
+        before = [t.clone() for t in (c.w.codes, c.w.absmax_q, c.w.absmax_scale)]
+        outs = []
+        for _ in range(3):
+            Y, T = c.gpu_fwd()
+            dX, dA, dB = q.qlora_linear_bwd(c.dY, c.X, c.w, c.A, c.B, c.s, T=T)
+            torch.cuda.synchronize()
+            outs.append([bits(Y), T.cpu().numpy(), bits(dX), bits(dA), bits(dB)])
+        for a, b in zip(before, (c.w.codes, c.w.absmax_q, c.w.absmax_scale)):
+            assert torch.equal(a, b)
+        for o in outs[1:]:
+            for x, y in zip(outs[0], o):
+                np.testing.assert_array_equal(x, y)
+
+
+def test_bwd_without_dx():
+    need_gpu()
+    c = Case(64, 256, 256, 16, 1.0, seed=3)
+    Y, T = c.gpu_fwd()
+    dX, dA, dB = q.qlora_linear_bwd(c.dY, c.X, c.w, c.A, c.B, c.s, T=T, need_dx=False)
+    torch.cuda.synchronize()
+    assert dX is None
+    _, dAr, dBr = c.ref_bwd()
+    assert_close("dA", dA.float().cpu().numpy(), dAr)
+    assert_close("dB", dB.float().cpu().numpy(), dBr)
+
+
+# ---------------------------------------------------------------------------
+# Full-size configurations
+# ---------------------------------------------------------------------------
+
+def _full_linear_check(cfg_idx, lin_idx, M=None, rows=None):
+    cfg = workloads.CONFIGS[cfg_idx]
+    (lin, inp), = list(workloads.config_inputs(cfg_idx, M=M, linears=[lin_idx]))
+    m = inp.X.shape[0]
+    say(f"config {cfg_idx} linear {lin.name} N={lin.N} K={lin.K} M={m}")
+    w = q.qlora_nf4_quantize(f32(inp.W))
+    X, A, B, dY = bf16(inp.X), bf16(inp.A), bf16(inp.B), bf16(inp.dY)
+    Y, T = q.qlora_linear_fwd(X, w, A, B, cfg.s)
+    dX, dA, dB = q.qlora_linear_bwd(dY, X, w, A, B, cfg.s, T=T)
+    torch.cuda.synchronize()
+    codes, e, d, _ = oracle.quantize(inp.W)
+    np.testing.assert_array_equal(w.codes.cpu().numpy(), codes)
+    np.testing.assert_array_equal(w.absmax_q.cpu().numpy(), e)
+    What = oracle.dequantize(codes, e, d, lin.N, lin.K)
+    sel = slice(None) if rows is None else rows
+    Yr, _ = oracle.linear_fwd(inp.X[sel], What, inp.A, inp.B, cfg.s)
+    assert_close("Y", Y.float().cpu().numpy()[sel], Yr)
+    dXr, dAr, dBr = oracle.linear_bwd(inp.dY, inp.X, What, inp.A, inp.B, cfg.s)
+    assert_close("dX", dX.float().cpu().numpy(), dXr)
+    assert_close("dA", dA.float().cpu().numpy(), dAr)
+    assert_close("dB", dB.float().cpu().numpy(), dBr)
+
+
+@pytest.mark.parametrize("lin_idx", [0, 4, 6])
+def test_config1_full_size(lin_idx):
+    """LLaMA-7B linears at M=2048 (q, gate, down shapes), compared in full."""
+    need_gpu()
+    _full_linear_check(1, lin_idx)
+
+
+@pytest.mark.parametrize("lin_idx,M", [(0, 1), (1, 4), (2, 16), (2, 1)])
+def test_config2_decode_full_size(lin_idx, M):
+    """65B-shaped decode linears at M in {1, 4, 16}, compared in full."""
+    need_gpu()
+    cfg = workloads.CONFIGS[2]
+    (lin, inp), = list(workloads.config_inputs(2, M=M, linears=[lin_idx], with_grad=False))
+    say(f"config 2 {lin.name} N={lin.N} K={lin.K} M={M}")
+    w = q.qlora_nf4_quantize(f32(inp.W))
+    Y, T = q.qlora_linear_fwd(bf16(inp.X), w, bf16(inp.A), bf16(inp.B), cfg.s)
+    torch.cuda.synchronize()
+    codes, e, d, _ = oracle.quantize(inp.W)
+    np.testing.assert_array_equal(w.codes.cpu().numpy(), codes)
+    What = oracle.dequantize(codes, e, d, lin.N, lin.K)
+    Yr, _ = oracle.linear_fwd(inp.X, What, inp.A, inp.B, cfg.s)
+    assert_close("Y", Y.float().cpu().numpy(), Yr)
+
+
+@pytest.mark.parametrize("lin_idx", [0, 6])
+def test_config3_full_size_recompute(lin_idx):
+    """33B-shaped linears at M=4096 with the recompute (checkpointing) bwd:
+    sampled rows of Y and dX, full dA and dB."""
+    need_gpu()
+    cfg = workloads.CONFIGS[3]
+    (lin, inp), = list(workloads.config_inputs(3, linears=[lin_idx]))
+    say(f"config 3 {lin.name} N={lin.N} K={lin.K} M={inp.X.shape[0]}")
+    w = q.qlora_nf4_quantize(f32(inp.W))
+    X, A, B, dY = bf16(inp.X), bf16(inp.A), bf16(inp.B), bf16(inp.dY)
+    Y, _ = q.qlora_linear_fwd(X, w, A, B, cfg.s)
+    dX, dA, dB = q.qlora_linear_bwd(dY, X, w, A, B, cfg.s, T=None)
+    torch.cuda.synchronize()
+    codes, e, d, _ = oracle.quantize(inp.W)
+    What = oracle.dequantize(codes, e, d, lin.N, lin.K)
+    rows = np.random.default_rng(1).choice(inp.X.shape[0], 256, replace=False)
+    Yr, _ = oracle.linear_fwd(inp.X[rows], What, inp.A, inp.B, cfg.s)
+    assert_close("Y[rows]", Y.float().cpu().numpy()[rows], Yr)
+    dXr, _, _ = oracle.linear_bwd(inp.dY[rows], inp.X[rows], What, inp.A, inp.B, cfg.s)
+    assert_close("dX[rows]", dX.float().cpu().numpy()[rows], dXr)
+    _, dAr, dBr = oracle.linear_bwd(inp.dY, inp.X, What, inp.A, inp.B, cfg.s, need_dx=False)
+    assert_close("dA", dA.float().cpu().numpy(), dAr)
+    assert_close("dB", dB.float().cpu().numpy(), dBr)

@@ -5,9 +5,10 @@ arithmetic.  Both the oracle-side tests and the GPU-side tests and benchmark
 take their inputs from here, so both sides see the same bytes.
 
 Recipe (stated once, used everywhere):
-  * config i draws from numpy.random.default_rng(seed) with seed = i unless
-    a test picks another seed;
-  * per linear, in the order q, k, v, o, gate, up, down, the draws are:
+  * linear j of config i draws from numpy.random.default_rng([seed, j]) with
+    seed = i unless a test picks another seed (linears are numbered in the
+    order q, k, v, o, gate, up, down);
+  * per linear the draws are, in this order:
       W   float32 [N, K], standard normal x 0.02
       an outlier mask, uniform(0,1) < 0.001, and W *= 10 on the mask
       X   [M, K] standard normal, rounded to bf16
@@ -107,21 +108,21 @@ def draw_linear(rng, N: int, K: int, M: int, r: int, b_std: float = 0.01,
     return LinearInputs(W, X, A, B, dY)
 
 
+def linear_rng(cfg_idx: int, lin_idx: int, seed: int = None):
+    return np.random.default_rng([cfg_idx if seed is None else seed, lin_idx])
+
+
 def config_inputs(cfg_idx: int, M: int = None, seed: int = None,
                   linears: List[int] = None, with_grad: bool = True):
     """Yield (Linear, LinearInputs) for the linears of a config, in order.
 
-    All linears are drawn in sequence from one generator, so asking for a
-    subset still yields the same bytes as the full config for those linears.
+    Each linear has its own generator, so a subset yields the same bytes as
+    the full config for those linears.
     """
     cfg = CONFIGS[cfg_idx]
-    rng = np.random.default_rng(cfg_idx if seed is None else seed)
     m = cfg.M[0] if M is None else M
-    want = set(range(len(cfg.linears))) if linears is None else set(linears)
-    last = max(want) if want else -1
-    for i, lin in enumerate(cfg.linears):
-        if i > last:
-            break
-        inp = draw_linear(rng, lin.N, lin.K, m, cfg.r, with_grad=with_grad)
-        if i in want:
-            yield lin, inp
+    idxs = range(len(cfg.linears)) if linears is None else linears
+    for i in idxs:
+        lin = cfg.linears[i]
+        yield lin, draw_linear(linear_rng(cfg_idx, i, seed), lin.N, lin.K, m, cfg.r,
+                               with_grad=with_grad)
