@@ -42,23 +42,52 @@ __global__ __launch_bounds__(256) void k_fwd_decode(
   const uint16_t* xrow = X + (int64_t)li * K;
   const int64_t brow = n * (K / kBlock);
 
+  // Chunks of this wave: c = wave + 4t.  Loads are issued a batch of DB
+  // chunks at a time, one batch ahead of the batch being multiplied, so each
+  // wave keeps 2 x DB 16-byte code loads (and their X fragments) in flight.
+  constexpr int DB = 4;
+  const int nmine = nchunks > wave ? (nchunks - wave + 3) / 4 : 0;
+  u32x4 cw[2][DB];
+  uint32_t ce[2][DB];
+  float cd[2][DB];
+  u32x4 xv[2][DB][4];
+  auto load_batch = [&](int t0, int st) {
+#pragma unroll
+    for (int u = 0; u < DB; ++u) {
+      const int t = t0 + u;
+      const int64_t k0 = (int64_t)(wave + 4 * t) * 128 + 32 * g;
+      const bool ok = t < nmine && k0 < K;
+      cw[st][u] = u32x4{0, 0, 0, 0};
+      ce[st][u] = 0;
+      cd[st][u] = 0.f;
+      if (n_ok && ok) {
+        const int64_t blk = brow + k0 / kBlock;
+        cw[st][u] = *reinterpret_cast<const u32x4*>(crow + k0 / 2);
+        ce[st][u] = absmax_q[blk];
+        cd[st][u] = absmax_scale[blk >> 8];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xv[st][u][i] = (m_ok && ok) ? *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * i)
+                                    : u32x4{0, 0, 0, 0};
+    }
+  };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c = wave; c < nchunks; c += 4) {
-    const int64_t k0 = (int64_t)c * 128 + 32 * g;
-    const bool k_ok = k0 < K;
-    u32x4 cw = {0, 0, 0, 0};
-    float chat = 0.f;
-    if (n_ok && k_ok) {
-      cw = *reinterpret_cast<const u32x4*>(crow + k0 / 2);
-      chat = block_scale(absmax_q, absmax_scale, brow + k0 / kBlock);
-    }
-    u32x4 xv[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-    if (m_ok && k_ok) {
+  auto mul_batch = [&](int st) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * i);
-    }
+    for (int u = 0; u < DB; ++u) {
+      const float chat = static_cast<float>(ce[st][u]) * cd[st][u];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc = mfma16(dequant8(cw[i], chat, tab), xv[i], acc);
+      for (int i = 0; i < 4; ++i) acc = mfma16(dequant8(cw[st][u][i], chat, tab), xv[st][u][i], acc);
+    }
+  };
+  if (nmine > 0) load_batch(0, 0);
+  for (int t0 = 0; t0 < nmine; t0 += 2 * DB) {
+    if (t0 + DB < nmine) load_batch(t0 + DB, 1);
+    mul_batch(0);
+    if (t0 + DB >= nmine) break;
+    if (t0 + 2 * DB < nmine) load_batch(t0 + 2 * DB, 0);
+    mul_batch(1);
   }
 
   if (wave == 0 && r > 0) {

@@ -1,6 +1,7 @@
 // MFMA GEMMs of the QLoRA NF4 linear layer on gfx950.
 //
-// Every product here has the form C[q, p] = sum_k P[p, k] . Q[q, k]: the
+// Every product here (the backward dX and the rank-r products; the forward
+// GEMM has its own kernel) has the form C[q, p] = sum_k P[p, k] . Q[q, k]: the
 // workgroup stages a P tile [BP x 64] and a Q tile [BQ x 64] in LDS, both
 // laid out reduction-contiguous ("MFMA ready": a lane's 8 reduction elements
 // are one 16-byte LDS read), and four waves (2 x 2) accumulate their
@@ -217,7 +218,8 @@ struct Nf4Nat {    // element (n, k) = deq(W)[n, k]; one thread = half a block
   int64_t row0;
   const float2* tab;
   u32x4 r[CPT];
-  float chat[CPT];
+  uint32_t ce[CPT];
+  float cd[CPT];
   __device__ void load(int kt, int tid) {
     const uint8_t* codes = static_cast<const uint8_t*>(o.ptr);
 #pragma unroll
@@ -226,11 +228,14 @@ struct Nf4Nat {    // element (n, k) = deq(W)[n, k]; one thread = half a block
       const int64_t n = row0 + (idx >> 1);
       const int half = idx & 1;
       if (idx < CH && n < o.N) {
+        const int64_t blk = n * (o.K / kBlock) + kt;
         r[c] = ld16(codes + n * (o.K / 2) + (int64_t)kt * 32 + half * 16);
-        chat[c] = block_scale(o.absmax_q, o.absmax_scale, n * (o.K / kBlock) + kt);
+        ce[c] = o.absmax_q[blk];
+        cd[c] = o.absmax_scale[blk >> 8];
       } else {
         r[c] = u32x4{0, 0, 0, 0};
-        chat[c] = 0.f;
+        ce[c] = 0;
+        cd[c] = 0.f;
       }
     }
   }
@@ -240,8 +245,9 @@ struct Nf4Nat {    // element (n, k) = deq(W)[n, k]; one thread = half a block
       const int idx = tid + c * NT;
       if (idx < CH) {
         uint16_t* dst = lds + (idx >> 1) * LDS_STRIDE + (idx & 1) * 32;
+        const float chat = static_cast<float>(ce[c]) * cd[c];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st_lds16(dst + 8 * i, dequant8(r[c][i], chat[c], tab));
+        for (int i = 0; i < 4; ++i) st_lds16(dst + 8 * i, dequant8(r[c][i], chat, tab));
       }
     }
   }
@@ -256,7 +262,8 @@ struct Nf4Tr {     // element (k, n) = deq(W)[n, k]: rows k, reduction n
   int64_t row0;
   const float2* tab;
   uint32_t r[PPT][8];
-  float chat[PPT][8];
+  uint32_t ce[PPT][8];   // 8-bit block constants and fp32 group scales, as
+  float cd[PPT][8];      // loaded; multiplied out in store()
   __device__ void load(int kt, int tid) {
     const uint8_t* codes = static_cast<const uint8_t*>(o.ptr);
 #pragma unroll
@@ -268,11 +275,14 @@ struct Nf4Tr {     // element (k, n) = deq(W)[n, k]: rows k, reduction n
       for (int i = 0; i < 8; ++i) {
         const int64_t n = (int64_t)kt * BK + np * 8 + i;
         if (p < NP && n < o.N && k < o.K) {
+          const int64_t blk = n * (o.K / kBlock) + k / kBlock;
           r[c][i] = *reinterpret_cast<const uint32_t*>(codes + n * (o.K / 2) + k / 2);
-          chat[c][i] = block_scale(o.absmax_q, o.absmax_scale, n * (o.K / kBlock) + k / kBlock);
+          ce[c][i] = o.absmax_q[blk];
+          cd[c][i] = o.absmax_scale[blk >> 8];
         } else {
           r[c][i] = 0;
-          chat[c][i] = 0.f;
+          ce[c][i] = 0;
+          cd[c][i] = 0.f;
         }
       }
     }
@@ -285,7 +295,8 @@ struct Nf4Tr {     // element (k, n) = deq(W)[n, k]: rows k, reduction n
         const int kp = p % KS, np = p / KS;
         float v[8][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dequant8_f32(r[c][i], chat[c][i], tab, v[i]);
+        for (int i = 0; i < 8; ++i)
+          dequant8_f32(r[c][i], static_cast<float>(ce[c][i]) * cd[c][i], tab, v[i]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const u32x4 o4 = {pack_bf16x2(v[0][j], v[1][j]), pack_bf16x2(v[2][j], v[3][j]),
@@ -395,38 +406,6 @@ __device__ void store_f32(const Mma<BP, BQ>& mma, float* out, int64_t ldo,
       const int64_t p = wp + 16 * i, q = wq + 16 * j;
       if (p < P && q < Q) *reinterpret_cast<f32x4*>(out + q * ldo + p) = mma.acc[i][j];
     }
-}
-
-// ---------------------------------------------------------------------------
-// Forward, large M: Y = X . deq(W)^T + s . T . B.  P = n, Q = m.
-// ---------------------------------------------------------------------------
-
-constexpr int FBP = 128, FBQ = 128;
-
-__global__ __launch_bounds__(NT) void k_fwd_gemm(OpParams w, OpParams x, OpParams bl,
-                                                 OpParams tl, int r, uint16_t* Y,
-                                                 int64_t M, int64_t N, Nf4Tables tb) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (FBP + FBQ) * LDS_STRIDE];
-  __shared__ float2 tab[256];
-  const int tid = threadIdx.x;
-  build_pair_table(tab, tb, tid, NT);
-  const int64_t p0 = (int64_t)blockIdx.x * FBP, q0 = (int64_t)blockIdx.y * FBQ;
-  Mma<FBP, FBQ> mma;
-  mma.zero();
-  {
-    Nf4Nat<FBP> lp{w, p0, tab};
-    Bf16Nat<FBQ> lq{x, q0};
-    run_tiles<FBP, FBQ>(lp, lq, 0, (int)(w.K / BK), mma, lds, tid);
-  }
-  if (r > 0) {
-    const int nt = (r + BK - 1) / BK;
-    Bf16Tr<FBP> lp{bl, p0};
-    for (int pass = 0; pass < 2; ++pass) {
-      F32Nat<FBQ> lq{tl, q0, pass};
-      run_tiles<FBP, FBQ>(lp, lq, 0, nt, mma, lds, tid);
-    }
-  }
-  store_bf16(mma, Y, N, p0, q0, N, M, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -541,14 +520,14 @@ struct Split {
   int ntiles, tps, splits;
 };
 
-// Split the reduction so that the grid has about 512 workgroups, at least two
-// tiles per split.
+// Split the reduction so that the grid has about one workgroup per CU, with
+// at least four reduction tiles per split (fewer, larger splits keep the fp32
+// partial sums small next to the operands they reduce).
 Split choose_split(int64_t nred, int64_t ptiles, int64_t qtiles) {
   Split s;
   s.ntiles = static_cast<int>((nred + BK - 1) / BK);
-  int64_t want = 512 / std::max<int64_t>(1, ptiles * qtiles);
-  want = std::max<int64_t>(1, std::min<int64_t>(want, (s.ntiles + 1) / 2));
-  s.tps = static_cast<int>((s.ntiles + want - 1) / want);
+  const int64_t want = std::max<int64_t>(1, 256 / std::max<int64_t>(1, ptiles * qtiles));
+  s.tps = static_cast<int>(std::max<int64_t>(4, (s.ntiles + want - 1) / want));
   s.splits = (s.ntiles + s.tps - 1) / s.tps;
   return s;
 }
@@ -580,17 +559,6 @@ size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r) {
   m = std::max<size_t>(m, (size_t)a.splits * K * r);
   m = std::max<size_t>(m, (size_t)b.splits * r * N);
   return m;
-}
-
-hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
-                           const float* T, const uint16_t* B, int r, float s,
-                           uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
-  dim3 grid(cdiv(w.N, FBP), cdiv(M, FBQ));
-  prof_begin(0, stream);
-  hipLaunchKernelGGL(k_fwd_gemm, grid, dim3(NT), 0, stream, nf4op(w), op(X, w.K, M, w.K),
-                     op(B, w.N, w.N, r), op(T, r, M, r, s), r, Y, M, w.N, tb);
-  prof_end(0, stream);
-  return hipGetLastError();
 }
 
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
