@@ -108,6 +108,9 @@ size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
 
 constexpr int kFamilies = 5;
 
+// Token counts up to this fold the T reduction into the decode kernel.
+constexpr int64_t kFewTokensFoldT = 4;
+
 struct Profiler {
   std::mutex mu;
   bool enabled = false;
@@ -274,10 +277,19 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const Nf4View v = view(w);
   hipError_t e = hipSuccess;
-  if (r > 0) e = launch_lora_down(X, M, w->K, A, r, T, static_cast<float*>(workspace), hs);
+  float* ws = static_cast<float*>(workspace);
+  if (M <= kFewTokensFoldT && r > 0) {
+    // T's partial sums are added up inside the decode kernel (no reduction
+    // launch); its workgroup 0 writes T.
+    int nz = 0;
+    e = launch_lora_down_partials(X, M, w->K, A, r, ws, &nz, hs);
+    if (e == hipSuccess) e = launch_fwd_decode(X, M, v, ws, nz, T, B, r, s, Y, tables(), hs);
+    return hip_status(e);
+  }
+  if (r > 0) e = launch_lora_down(X, M, w->K, A, r, T, ws, hs);
   if (e != hipSuccess) return QLORA_ERR_HIP;
   if (M <= 16)
-    e = launch_fwd_decode(X, M, v, T, B, r, s, Y, tables(), hs);
+    e = launch_fwd_decode(X, M, v, T, 0, nullptr, B, r, s, Y, tables(), hs);
   else
     e = launch_fwd_gemm(X, M, v, T, B, r, s, Y, tables(), hs);
   return hip_status(e);

@@ -93,6 +93,25 @@ __device__ __forceinline__ void dequant8_f32(uint32_t w, float c_hat,
   }
 }
 
+// Raw buffer access: a descriptor over [p, p + nbytes) in scalar registers
+// and 32-bit byte offsets; reads outside the range return zero.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+constexpr int kBufDword3 = 0x00020000;   // raw, untyped buffer (gfx9 family)
+
+__device__ __forceinline__ BufRes make_bufres(const void* p, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                           static_cast<int>(nbytes), kBufDword3);
+}
+__device__ __forceinline__ u32x4 buf_load16(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_u8(BufRes r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+__device__ __forceinline__ float buf_load_f32(BufRes r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // Block constant c_hat = fl32(e * d).
 __device__ __forceinline__ float block_scale(const uint8_t* absmax_q,
                                              const float* absmax_scale,

@@ -477,14 +477,84 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* ws, int split
                                                       void* out) {
   const int64_t i = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (i >= count) return;
-  f32x4 s = *reinterpret_cast<const f32x4*>(ws + i);
-  for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(ws + (int64_t)z * count + i);
+  // four independent partial sums so the loads of several splits overlap;
+  // the combination order is fixed, so results are deterministic
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
+  int z = 0;
+  for (; z + 4 <= splits; z += 4) {
+    s0 += *reinterpret_cast<const f32x4*>(ws + (int64_t)(z + 0) * count + i);
+    s1 += *reinterpret_cast<const f32x4*>(ws + (int64_t)(z + 1) * count + i);
+    s2 += *reinterpret_cast<const f32x4*>(ws + (int64_t)(z + 2) * count + i);
+    s3 += *reinterpret_cast<const f32x4*>(ws + (int64_t)(z + 3) * count + i);
+  }
+  for (; z < splits; ++z) s0 += *reinterpret_cast<const f32x4*>(ws + (int64_t)z * count + i);
+  f32x4 s = (s0 + s1) + (s2 + s3);
   s *= scale;
   if constexpr (BF16_OUT) {
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + i) =
         u32x2{pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w)};
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(out) + i) = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LoRA down-projection for few tokens (M <= 16): workgroup z covers spw
+// consecutive slices of 256 k; partial[z][m][j] = sum over them of
+// X[m, k] A[k, j].  Each A slice is transposed through LDS in 8x8 patches,
+// 64 ranks at a time; wave w multiplies ranks 16w..16w+15 of the 64 against
+// the token fragments, which come straight from global memory.
+// ---------------------------------------------------------------------------
+
+constexpr int LDS_K = 256;             // k per slice
+constexpr int LDS_KS = LDS_K + 8;      // LDS row stride (elements)
+
+__global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restrict__ X, int M,
+                                                         int64_t K, const uint16_t* __restrict__ A,
+                                                         int r, int spw, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t at[64 * LDS_KS];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, g = lane >> 4;
+  const bool m_ok = li < M;
+  for (int j0 = 0; j0 < r; j0 += 64) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sub = 0; sub < spw; ++sub) {
+      const int64_t k0 = ((int64_t)blockIdx.x * spw + sub) * LDS_K;
+      u32x4 xf[8];   // token fragments for the 8 k32 steps of this slice
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int64_t k = k0 + 32 * st + 8 * g;
+        xf[st] = (m_ok && k < K) ? *reinterpret_cast<const u32x4*>(X + (int64_t)li * K + k)
+                                 : u32x4{0, 0, 0, 0};
+      }
+      {  // patch p: ranks j0 + 8*(p % 8) .. +8, k rows k0 + 8*(p / 8) .. +8
+        const int jp = tid & 7, kp = tid >> 3;
+        u32x4 rows[8], cols[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int64_t k = k0 + kp * 8 + t;
+          const int j = j0 + jp * 8;
+          rows[t] = (k < K && j < r) ? *reinterpret_cast<const u32x4*>(A + k * r + j)
+                                     : u32x4{0, 0, 0, 0};
+        }
+        transpose8x8_b16(rows, cols);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          *reinterpret_cast<u32x4*>(at + (jp * 8 + t) * LDS_KS + kp * 8) = cols[t];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const u32x4 af =
+            *reinterpret_cast<const u32x4*>(at + (16 * wave + li) * LDS_KS + 32 * st + 8 * g);
+        acc = mfma16(af, xf[st], acc);
+      }
+      __syncthreads();
+    }
+    const int j = j0 + 16 * wave + 4 * g;
+    if (m_ok && j < r)
+      *reinterpret_cast<f32x4*>(ws + ((int64_t)blockIdx.x * M + li) * r + j) = acc;
   }
 }
 
@@ -548,6 +618,8 @@ constexpr int RB_X = 128;    // tile of the long dimension
 
 size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r) {
   if (r <= 0) return 0;
+  if (M <= 16)
+    return (size_t)lora_down_partial_count(K) * M * r + rank_ws_floats(17, N, K, r);
   const int64_t rt = (r + RB_R - 1) / RB_R;
   const Split t = choose_split(K, rt, (M + RB_X - 1) / RB_X);
   const Split g = choose_split(N, rt, (M + RB_X - 1) / RB_X);
@@ -572,8 +644,36 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
   return hipGetLastError();
 }
 
+int lora_down_partial_count(int64_t K) {
+  const int64_t slices = (K + LDS_K - 1) / LDS_K;
+  const int64_t spw = (slices + kMaxDownPartials - 1) / kMaxDownPartials;
+  return static_cast<int>((slices + spw - 1) / spw);
+}
+
+hipError_t launch_lora_down_partials(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A,
+                                     int r, float* ws, int* nz, hipStream_t stream) {
+  const int64_t slices = (K + LDS_K - 1) / LDS_K;
+  const int spw = static_cast<int>((slices + kMaxDownPartials - 1) / kMaxDownPartials);
+  *nz = lora_down_partial_count(K);
+  prof_begin(4, stream);
+  hipLaunchKernelGGL(k_lora_down_small, dim3(*nz), dim3(256), 0, stream, X, (int)M, K, A, r, spw,
+                     ws);
+  prof_end(4, stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A,
                             int r, float* T, float* ws, hipStream_t stream) {
+  if (M <= 16) {
+    int nz = 0;
+    hipError_t e = launch_lora_down_partials(X, M, K, A, r, ws, &nz, stream);
+    if (e == hipSuccess) {
+      prof_begin(4, stream);
+      e = reduce<false>(ws, nz, M * r, 1.f, T, stream);
+      prof_end(4, stream);
+    }
+    return e;
+  }
   const int64_t pt = (r + RB_R - 1) / RB_R, qt = (M + RB_X - 1) / RB_X;
   const Split sp = choose_split(K, pt, qt);
   prof_begin(4, stream);

@@ -37,9 +37,12 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
                            uint16_t* Y, const Nf4Tables& tb, hipStream_t stream);
 
 // Same result, small-M (M <= 16) streaming path.
+// With nz > 0, T holds nz partial sums [nz][M][r] of X . A which the kernel
+// adds up itself (workgroup 0 also writes the total to Tout); with nz == 0, T
+// is the final [M][r] and Tout is unused.
 hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
-                             const float* T, const uint16_t* B, int r, float s,
-                             uint16_t* Y, const Nf4Tables& tb, hipStream_t stream);
+                             const float* T, int nz, float* Tout, const uint16_t* B, int r,
+                             float s, uint16_t* Y, const Nf4Tables& tb, hipStream_t stream);
 
 // dX[M,K] = bf16( dY . deq(W) + s . G . A^T ).
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
@@ -48,6 +51,13 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
 
 // Rank-r products with a split reduction; partials go to `ws`.
 size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r);
+
+// Few-token LoRA down-projection: at most kMaxDownPartials fp32 partial sums
+// [nz][M][r] of T = X . A go to ws (nz returned); M <= 16.
+constexpr int kMaxDownPartials = 32;
+int lora_down_partial_count(int64_t K);
+hipError_t launch_lora_down_partials(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A,
+                                     int r, float* ws, int* nz, hipStream_t stream);
 
 // T[M,r] = X . A (fp32 out).
 hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K,

@@ -246,3 +246,26 @@ def test_config3_full_size_recompute(lin_idx):
     _, dAr, dBr = oracle.linear_bwd(inp.dY, inp.X, What, inp.A, inp.B, cfg.s, need_dx=False)
     assert_close("dA", dA.float().cpu().numpy(), dAr)
     assert_close("dB", dB.float().cpu().numpy(), dBr)
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF, 0x5A])
+def test_workspace_contents_do_not_matter(fill):
+    """The forward workspace needs no initialisation: prefilled garbage, and
+    reuse across calls of different shapes, give the same bitwise output."""
+    need_gpu()
+    say(f"workspace fill=0x{fill:02x}")
+    c = Case(4, 512, 2048, 64, 0.25, seed=21)
+    c2 = Case(16, 256, 1024, 32, 0.5, seed=22)
+    need = max(q.lib().qlora_linear_fwd_workspace_bytes(4, 512, 2048, 64),
+               q.lib().qlora_linear_fwd_workspace_bytes(16, 256, 1024, 32))
+    ws = torch.full((need,), fill, dtype=torch.uint8, device=dev())
+    Y1, T1 = q.qlora_linear_fwd(c.X, c.w, c.A, c.B, c.s, workspace=ws)
+    Y1, T1 = bits(Y1), T1.cpu().numpy()
+    q.qlora_linear_fwd(c2.X, c2.w, c2.A, c2.B, c2.s, workspace=ws)
+    Y2, T2 = q.qlora_linear_fwd(c.X, c.w, c.A, c.B, c.s, workspace=ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(Y2), Y1)
+    np.testing.assert_array_equal(T2.cpu().numpy(), T1)
+    Yr, Tr = c.ref_fwd()
+    assert_close("Y", oracle.bf16_bits_to_f64(Y1), Yr)
+    assert_close("T", T1, Tr)
