@@ -1,7 +1,6 @@
 // MFMA GEMMs of the QLoRA NF4 linear layer on gfx950.
 //
-// Every product here (the backward dX and the rank-r products; the forward
-// GEMM has its own kernel) has the form C[q, p] = sum_k P[p, k] . Q[q, k]: the
+// The rank-r products (T = X.A, G = dY.B^T, dA, dB) have the form C[q, p] = sum_k P[p, k] . Q[q, k]: the
 // workgroup stages a P tile [BP x 64] and a Q tile [BQ x 64] in LDS, both
 // laid out reduction-contiguous ("MFMA ready": a lane's 8 reduction elements
 // are one 16-byte LDS read), and four waves (2 x 2) accumulate their
@@ -9,18 +8,9 @@
 // operand into that layout whatever its layout in HBM:
 //   Bf16Nat  bf16 rows, reduction contiguous          (X, dY, B as [r,N], A as [K,r])
 //   Bf16Tr   bf16 with the reduction as the row index (X^T, dY^T, B^T)
-//   F32Nat / F32Tr  fp32 (T, G) split into bf16 hi and lo passes
-//   Nf4Nat   the NF4 weight with rows n, reduction k (forward): dequantized
-//            in registers from 16-byte code loads, written to LDS as bf16
-//   Nf4Tr    the NF4 weight with rows k, reduction n (backward dX): 8 x 8
-//            patches dequantized and packed across rows
-// The dequantization (Mathematical Formulation of "DL0087 QLoRA": a bf16 tile
-// is rebuilt just before the matmul and discarded) happens once per
-// workgroup tile; no bf16 copy of the weight ever reaches HBM.
-//
-// The fused LoRA terms are extra reduction steps over the rank dimension
-// appended to the main loop (forward: s.T.B; dX: s.G.A^T), with the fp32
-// factor split into bf16 hi + lo so the adapter term keeps ~16 bits.
+//   F32Nat / F32Tr  fp32 (T, G) split into bf16 hi and lo passes, so the
+//            fp32 factor keeps ~16 bits through the bf16 MFMA
+// The weight-streaming GEMMs (forward and dX) have kernels of their own.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -210,104 +200,6 @@ struct F32Tr {     // element (row, k) = scale * src[k * ld + row], fp32 source
   }
 };
 
-template <int ROWS>
-struct Nf4Nat {    // element (n, k) = deq(W)[n, k]; one thread = half a block
-  static constexpr int CH = ROWS * 2;
-  static constexpr int CPT = (CH + NT - 1) / NT;
-  OpParams o;
-  int64_t row0;
-  const float2* tab;
-  u32x4 r[CPT];
-  uint32_t ce[CPT];
-  float cd[CPT];
-  __device__ void load(int kt, int tid) {
-    const uint8_t* codes = static_cast<const uint8_t*>(o.ptr);
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      const int64_t n = row0 + (idx >> 1);
-      const int half = idx & 1;
-      if (idx < CH && n < o.N) {
-        const int64_t blk = n * (o.K / kBlock) + kt;
-        r[c] = ld16(codes + n * (o.K / 2) + (int64_t)kt * 32 + half * 16);
-        ce[c] = o.absmax_q[blk];
-        cd[c] = o.absmax_scale[blk >> 8];
-      } else {
-        r[c] = u32x4{0, 0, 0, 0};
-        ce[c] = 0;
-        cd[c] = 0.f;
-      }
-    }
-  }
-  __device__ void store(uint16_t* lds, int tid) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      if (idx < CH) {
-        uint16_t* dst = lds + (idx >> 1) * LDS_STRIDE + (idx & 1) * 32;
-        const float chat = static_cast<float>(ce[c]) * cd[c];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st_lds16(dst + 8 * i, dequant8(r[c][i], chat, tab));
-      }
-    }
-  }
-};
-
-template <int ROWS>
-struct Nf4Tr {     // element (k, n) = deq(W)[n, k]: rows k, reduction n
-  static constexpr int NP = ROWS;                 // 8 (n) x 8 (k) patches
-  static constexpr int PPT = (NP + NT - 1) / NT;
-  static constexpr int KS = ROWS / 8;
-  OpParams o;
-  int64_t row0;
-  const float2* tab;
-  uint32_t r[PPT][8];
-  uint32_t ce[PPT][8];   // 8-bit block constants and fp32 group scales, as
-  float cd[PPT][8];      // loaded; multiplied out in store()
-  __device__ void load(int kt, int tid) {
-    const uint8_t* codes = static_cast<const uint8_t*>(o.ptr);
-#pragma unroll
-    for (int c = 0; c < PPT; ++c) {
-      const int p = tid + c * NT;
-      const int kp = p % KS, np = p / KS;
-      const int64_t k = row0 + kp * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t n = (int64_t)kt * BK + np * 8 + i;
-        if (p < NP && n < o.N && k < o.K) {
-          const int64_t blk = n * (o.K / kBlock) + k / kBlock;
-          r[c][i] = *reinterpret_cast<const uint32_t*>(codes + n * (o.K / 2) + k / 2);
-          ce[c][i] = o.absmax_q[blk];
-          cd[c][i] = o.absmax_scale[blk >> 8];
-        } else {
-          r[c][i] = 0;
-          ce[c][i] = 0;
-          cd[c][i] = 0.f;
-        }
-      }
-    }
-  }
-  __device__ void store(uint16_t* lds, int tid) {
-#pragma unroll
-    for (int c = 0; c < PPT; ++c) {
-      const int p = tid + c * NT;
-      if (p < NP) {
-        const int kp = p % KS, np = p / KS;
-        float v[8][8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          dequant8_f32(r[c][i], static_cast<float>(ce[c][i]) * cd[c][i], tab, v[i]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const u32x4 o4 = {pack_bf16x2(v[0][j], v[1][j]), pack_bf16x2(v[2][j], v[3][j]),
-                            pack_bf16x2(v[4][j], v[5][j]), pack_bf16x2(v[6][j], v[7][j])};
-          st_lds16(lds + (kp * 8 + j) * LDS_STRIDE + np * 8, o4);
-        }
-      }
-    }
-  }
-};
-
 // ---------------------------------------------------------------------------
 // MFMA tile step and the double-buffered tile loop
 // ---------------------------------------------------------------------------
@@ -406,38 +298,6 @@ __device__ void store_f32(const Mma<BP, BQ>& mma, float* out, int64_t ldo,
       const int64_t p = wp + 16 * i, q = wq + 16 * j;
       if (p < P && q < Q) *reinterpret_cast<f32x4*>(out + q * ldo + p) = mma.acc[i][j];
     }
-}
-
-// ---------------------------------------------------------------------------
-// Backward dX = dY . deq(W) + s . G . A^T.  P = k, Q = m.
-// ---------------------------------------------------------------------------
-
-constexpr int DBP = 128, DBQ = 128;
-
-__global__ __launch_bounds__(NT) void k_dx_gemm(OpParams w, OpParams dy, OpParams al,
-                                                OpParams gl, int r, uint16_t* dX,
-                                                int64_t M, int64_t K, Nf4Tables tb) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (DBP + DBQ) * LDS_STRIDE];
-  __shared__ float2 tab[256];
-  const int tid = threadIdx.x;
-  build_pair_table(tab, tb, tid, NT);
-  const int64_t p0 = (int64_t)blockIdx.x * DBP, q0 = (int64_t)blockIdx.y * DBQ;
-  Mma<DBP, DBQ> mma;
-  mma.zero();
-  {
-    Nf4Tr<DBP> lp{w, p0, tab};
-    Bf16Nat<DBQ> lq{dy, q0};
-    run_tiles<DBP, DBQ>(lp, lq, 0, (int)((w.N + BK - 1) / BK), mma, lds, tid);
-  }
-  if (r > 0) {
-    const int nt = (r + BK - 1) / BK;
-    Bf16Nat<DBP> lp{al, p0};
-    for (int pass = 0; pass < 2; ++pass) {
-      F32Nat<DBQ> lq{gl, q0, pass};
-      run_tiles<DBP, DBQ>(lp, lq, 0, nt, mma, lds, tid);
-    }
-  }
-  store_bf16(mma, dX, K, p0, q0, K, M, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -631,17 +491,6 @@ size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r) {
   m = std::max<size_t>(m, (size_t)a.splits * K * r);
   m = std::max<size_t>(m, (size_t)b.splits * r * N);
   return m;
-}
-
-hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
-                          const float* G, const uint16_t* A, int r, float s,
-                          uint16_t* dX, const Nf4Tables& tb, hipStream_t stream) {
-  dim3 grid(cdiv(w.K, DBP), cdiv(M, DBQ));
-  prof_begin(1, stream);
-  hipLaunchKernelGGL(k_dx_gemm, grid, dim3(NT), 0, stream, nf4op(w), op(dY, w.N, M, w.N),
-                     op(A, r, w.K, r), op(G, r, M, r, s), r, dX, M, w.K, tb);
-  prof_end(1, stream);
-  return hipGetLastError();
 }
 
 int lora_down_partial_count(int64_t K) {
