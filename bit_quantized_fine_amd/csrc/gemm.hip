@@ -155,6 +155,18 @@ struct F32Nat {    // element (row, k) = scale * src[row * ld + k], fp32 source
                  f32x8_to_bf16(r[c][0], r[c][1], o.scale, pass));
     }
   }
+  // both halves at once: hi into `hi`, lo into `lo`
+  __device__ void store2(uint16_t* hi, uint16_t* lo, int tid) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      if (idx < CH) {
+        const int off = (idx >> 3) * LDS_STRIDE + (idx & 7) * 8;
+        st_lds16(hi + off, f32x8_to_bf16(r[c][0], r[c][1], o.scale, 0));
+        st_lds16(lo + off, f32x8_to_bf16(r[c][0], r[c][1], o.scale, 1));
+      }
+    }
+  }
 };
 
 template <int ROWS>
@@ -195,6 +207,26 @@ struct F32Tr {     // element (row, k) = scale * src[k * ld + row], fp32 source
         transpose8x8_b16(rows, t);
 #pragma unroll
         for (int j = 0; j < 8; ++j) st_lds16(lds + (rp * 8 + j) * LDS_STRIDE + kp * 8, t[j]);
+      }
+    }
+  }
+  __device__ void store2(uint16_t* hi, uint16_t* lo, int tid) {
+#pragma unroll
+    for (int c = 0; c < PPT; ++c) {
+      const int p = tid + c * NT;
+      if (p < NP) {
+        const int rp = p % RS, kp = p / RS;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4 rows[8], t[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            rows[i] = f32x8_to_bf16(r[c][i][0], r[c][i][1], o.scale, half);
+          transpose8x8_b16(rows, t);
+          uint16_t* dst = half ? lo : hi;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) st_lds16(dst + (rp * 8 + j) * LDS_STRIDE + kp * 8, t[j]);
+        }
       }
     }
   }
@@ -265,6 +297,51 @@ __device__ void run_tiles(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mma,
   }
 }
 
+// Same tile loop with one operand an fp32 source split into bf16 hi and lo
+// halves (HL = 1: the P operand, HL = 2: the Q operand): both halves are
+// staged per tile and multiplied against the other operand, which is loaded
+// once.  Buffer layout: [P or P_hi][Q or Q_hi][second half].
+template <int BP, int BQ, int HL, class LP, class LQ>
+__device__ void run_tiles_hilo(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mma,
+                               uint16_t* lds, int tid) {
+  if (kt0 >= kt1) return;
+  constexpr int XR = HL == 1 ? BP : BQ;   // rows of the extra (lo) tile
+  constexpr int BUF = (BP + BQ + XR) * LDS_STRIDE;
+  const int wave = tid >> 6, lane = tid & 63;
+  auto P = [&](int b) { return lds + b * BUF; };
+  auto Q = [&](int b) { return lds + b * BUF + BP * LDS_STRIDE; };
+  auto X = [&](int b) { return lds + b * BUF + (BP + BQ) * LDS_STRIDE; };
+  auto store = [&](int b) {
+    if constexpr (HL == 1) {
+      lp.store2(P(b), X(b), tid);
+      lq.store(Q(b), tid);
+    } else {
+      lp.store(P(b), tid);
+      lq.store2(Q(b), X(b), tid);
+    }
+  };
+  lp.load(kt0, tid);
+  lq.load(kt0, tid);
+  __syncthreads();
+  store(0);
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) {
+      lp.load(kt + 1, tid);
+      lq.load(kt + 1, tid);
+    }
+    mma.step(P(cur), Q(cur), wave, lane);
+    if constexpr (HL == 1)
+      mma.step(X(cur), Q(cur), wave, lane);
+    else
+      mma.step(P(cur), X(cur), wave, lane);
+    if (more) store(cur ^ 1);
+    __syncthreads();
+  }
+}
+
 // Stores C[q, p] as bf16 (lane holds 4 consecutive p of one q per tile).
 template <int BP, int BQ>
 __device__ void store_bf16(const Mma<BP, BQ>& mma, uint16_t* out, int64_t ldo,
@@ -304,29 +381,26 @@ __device__ void store_f32(const Mma<BP, BQ>& mma, float* out, int64_t ldo,
 // Rank-r products with a split reduction: partial sums of C[q, p] for
 // reduction tiles [z*tps, (z+1)*tps) go to ws[z][q][p]; a second kernel sums
 // the partials in split order (deterministic) and writes the result.
-// PASSES = 2 runs the tiles twice with the fp32 operand's hi and lo parts.
 // ---------------------------------------------------------------------------
 
-template <int BP, int BQ, class LP, class LQ, int PASSES>
+// HL: 0 = both operands bf16; 1 = P is fp32 (hi/lo); 2 = Q is fp32 (hi/lo).
+template <int BP, int BQ, class LP, class LQ, int HL>
 __global__ __launch_bounds__(NT) void k_rank(OpParams po, OpParams qo, int ntiles,
                                              int tps, float* ws, int64_t P, int64_t Q) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BP + BQ) * LDS_STRIDE];
+  constexpr int XR = HL == 0 ? 0 : (HL == 1 ? BP : BQ);
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BP + BQ + XR) * LDS_STRIDE];
   const int tid = threadIdx.x;
   const int64_t p0 = (int64_t)blockIdx.x * BP, q0 = (int64_t)blockIdx.y * BQ;
   const int z = blockIdx.z;
   const int kt0 = z * tps, kt1 = min(ntiles, kt0 + tps);
   Mma<BP, BQ> mma;
   mma.zero();
-  for (int pass = 0; pass < PASSES; ++pass) {
-    LP lp{po, p0};
-    LQ lq{qo, q0};
-    if constexpr (PASSES == 2) {
-      // exactly one of the two operands is an fp32 hi/lo source
-      if constexpr (requires { lp.pass; }) lp.pass = pass;
-      if constexpr (requires { lq.pass; }) lq.pass = pass;
-    }
+  LP lp{po, p0};
+  LQ lq{qo, q0};
+  if constexpr (HL == 0)
     run_tiles<BP, BQ>(lp, lq, kt0, kt1, mma, lds, tid);
-  }
+  else
+    run_tiles_hilo<BP, BQ, HL>(lp, lq, kt0, kt1, mma, lds, tid);
   store_f32(mma, ws + (int64_t)z * P * Q, P, p0, q0, P, Q, tid);
 }
 
@@ -526,7 +600,7 @@ hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint1
   const int64_t pt = (r + RB_R - 1) / RB_R, qt = (M + RB_X - 1) / RB_X;
   const Split sp = choose_split(K, pt, qt);
   prof_begin(4, stream);
-  hipLaunchKernelGGL((k_rank<RB_R, RB_X, Bf16Tr<RB_R>, Bf16Nat<RB_X>, 1>),
+  hipLaunchKernelGGL((k_rank<RB_R, RB_X, Bf16Tr<RB_R>, Bf16Nat<RB_X>, 0>),
                      dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(A, r, r, K),
                      op(X, K, M, K), sp.ntiles, sp.tps, ws, (int64_t)r, M);
   hipError_t e = hipGetLastError();
@@ -541,7 +615,7 @@ hipError_t launch_lora_grad_in(const uint16_t* dY, int64_t M, int64_t N,
   const int64_t pt = (r + RB_R - 1) / RB_R, qt = (M + RB_X - 1) / RB_X;
   const Split sp = choose_split(N, pt, qt);
   prof_begin(4, stream);
-  hipLaunchKernelGGL((k_rank<RB_R, RB_X, Bf16Nat<RB_R>, Bf16Nat<RB_X>, 1>),
+  hipLaunchKernelGGL((k_rank<RB_R, RB_X, Bf16Nat<RB_R>, Bf16Nat<RB_X>, 0>),
                      dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(B, N, r, N),
                      op(dY, N, M, N), sp.ntiles, sp.tps, ws, (int64_t)r, M);
   hipError_t e = hipGetLastError();
@@ -555,7 +629,7 @@ hipError_t launch_grad_a(const uint16_t* X, int64_t M, int64_t K, const float* G
   const int64_t pt = (r + RB_R - 1) / RB_R, qt = (K + RB_X - 1) / RB_X;
   const Split sp = choose_split(M, pt, qt);
   prof_begin(4, stream);
-  hipLaunchKernelGGL((k_rank<RB_R, RB_X, F32Tr<RB_R>, Bf16Tr<RB_X>, 2>),
+  hipLaunchKernelGGL((k_rank<RB_R, RB_X, F32Tr<RB_R>, Bf16Tr<RB_X>, 1>),
                      dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(G, r, r, M),
                      op(X, K, K, M), sp.ntiles, sp.tps, ws, (int64_t)r, K);
   hipError_t e = hipGetLastError();
