@@ -127,7 +127,7 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
     g.manual_seed(2000)
     out = {}
     for M in cfg.M:
-        tot_bytes, tot_ms, kern_ms, kern_n = 0.0, 0.0, 0.0, 0
+        tot_bytes, tot_ms, kern_bytes, kern_ms = 0.0, 0.0, 0.0, 0.0
         per_shape = {}
         for lin in cfg.linears:
             N, K = lin.N, lin.K
@@ -149,8 +149,7 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
             for w in pool[:2]:
                 q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
             torch.cuda.synchronize()
-            q.qlora_profile_reset()
-            q.qlora_profile_enable(True)
+            # per-call rate: profiler off, so no events between the launches
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ev0.record()
             calls = 0
@@ -160,8 +159,15 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
                     calls += 1
             ev1.record()
             torch.cuda.synchronize()
-            q.qlora_profile_enable(False)
             ms = ev0.elapsed_time(ev1)
+            # decode-kernel time alone: a second pass with the launch profiler on
+            q.qlora_profile_reset()
+            q.qlora_profile_enable(True)
+            for _ in range(max(1, reps // 4)):
+                for w in pool:
+                    q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
+            torch.cuda.synchronize()
+            q.qlora_profile_enable(False)
             kms, kn = q.qlora_profile_read(2)
             alg = nf4_bytes + 2 * (M * K + M * N + K * r + r * N)
             per_shape[f"{N}x{K}"] = dict(us_per_call=1e3 * ms / calls,
@@ -171,12 +177,12 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
                                          copies=copies)
             tot_bytes += alg * calls
             tot_ms += ms
+            kern_bytes += alg * kn
             kern_ms += kms
-            kern_n += kn
             del pool
             torch.cuda.empty_cache()
         out[f"M={M}"] = dict(gbs_call=tot_bytes / (tot_ms * 1e-3) / 1e9,
-                             gbs_decode_kernel=tot_bytes / (kern_ms * 1e-3) / 1e9,
+                             gbs_decode_kernel=kern_bytes / (kern_ms * 1e-3) / 1e9,
                              shapes=per_shape)
         log(f"decode M={M}: {out[f'M={M}']['gbs_call']:.0f} GB/s per call, "
             f"{out[f'M={M}']['gbs_decode_kernel']:.0f} GB/s decode kernel")
@@ -185,8 +191,8 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
 
 def run_cpu_baseline(train):
     """The oracle (dequantize + forward + backward, float64 products) on a
-    bounded sample of the same workload: the q and gate linears of the seven,
-    full M, on this host's cores."""
+    bounded sample of the same workload: all seven linears once at full M
+    (one training step), on this host's cores."""
     import numpy as np
 
     import oracle
@@ -200,7 +206,7 @@ def run_cpu_baseline(train):
     flops, secs = 0, 0.0
     ctx = threadpool_limits(cores) if threadpool_limits else None
     try:
-        for idx in (0, 4):
+        for idx in range(len(cfg.linears)):
             (lin, inp), = list(workloads.config_inputs(1, linears=[idx]))
             codes, e, d, _ = oracle.quantize(inp.W)       # load-time, untimed
             t0 = time.perf_counter()
@@ -219,9 +225,53 @@ def run_cpu_baseline(train):
             ctx.__exit__(None, None, None)
     return dict(value=flops / secs / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
                 seconds=secs,
-                sample="linears q [4096x4096] and gate [11008x4096] of the seven, M=2048, "
-                       "r=64: oracle dequantize + fwd + bwd (float64 products), "
-                       "quantization untimed")
+                sample="one step: all seven linears, M=2048, r=64: oracle dequantize + "
+                       "fwd + bwd (float64 products); load-time quantization untimed")
+
+
+def _rocprof_csvs(root, suffix):
+    out = []
+    for d, _, files in os.walk(root):
+        out += [os.path.join(d, f) for f in files if f.endswith(suffix)]
+    return sorted(out)
+
+
+def summarize_rocprof(root, copy_mib, top=16):
+    """Text summary of a rocprofv3 output folder (csv format): the kernel
+    statistics table, and per-dispatch counter means per kernel.  With a
+    calibration copy of `copy_mib` MiB in the run, the FETCH_SIZE/WRITE_SIZE
+    scale factors (bytes moved / counter bytes) are printed too."""
+    import csv
+    lines = []
+    for path in _rocprof_csvs(root, "kernel_stats.csv"):
+        rows = list(csv.DictReader(open(path)))
+        rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+        lines.append(f"{'kernel':70s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
+                     f"{'max_us':>9s} {'total_%':>7s}")
+        for r in rows[:top]:
+            lines.append(f"{r['Name'][:70]:70s} {int(r['Calls']):6d} "
+                         f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                         f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):7.2f}")
+    traffic = {}
+    for path in _rocprof_csvs(root, "counter_collection.csv"):
+        agg = {}
+        for r in csv.DictReader(open(path)):
+            key = (r["Kernel_Name"], r["Counter_Name"])
+            agg.setdefault(key, []).append(float(r["Counter_Value"]))
+        lines.append(f"{'kernel':70s} {'counter':>12s} {'dispatches':>10s} {'mean_per_dispatch':>18s}")
+        for (k, c), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+            mean = sum(v) / len(v)
+            traffic.setdefault(k, {})[c] = (mean, len(v))
+            lines.append(f"{k[:70]:70s} {c:>12s} {len(v):10d} {mean:18.1f}")
+        if copy_mib:
+            exp_kib = copy_mib * 1024.0
+            for k, cs in traffic.items():
+                if "neg" in k:
+                    for c, (mean, n) in cs.items():
+                        if c in ("FETCH_SIZE", "WRITE_SIZE"):
+                            lines.append(f"calibration copy ({k[:40]}): {c} {mean:.0f} KiB for "
+                                         f"{exp_kib:.0f} KiB moved -> scale {exp_kib / mean:.4f}")
+    return "\n".join(lines)
 
 
 def main():
@@ -231,7 +281,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain elementwise copy (torch.neg) of this many MiB before "
+                         "the step, as the yardstick for rocprofv3 FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="print a text summary of a rocprofv3 csv output folder and exit")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        print(summarize_rocprof(args.summarize_rocprof, args.copy_calibration_mib))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -245,6 +303,14 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     q.lib()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 18          # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     tr = run_training(q, torch, args.steps, args.warmup, dev)
     value = tr["flops_step"] / (tr["ms_step"] * 1e-3) / 1e12
