@@ -72,9 +72,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+constexpr int64_t kMaxK = int64_t(1) << 24;        // longest reduction dimension
+constexpr int64_t kMaxElems = int64_t(1) << 32;    // N * K of one weight
+
 int check_weight(const qlora_nf4_weight* w) {
   if (!w || !w->codes || !w->absmax_q || !w->absmax_scale) return QLORA_ERR_NULL;
   if (w->N < 1 || w->K < kBlock || w->K % kBlock != 0) return QLORA_ERR_SHAPE;
+  // kernels address the code stream with 32-bit byte offsets
+  if (w->K > kMaxK || w->N > kMaxElems / w->K) return QLORA_ERR_SHAPE;
   if (!aligned16(w->codes) || (reinterpret_cast<uintptr_t>(w->absmax_scale) & 3u))
     return QLORA_ERR_ALIGN;
   return QLORA_OK;
@@ -107,9 +112,6 @@ size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
 // ---------------------------------------------------------------------------
 
 constexpr int kFamilies = 5;
-
-// Token counts up to this fold the T reduction into the decode kernel.
-constexpr int64_t kFewTokensFoldT = 4;
 
 struct Profiler {
   std::mutex mu;
@@ -230,6 +232,7 @@ int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
                        uint8_t* absmax_q, float* absmax_scale, qlora_stream_t stream) {
   if (!W || !codes || !absmax_q || !absmax_scale) return QLORA_ERR_NULL;
   if (N < 1 || K < kBlock || K % kBlock != 0) return QLORA_ERR_SHAPE;
+  if (K > kMaxK || N > kMaxElems / K) return QLORA_ERR_SHAPE;
   if (!aligned16(W) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(absmax_scale) & 3u))
     return QLORA_ERR_ALIGN;
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -278,7 +281,8 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
   const Nf4View v = view(w);
   hipError_t e = hipSuccess;
   float* ws = static_cast<float*>(workspace);
-  if (M <= kFewTokensFoldT && r > 0) {
+  const bool decode = decode_fits(M, w->K);
+  if (decode && decode_folds_t(M, r)) {
     // T's partial sums are added up inside the decode kernel (no reduction
     // launch); its workgroup 0 writes T.
     int nz = 0;
@@ -288,7 +292,7 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
   }
   if (r > 0) e = launch_lora_down(X, M, w->K, A, r, T, ws, hs);
   if (e != hipSuccess) return QLORA_ERR_HIP;
-  if (M <= 16)
+  if (decode)
     e = launch_fwd_decode(X, M, v, T, 0, nullptr, B, r, s, Y, tables(), hs);
   else
     e = launch_fwd_gemm(X, M, v, T, B, r, s, Y, tables(), hs);

@@ -25,6 +25,14 @@ struct Nf4Tables {
 constexpr int kBlock = 64;    // weights per absmax constant
 constexpr int kGroup = 256;   // constants per fp32 second-level scale
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: branches on it are scalar branches, never EXEC-masked ones.  An MFMA
+// placed under an EXEC-masked branch still runs for a wave whose mask is
+// empty, so MFMAs may only sit under conditions the compiler sees as uniform.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+}
+
 // Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 // `a` lands in the low half (the lower-addressed element).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

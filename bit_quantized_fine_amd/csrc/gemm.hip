@@ -274,7 +274,7 @@ __device__ void run_tiles(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mma,
   if (kt0 >= kt1) return;
   uint16_t* bufP[2] = {lds, lds + (BP + BQ) * LDS_STRIDE};
   uint16_t* bufQ[2] = {lds + BP * LDS_STRIDE, lds + (2 * BP + BQ) * LDS_STRIDE};
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = wave_id(), lane = tid & 63;
   lp.load(kt0, tid);
   lq.load(kt0, tid);
   __syncthreads();
@@ -307,7 +307,7 @@ __device__ void run_tiles_hilo(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mm
   if (kt0 >= kt1) return;
   constexpr int XR = HL == 1 ? BP : BQ;   // rows of the extra (lo) tile
   constexpr int BUF = (BP + BQ + XR) * LDS_STRIDE;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = wave_id(), lane = tid & 63;
   auto P = [&](int b) { return lds + b * BUF; };
   auto Q = [&](int b) { return lds + b * BUF + BP * LDS_STRIDE; };
   auto X = [&](int b) { return lds + b * BUF + (BP + BQ) * LDS_STRIDE; };
@@ -346,7 +346,7 @@ __device__ void run_tiles_hilo(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mm
 template <int BP, int BQ>
 __device__ void store_bf16(const Mma<BP, BQ>& mma, uint16_t* out, int64_t ldo,
                            int64_t p0, int64_t q0, int64_t P, int64_t Q, int tid) {
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = wave_id(), lane = tid & 63;
   const int64_t wp = p0 + (wave & 1) * (BP / 2) + 4 * (lane >> 4);
   const int64_t wq = q0 + (wave >> 1) * (BQ / 2) + (lane & 15);
 #pragma unroll
@@ -365,7 +365,7 @@ __device__ void store_bf16(const Mma<BP, BQ>& mma, uint16_t* out, int64_t ldo,
 template <int BP, int BQ>
 __device__ void store_f32(const Mma<BP, BQ>& mma, float* out, int64_t ldo,
                           int64_t p0, int64_t q0, int64_t P, int64_t Q, int tid) {
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = wave_id(), lane = tid & 63;
   const int64_t wp = p0 + (wave & 1) * (BP / 2) + 4 * (lane >> 4);
   const int64_t wq = q0 + (wave >> 1) * (BQ / 2) + (lane & 15);
 #pragma unroll
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
                                                          int r, int spw, float* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) uint16_t at[64 * LDS_KS];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = wave_id(), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const bool m_ok = li < M;
   for (int j0 = 0; j0 < r; j0 += 64) {

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd_gemm2(
   __shared__ float2 tab[256];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = wave_id(), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   build_pair_table(tab, tb, tid, NT_);
 

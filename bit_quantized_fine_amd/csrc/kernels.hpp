@@ -36,7 +36,10 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
                            const float* T, const uint16_t* B, int r, float s,
                            uint16_t* Y, const Nf4Tables& tb, hipStream_t stream);
 
-// Same result, small-M (M <= 16) streaming path.
+// Same result, small-M streaming path, for shapes with decode_fits(M, K).
+// decode_folds_t(M, r): the kernel can add up T's partial sums itself.
+bool decode_fits(int64_t M, int64_t K);
+bool decode_folds_t(int64_t M, int r);
 // With nz > 0, T holds nz partial sums [nz][M][r] of X . A which the kernel
 // adds up itself (workgroup 0 also writes the total to Tout); with nz == 0, T
 // is the final [M][r] and Tout is unused.

@@ -1,5 +1,5 @@
-// NF4 quantization with double quantization (S2-S3), and standalone
-// dequantization to bf16 (S4 as an op of its own).
+// NF4 quantization with double quantization, and standalone
+// dequantization to bf16 (an op of its own).
 //
 // Format (list items (2) and (3) of "DL0087 QLoRA: 4-bit Quantized LoRA";
 // "Double Quantization and Paged Optimizers" of "QLoRA: Finetuning 65B Models

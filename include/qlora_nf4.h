@@ -110,20 +110,22 @@ size_t qlora_nf4_scale_count(int64_t N, int64_t K);
 
 /*
  * Quantize a float32 weight W [N, K] (device) to NF4 with double
- * quantization (S2-S3; list items (1)-(3) of "DL0087 QLoRA").
+ * quantization (list items (1)-(3) of "DL0087 QLoRA").
  * Per block: c = max|w|, x = fl32(w / c) (IEEE divide), code = nearest
  * level (lower on ties); an all-zero block gets c = 0 and code 7.
  * Per group of 256 blocks: d = fl32(max c / 255), e = rint_even(fl32(c / d))
  * clamped to [0, 255] (e = 0 when d = 0).  The codes use the unquantized c.
  * Outputs (device): codes [N*K/2], absmax_q [N*K/64], absmax_scale
- * [ceil(N*K/16384)].  W must be finite.  N >= 1, K >= 64, K % 64 == 0.
+ * [ceil(N*K/16384)].  W must be finite.  N >= 1, K >= 64, K % 64 == 0,
+ * K <= 2^24 and N*K <= 2^32 (the kernels address a weight's codes with
+ * 32-bit byte offsets); the same limits apply to every qlora_nf4_weight.
  */
 int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
                        uint8_t* absmax_q, float* absmax_scale,
                        qlora_stream_t stream);
 
 /*
- * Dequantize W to bf16 (S4 as a standalone op; Mathematical Formulation of
+ * Dequantize W to bf16 (a standalone op; Mathematical Formulation of
  * "DL0087 QLoRA").  W_bf16 [N, K] (device, bf16 bit patterns) receives
  * bf16_rne(fl32(level[code] * fl32(e * d))).  The training path never
  * materialises this tensor; this entry point exists for inspection.
@@ -138,7 +140,7 @@ int qlora_nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16,
 size_t qlora_linear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
 
 /*
- * Forward (S5-S7; Mathematical Formulation and Figure 1 of "DL0087 QLoRA";
+ * Forward (Mathematical Formulation and Figure 1 of "DL0087 QLoRA";
  * "The Quantization Layer" of "QLoRA: Quantized Low Rank Adaptation at
  * Extreme Scale": dequantize to bf16 on the fly, matmul, add the LoRA update).
  *   X  [M, K] bf16 (device)          Y [M, N] bf16 (device, output)
@@ -162,7 +164,7 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
 size_t qlora_linear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
 
 /*
- * Backward (S8-S10; list item (4) of "DL0087 QLoRA": gradients pass through
+ * Backward (list item (4) of "DL0087 QLoRA": gradients pass through
  * the frozen 4-bit weights and are stored only for the adapters; the
  * backward dequantizes again; "The Efficient Symphony of the QLoRA
  * Workflow" of "QLoRA (Quantized Low-Rank Adaptation)").

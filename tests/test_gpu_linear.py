@@ -54,7 +54,11 @@ FWD_CASES = [
     (4, 1024, 1024, 16, 1.0),
     (16, 1024, 1024, 16, 1.0),
     (7, 200, 320, 8, 0.5),           # ragged N (not a multiple of 16), K = 5 * 64
-    (16, 1000, 64 * 33, 64, 0.25),   # K with a half chunk
+    (16, 1000, 64 * 33, 64, 0.25),   # K with a half chunk; X read from global memory
+    (1, 232, 64 * 33, 32, 0.5),      # K with a half chunk; X staged in LDS
+    (4, 96, 16384, 64, 0.25),        # T folded, X too large for LDS
+    (4, 96, 1024, 256, 0.25),        # M * r too large to fold T into the decode kernel
+    (2, 64, 32768 + 64, 8, 0.5),     # K beyond the decode kernel: GEMM path at M = 2
     (17, 1024, 1024, 16, 1.0),       # first GEMM size
     (300, 520, 448, 64, 0.25),       # ragged M, N, K over several tiles
     (256, 384, 1024, 256, 0.0625),   # maximum rank

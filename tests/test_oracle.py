@@ -26,7 +26,7 @@ def _next_f32(x, direction):
 
 
 # ---------------------------------------------------------------------------
-# S1: the level table
+# The level table
 # ---------------------------------------------------------------------------
 
 def test_levels_invariants():
@@ -100,7 +100,7 @@ def test_bf16_rne_matches_torch():
 
 
 # ---------------------------------------------------------------------------
-# S2: encoding
+# Encoding
 # ---------------------------------------------------------------------------
 
 def _exact_nearest(x):
@@ -179,7 +179,7 @@ def test_encode_monotone_dense_and_near_boundaries():
 
 
 # ---------------------------------------------------------------------------
-# S2-S4: quantize / dequantize round trip, double quantization
+# Quantize / dequantize round trip, double quantization
 # ---------------------------------------------------------------------------
 
 def _grid_weight(rng, N, K):
@@ -334,7 +334,7 @@ def test_storage_bytes_counts_short_last_group():
 
 
 # ---------------------------------------------------------------------------
-# S5-S10: the linear layer
+# The linear layer
 # ---------------------------------------------------------------------------
 
 def _rand(rng, *shape):
