@@ -21,7 +21,7 @@ GROUP = 256   # constants per second-level fp32 scale: list item (3) of "DL0087 
 
 
 # ---------------------------------------------------------------------------
-# S1: the NF4 level table
+# The NF4 level table
 # ---------------------------------------------------------------------------
 
 def _std_normal_cdf(z: float) -> float:
@@ -105,7 +105,7 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# S2: blockwise absmax + nearest-level encoding + packing
+# Blockwise absmax + nearest-level encoding + packing
 # ---------------------------------------------------------------------------
 
 def encode(x) -> np.ndarray:
@@ -185,7 +185,7 @@ def unpack_codes(codes) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# S4: dequantization
+# Dequantization
 # ---------------------------------------------------------------------------
 
 def dequantize_at(codes, absmax_q, absmax_scale, flat_index) -> np.ndarray:
