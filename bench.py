@@ -119,7 +119,11 @@ def run_training(q, torch, steps, warmup, dev):
 
 
 def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
-    """Decode GB/s on the 65B shapes, rotating over >1 GB of weight copies."""
+    """Decode GB/s on the 65B shapes, rotating over >1 GB of weight copies.
+
+    The rate is device time per call: one pass over the pool is captured as
+    a graph (the calls allocate nothing and record no memsets) and replayed;
+    the eager per-call time, host launch path included, is reported too."""
     import workloads
     cfg = workloads.CONFIGS[2]
     r, s = cfg.r, cfg.s
@@ -149,17 +153,36 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
             for w in pool[:2]:
                 q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
             torch.cuda.synchronize()
-            # per-call rate: profiler off, so no events between the launches
+            # eager per-call rate (includes the Python launch path)
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ev0.record()
-            calls = 0
-            for _ in range(reps):
+            for w in pool:
+                q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
+            ev1.record()
+            torch.cuda.synchronize()
+            ms_eager = ev0.elapsed_time(ev1) / len(pool)
+            # device rate: one pass over the pool captured as a graph and
+            # replayed, so host launch overhead is not on the clock
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
                 for w in pool:
                     q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
-                    calls += 1
+            graph.replay()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(reps):
+                graph.replay()
             ev1.record()
             torch.cuda.synchronize()
             ms = ev0.elapsed_time(ev1)
+            calls = reps * len(pool)
+            # the last call of every replay used pool[-1]: recompute it eagerly
+            Y_graph = Y.clone()
+            q.qlora_linear_fwd(X, pool[-1], A, B, s, Y=Y, T=T, workspace=ws)
+            torch.cuda.synchronize()
+            if not torch.equal(Y_graph, Y):
+                raise RuntimeError(f"decode {N}x{K} M={M}: graph replay differs from eager call")
+            del graph
             # decode-kernel time alone: a second pass with the launch profiler on
             q.qlora_profile_reset()
             q.qlora_profile_enable(True)
@@ -172,6 +195,7 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
             alg = nf4_bytes + 2 * (M * K + M * N + K * r + r * N)
             per_shape[f"{N}x{K}"] = dict(us_per_call=1e3 * ms / calls,
                                          gbs_call=alg * calls / (ms * 1e-3) / 1e9,
+                                         us_per_call_eager=1e3 * ms_eager,
                                          us_decode_kernel=1e3 * kms / max(1, kn),
                                          gbs_decode_kernel=alg * kn / (kms * 1e-3) / 1e9,
                                          copies=copies)
