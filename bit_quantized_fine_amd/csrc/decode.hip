@@ -32,7 +32,6 @@ constexpr int kDecKSlots = 8;                  // waves on one fragment
 constexpr int kDecWaves = kDecR * kDecKSlots;
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kDecRows = 16 * kDecR;
-constexpr int kTabBytes = 256 * 256;           // 256 entries x 32 copies x 8 bytes
 // A buffer offset past the end of every buffer the kernel reads (weights are
 // limited to N*K <= 2^32, so their code buffers hold at most 2^31 bytes).
 constexpr uint32_t kDecOffNone = 0x80000000u;
@@ -57,33 +56,13 @@ struct DecLds {
   int eoff, doff, xoff, dmax, total;
   DecLds(int64_t M, int64_t K, bool xlds) {
     const int64_t kb = K / kBlock;
-    eoff = kTabBytes + kDecThreads * 16 + kDecTSumMaxMR * 4;
+    eoff = kRepTabBytes + kDecThreads * 16 + kDecTSumMaxMR * 4;
     doff = eoff + round16(kDecRows * (kb + 1));
     dmax = static_cast<int>(kDecRows * kb / kGroup + 2);
     xoff = doff + round16(4 * dmax);
     total = xoff + (xlds ? round16(M * K * 2) + 128 : 0);
   }
 };
-
-typedef __attribute__((address_space(3))) const f32x2 LdsF32x2;
-
-// Write byte B of w into byte 1 of a (bits 8..15), keeping a's other bytes:
-// a = (byte << 8) | (a & 0xFFFF00FF).
-template <int B>
-__device__ __forceinline__ void put_byte1(uint32_t& a, uint32_t w) {
-  if constexpr (B == 0)
-    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0"
-        : "+v"(a) : "v"(w));
-  else if constexpr (B == 1)
-    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
-        : "+v"(a) : "v"(w));
-  else if constexpr (B == 2)
-    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2"
-        : "+v"(a) : "v"(w));
-  else
-    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
-        : "+v"(a) : "v"(w));
-}
 
 }  // namespace
 
@@ -97,7 +76,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   constexpr int ROWS = kDecRows;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   char* tab = reinterpret_cast<char*>(dyn);                          // level pairs
-  f32x4* red = reinterpret_cast<f32x4*>(dyn + kTabBytes);            // [kDecThreads]
+  f32x4* red = reinterpret_cast<f32x4*>(dyn + kRepTabBytes);            // [kDecThreads]
   f32x4* tfin = red + kDecThreads;                                   // [kDecTSumMaxMR / 4]
   uint8_t* et = dyn + eoff;                                          // [KB + 1][ROWS]
   float* dsc = reinterpret_cast<float*>(dyn + doff);                 // [dmax]
@@ -204,17 +183,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   }
 
   // Stage into LDS: level table, X, the T partial sums.
-  if (tid < 256) {   // entry tid, copy c at byte 256 tid + 8 c
-    float lo = 0.f, hi = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      lo = ((tid & 15) == j) ? tb.q[j] : lo;
-      hi = ((tid >> 4) == j) ? tb.q[j] : hi;
-    }
-#pragma unroll
-    for (int c = 0; c < 32; ++c)   // lanes start at different copies: no bank conflict
-      reinterpret_cast<float2*>(tab)[32 * tid + ((c + tid) & 31)] = make_float2(lo, hi);
-  }
+  build_rep_pair_table(tab, tb, tid);
   if constexpr (XLDS) {
 #pragma unroll
     for (int i = 0; i < kDecXPieces; ++i) {
@@ -259,7 +228,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // start, begins at LDS address 0 and the address needs no base added.
   uint32_t ta[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) ta[b] = static_cast<uint32_t>(lane & 31) << 3;
+  for (int b = 0; b < 4; ++b) ta[b] = rep_lane_base(lane);
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   // All LDS reads of a chunk (constant, table lookups, X) are issued before
@@ -273,14 +242,10 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t w = cw[st][i];
-      put_byte1<0>(ta[0], w);
-      lk[i][0] = *reinterpret_cast<LdsF32x2*>(static_cast<uintptr_t>(ta[0]));
-      put_byte1<1>(ta[1], w);
-      lk[i][1] = *reinterpret_cast<LdsF32x2*>(static_cast<uintptr_t>(ta[1]));
-      put_byte1<2>(ta[2], w);
-      lk[i][2] = *reinterpret_cast<LdsF32x2*>(static_cast<uintptr_t>(ta[2]));
-      put_byte1<3>(ta[3], w);
-      lk[i][3] = *reinterpret_cast<LdsF32x2*>(static_cast<uintptr_t>(ta[3]));
+      lk[i][0] = rep_lookup<0>(ta[0], w);
+      lk[i][1] = rep_lookup<1>(ta[1], w);
+      lk[i][2] = rep_lookup<2>(ta[2], w);
+      lk[i][3] = rep_lookup<3>(ta[3], w);
     }
     u32x4 xf[4];
 #pragma unroll

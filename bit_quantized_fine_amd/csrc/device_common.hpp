@@ -101,6 +101,60 @@ __device__ __forceinline__ void dequant8_f32(uint32_t w, float c_hat,
   }
 }
 
+// Byte-pair table replicated for conflict-free lookups: 32 copies of the 256
+// entries, entry b of copy c at byte 256 b + 8 c, so lane l reads copy
+// (l % 32) and the 32 lanes of a half-wave always hit distinct bank pairs
+// whatever the codes.  64 KB; a kernel using it places it at LDS address 0
+// (first in its dynamic LDS, with no static LDS), so a lookup address is
+// (byte << 8) | ((lane % 32) << 3) with no base to add.
+constexpr int kRepTabBytes = 256 * 256;
+
+__device__ __forceinline__ void build_rep_pair_table(char* tab, const Nf4Tables& tb, int tid) {
+  if (tid < 256) {
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      lo = ((tid & 15) == j) ? tb.q[j] : lo;
+      hi = ((tid >> 4) == j) ? tb.q[j] : hi;
+    }
+#pragma unroll
+    for (int c = 0; c < 32; ++c)   // lanes start at different copies: no bank conflict
+      reinterpret_cast<float2*>(tab)[32 * tid + ((c + tid) & 31)] = make_float2(lo, hi);
+  }
+}
+
+typedef __attribute__((address_space(3))) const f32x2 LdsF32x2;
+
+// Write byte B of w into byte 1 of a (bits 8..15), keeping a's other bytes:
+// a = (byte << 8) | (a & 0xFFFF00FF).  One SDWA move.
+template <int B>
+__device__ __forceinline__ void put_byte1(uint32_t& a, uint32_t w) {
+  if constexpr (B == 0)
+    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0"
+        : "+v"(a) : "v"(w));
+  else if constexpr (B == 1)
+    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
+        : "+v"(a) : "v"(w));
+  else if constexpr (B == 2)
+    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2"
+        : "+v"(a) : "v"(w));
+  else
+    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
+        : "+v"(a) : "v"(w));
+}
+
+// The level pair of byte B of w from the replicated table; ta holds the
+// lane's copy offset in byte 0 and is reused as the address register.
+template <int B>
+__device__ __forceinline__ f32x2 rep_lookup(uint32_t& ta, uint32_t w) {
+  put_byte1<B>(ta, w);
+  return *reinterpret_cast<LdsF32x2*>(static_cast<uintptr_t>(ta));
+}
+
+__device__ __forceinline__ uint32_t rep_lane_base(int lane) {
+  return static_cast<uint32_t>(lane & 31) << 3;
+}
+
 // Raw buffer access: a descriptor over [p, p + nbytes) in scalar registers
 // and 32-bit byte offsets; reads outside the range return zero.
 typedef __amdgpu_buffer_rsrc_t BufRes;

@@ -1,21 +1,29 @@
-// Forward for many tokens: Y = X . deq(W)^T + s . T . B on bf16 MFMA.
+// Forward for many tokens: Y = X . deq(W)^T + s . T . B on bf16 MFMA, with the
+// dequantized weight tile staged in LDS (Mathematical Formulation and
+// Figure 1 of "DL0087 QLoRA": a bf16 tile of W is rebuilt just before the
+// matmul and discarded).
 //
-// Workgroup tile: 256 weight rows (n) x 128 tokens (m), reduction in chunks
-// of 128 k.  The token tile of X is shared through LDS; the weight rows are
-// split between the waves (each wave owns 256/NW consecutive rows), so each
-// NF4 code is loaded and dequantized exactly once per workgroup, straight
-// from a 16-byte global load into the A-operand registers of
-// v_mfma_f32_16x16x32_bf16 (the bf16 tile of the Mathematical Formulation
-// of "DL0087 QLoRA" lives only in registers).
+// Tile layouts in LDS: a row (weight row n or token m) holds its 64 k as
+// eight 16-byte pieces, piece q stored at slot q ^ ((row / 2) % 8).  The
+// writes (dequantized weights, 4 threads per row; X, 8 lanes per row) and the
+// MFMA fragment reads (16 rows per lane group) then all spread over the 64
+// banks.
 //
-// Reduction order inside a chunk: lane group g = lane/16 of a wave holds the
-// 32 codes k0+32g .. k0+32g+31 of its row (one 16-byte load); MFMA step i
-// consumes k0 + 32g + 8i + (0..7) from every lane group.  The X fragment is
-// read from LDS with the same k mapping, so the sum is over every k once.
+// Workgroup = 8 waves, tile = 128 weight rows (n) x 256 tokens (m), reduction
+// in chunks of 64 k (one NF4 block per row).  Every chunk the 512 threads
+// dequantize the tile's 128 x 64 weights once -- thread t takes 16 codes of
+// row t/4 -- into one of two LDS buffers, while the waves multiply the other
+// buffer.  Wave w owns tokens 64 (w % 4) .. +63 and all 128 rows, and the
+// 32-k half (w / 4) of every chunk: it reads its A fragments (weights) and
+// B fragments (X) from LDS.  X reaches LDS through coalesced 16-byte loads
+// (eight lanes per 128-byte token row) issued two chunks ahead.  Each weight is dequantized once per 256 tokens (about
+// one VALU instruction per MFMA); splitting the chunk's two 32-k steps
+// between two waves puts two waves on every SIMD, so one wave's
+// dequantization and LDS waits overlap the other's MFMAs.  The two halves'
+// accumulators are added through LDS at the end.
 //
-// The LoRA update is appended as extra reduction chunks over the rank:
-// columns 0..63 of such a chunk carry bf16(s.T) (hi part), columns 64..127
-// the bf16 remainder (lo part), both against B^T staged through LDS.
+// The LoRA update is appended as extra reduction steps over the rank: B^T is
+// staged in LDS through 8x8 transposes, s.T enters as bf16 hi and lo halves.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -25,16 +33,22 @@ namespace qnf4 {
 
 namespace {
 
-constexpr int FP = 256;          // weight rows per workgroup
-constexpr int FQ = 128;          // tokens per workgroup
-constexpr int FK = 128;          // reduction elements per chunk
-constexpr int XS = FK + 8;       // LDS row stride of the token tile (272 B)
-constexpr int BTS = 64 + 8;      // LDS row stride of the B^T tile (144 B)
-constexpr int SMEM_ELEMS = 2 * FQ * XS > FP * BTS + FQ * XS ? 2 * FQ * XS : FP * BTS + FQ * XS;
+constexpr int GP = 128;          // weight rows per workgroup
+constexpr int GQ = 256;          // tokens per workgroup
+constexpr int GK = 64;           // reduction elements per chunk (one block per row)
+constexpr int GWT = 4;           // token groups
+constexpr int GKS = 2;           // waves splitting a chunk's two 32-k steps
+constexpr int GW = GWT * GKS;    // waves
+constexpr int GT = 64 * GW;      // threads
+constexpr int AS = GK;           // LDS row stride of the A tile (128 B, XOR-swizzled)
+constexpr int GTA = GP / 16;     // 16-row subtiles (8)
+constexpr int GTB = GQ / GWT / 16;   // 16-token subtiles per wave (4)
+constexpr int BTS = 64 + 8;     // LDS row stride of the B^T tile
+constexpr int XTS = GK;          // LDS row stride of the X tile (128 B, XOR-swizzled)
+constexpr int kXTile = GQ * XTS;   // elements of one X tile buffer
+constexpr int kFwdLds = kRepTabBytes + 2 * GP * AS * 2 + 2 * kXTile * 2;
+constexpr int XPT = GQ * GK / 8 / GT;   // 16-byte X pieces a thread stages per chunk (4)
 
-// Tile id of workgroup b when consecutive workgroups go round-robin to the 8
-// XCDs: every XCD gets a contiguous run of tile ids, so workgroups sharing a
-// token tile (consecutive ids, token-major order) share an L2.
 __device__ __forceinline__ int xcd_remap(int b, int total) {
   const int n8 = total >> 3, rem = total & 7;
   const int x = b & 7, i = b >> 3;
@@ -43,170 +57,178 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
 
 }  // namespace
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void k_fwd_gemm2(
+__global__ __launch_bounds__(GT) void k_fwd_gemm(
     const uint16_t* __restrict__ X, int64_t M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
     int64_t N, int64_t K, const float* __restrict__ T, const uint16_t* __restrict__ Bl,
     int r, float s, uint16_t* __restrict__ Y, int ptiles, int qtiles, Nf4Tables tb) {
-  constexpr int NT_ = 64 * NW;
-  constexpr int RW = FP / NW;        // weight rows per wave
-  constexpr int TA = RW / 16;        // 16-row subtiles per wave
-  constexpr int TB = FQ / 16;        // 16-token subtiles
-  constexpr int XCH = FQ * FK / 8 / NT_;   // 16-byte X chunks per thread per chunk
-  static_assert(FQ * FK / 8 % NT_ == 0, "X tile split");
-
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
-  __shared__ float2 tab[256];
+  // Dynamic LDS only (so the table sits at address 0): the replicated level
+  // table, then two A tile buffers; after the main loop the same bytes hold
+  // the accumulator exchange and the B^T tile of the LoRA update.
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  char* tab = reinterpret_cast<char*>(dyn);
+  uint16_t* As = reinterpret_cast<uint16_t*>(dyn + kRepTabBytes);
+  uint16_t* Xs = As + 2 * GP * AS;   // two X tile buffers [GQ][XTS]
 
   const int tid = threadIdx.x;
   const int wave = wave_id(), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
-  build_pair_table(tab, tb, tid, NT_);
+  const int wt = wave % GWT, ks = wave / GWT;
+  build_rep_pair_table(tab, tb, tid);
 
   const int tile = xcd_remap(blockIdx.x, ptiles * qtiles);
   const int qt = tile / ptiles, pt = tile - qt * ptiles;
-  const int64_t p0 = (int64_t)pt * FP, q0 = (int64_t)qt * FQ;
-  const int nchunks = static_cast<int>((K + FK - 1) / FK);
+  const int64_t p0 = (int64_t)pt * GP, q0 = (int64_t)qt * GQ;
+  const int nchunks = static_cast<int>(K / GK);
+  const int KB = static_cast<int>(K / kBlock);
 
-  // weight rows of this lane
-  const uint8_t* crow[TA];
-  int64_t brow[TA];
-  bool nok[TA];
+  // Buffer descriptors: rows n >= N and tokens m >= M read as zero.
+  const uint32_t nb = static_cast<uint32_t>(N * K / kBlock);
+  const BufRes rc = make_bufres(codes, static_cast<uint32_t>(N * K / 2));
+  const BufRes re = make_bufres(absmax_q, nb);
+  const BufRes rd = make_bufres(absmax_scale, ((nb + kGroup - 1) / kGroup) * 4u);
+  const uint64_t xbytes = static_cast<uint64_t>(M) * K * 2;
+  const BufRes rx = make_bufres(X, xbytes < 0x80000000ull ? static_cast<uint32_t>(xbytes)
+                                                          : 0x80000000u);
+
+  // Dequantization role: row dr of the tile, codes 16 dq .. 16 dq + 15 of the chunk.
+  const int dr = tid >> 2, dq = tid & 3;
+  const int64_t dn = p0 + dr;
+  const uint32_t dcode = static_cast<uint32_t>(dn * (K / 2)) + 8u * dq;   // + 32 c
+  const uint32_t dblk = static_cast<uint32_t>(dn * KB);                   // + c
+  u32x2 cw[2];
+  uint32_t ce[2];
+  float cd[2];
+  auto load_codes = [&](int c, int st) {
+    const bool live = c < nchunks;
+    const uint32_t blk = dblk + static_cast<uint32_t>(c);
+    cw[st] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                           rc, live ? dcode + 32u * c : 0x80000000u, 0, 0));
+    ce[st] = buf_load_u8(re, live ? blk : 0x80000000u);
+    cd[st] = buf_load_f32(rd, live ? (blk / kGroup) * 4u : 0x80000000u);
+  };
+  // A tile row dr, columns 16 dq .. +15: bf16_rne(fl32(level * fl32(e * d)))
+  uint32_t ta[4];
 #pragma unroll
-  for (int a = 0; a < TA; ++a) {
-    const int64_t n = p0 + wave * RW + 16 * a + li;
-    nok[a] = n < N;
-    const int64_t nn = nok[a] ? n : 0;
-    crow[a] = codes + nn * (K / 2) + 16 * g;
-    brow[a] = nn * (K / kBlock) + (g >> 1);
-  }
-
-  f32x4 acc[TA][TB];
+  for (int b = 0; b < 4; ++b) ta[b] = rep_lane_base(lane);
+  auto dequant = [&](int st, int buf) {
+    const float chat = static_cast<float>(ce[st]) * cd[st];
+    uint16_t* dst = As + buf * GP * AS + dr * AS;
+    const int swz = (dr >> 1) & 7;
 #pragma unroll
-  for (int a = 0; a < TA; ++a)
-#pragma unroll
-    for (int b = 0; b < TB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t w = cw[st][i];
+      const f32x2 v0 = rep_lookup<0>(ta[0], w);
+      const f32x2 v1 = rep_lookup<1>(ta[1], w);
+      const f32x2 v2 = rep_lookup<2>(ta[2], w);
+      const f32x2 v3 = rep_lookup<3>(ta[3], w);
+      *reinterpret_cast<u32x4*>(dst + 8 * ((2 * dq + i) ^ swz)) =
+          u32x4{pack_bf16x2(v0.x * chat, v0.y * chat), pack_bf16x2(v1.x * chat, v1.y * chat),
+                pack_bf16x2(v2.x * chat, v2.y * chat), pack_bf16x2(v3.x * chat, v3.y * chat)};
+    }
+  };
 
-  // Register staging, two chunks deep: X(c) and the codes of chunk c live in
-  // stage c & 1 from the start of iteration c-2 until they are consumed.
-  u32x4 xr[2][XCH];
-  u32x4 cw[2][TA];
-  uint32_t ce[2][TA];   // 8-bit block constant, as loaded
-  float cd[2][TA];      // its fp32 group scale, as loaded
-
+  // X staging role: piece j of thread tid is token row xr + 64 j (xr = tid / 8)
+  // of the tile, 16-byte piece tid % 8 of its 128-byte chunk row.
+  const int xr = tid >> 3, xq = tid & 7;
+  const uint32_t xsrc = static_cast<uint32_t>(((q0 + xr) * K + 8 * xq) * 2);   // + 128 c
+  u32x4 xw[2][XPT];
   auto load_x = [&](int c, int st) {
+    const bool live = c < nchunks;
 #pragma unroll
-    for (int j = 0; j < XCH; ++j) {
-      const int idx = tid + j * NT_;
-      const int row = idx >> 4, col = idx & 15;
-      const int64_t m = q0 + row, k = (int64_t)c * FK + col * 8;
-      xr[st][j] = (m < M && k < K) ? *reinterpret_cast<const u32x4*>(X + m * K + k)
-                                   : u32x4{0, 0, 0, 0};
-    }
+    for (int j = 0; j < XPT; ++j)
+      xw[st][j] = buf_load16(
+          rx, live ? xsrc + static_cast<uint32_t>((64 * j * K + c * GK) * 2) : 0x80000000u);
   };
-  auto store_x = [&](int buf, int st) {
-    uint16_t* xs = smem + buf * FQ * XS;
+  auto store_x = [&](int st, int buf) {
 #pragma unroll
-    for (int j = 0; j < XCH; ++j) {
-      const int idx = tid + j * NT_;
-      *reinterpret_cast<u32x4*>(xs + (idx >> 4) * XS + (idx & 15) * 8) = xr[st][j];
-    }
-  };
-  auto load_w = [&](int c, int st) {
-    const bool kok = (int64_t)c * FK + 32 * g < K;
-#pragma unroll
-    for (int a = 0; a < TA; ++a) {
-      // The block constant is multiplied out only when the chunk is used,
-      // so these loads are not waited for here.
-      if (nok[a] && kok) {
-        const int64_t blk = brow[a] + 2 * c;
-        cw[st][a] = *reinterpret_cast<const u32x4*>(crow[a] + (int64_t)c * (FK / 2));
-        ce[st][a] = absmax_q[blk];
-        cd[st][a] = absmax_scale[blk >> 8];
-      } else {
-        cw[st][a] = u32x4{0, 0, 0, 0};
-        ce[st][a] = 0;
-        cd[st][a] = 0.f;
-      }
+    for (int j = 0; j < XPT; ++j) {
+      const int row = xr + 64 * j;
+      *reinterpret_cast<u32x4*>(Xs + buf * kXTile + row * XTS + 8 * (xq ^ ((row >> 1) & 7))) =
+          xw[st][j];
     }
   };
 
+  f32x4 acc[GTA][GTB];
+#pragma unroll
+  for (int a = 0; a < GTA; ++a)
+#pragma unroll
+    for (int b = 0; b < GTB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mma = [&](int buf) {
+    // rows 16 a + li (weights) and 64 wt + 16 b + li (tokens): swizzle
+    // (li / 2) % 8, piece g + 4 ks
+    const int piece = 8 * ((g + 4 * ks) ^ (li >> 1));
+    const uint16_t* at = As + buf * GP * AS + li * AS + piece;
+    const uint16_t* xt = Xs + buf * kXTile + (64 * wt + li) * XTS + piece;
+    u32x4 bf[GTB];
+#pragma unroll
+    for (int b = 0; b < GTB; ++b) bf[b] = *reinterpret_cast<const u32x4*>(xt + 16 * b * XTS);
+#pragma unroll
+    for (int a = 0; a < GTA; ++a) {
+      const u32x4 af = *reinterpret_cast<const u32x4*>(at + 16 * a * AS);
+#pragma unroll
+      for (int b = 0; b < GTB; ++b) acc[a][b] = mfma16(af, bf[b], acc[a][b]);
+    }
+  };
+
+  load_codes(0, 0);
+  load_codes(1, 1);
   load_x(0, 0);
-  load_w(0, 0);
-  if (nchunks > 1) {
-    load_x(1, 1);
-    load_w(1, 1);
-  }
-  __syncthreads();          // pair table ready
+  load_x(1, 1);
+  __syncthreads();   // level table
+  dequant(0, 0);
   store_x(0, 0);
+  load_codes(2, 0);
+  load_x(2, 0);
   __syncthreads();
-
-  // One chunk: take this chunk's codes out of their stage, refill the stage
-  // with chunk c+2 (codes and X), multiply chunk c from LDS buffer c & 1,
-  // then stage X(c+1) into the other LDS buffer.
-  auto step = [&](int c, auto stc) {
+  // iteration c: stage chunk c+1 into buffers (c+1)&1 -- dequantize its
+  // codes and store its X, both loaded two iterations ago -- and refill
+  // those register stages with chunk c+3; multiply chunk c from buffers c&1.
+  auto iter = [&](int c, auto stc) {
     constexpr int ST = decltype(stc)::value;
-    u32x4 cur[TA];
-    float cch[TA];
-#pragma unroll
-    for (int a = 0; a < TA; ++a) {
-      cur[a] = cw[ST][a];
-      cch[a] = static_cast<float>(ce[ST][a]) * cd[ST][a];   // fl32(e * d)
-    }
-    if (c + 2 < nchunks) {
-      load_w(c + 2, ST);
-      load_x(c + 2, ST);
-    }
-    const uint16_t* xs = smem + ST * FQ * XS;
-    // Software pipeline over the four 32-k steps: the X fragments and the
-    // level-table lookups of step i+1 are issued before the MFMAs of step i.
-    u32x4 bf[2][TB];
-    float2 lk[2][TA][4];
-    auto issue = [&](int i, int sb) {
-#pragma unroll
-      for (int b = 0; b < TB; ++b)
-        bf[sb][b] = *reinterpret_cast<const u32x4*>(xs + (16 * b + li) * XS + (4 * g + i) * 8);
-#pragma unroll
-      for (int a = 0; a < TA; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) lk[sb][a][q] = tab[(cur[a][i] >> (8 * q)) & 0xFFu];
-    };
-    issue(0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sb = i & 1;
-      if (i < 3) issue(i + 1, sb ^ 1);
-      u32x4 A[TA];
-#pragma unroll
-      for (int a = 0; a < TA; ++a) {
-        const float cc = cch[a];
-        A[a] = u32x4{pack_bf16x2(lk[sb][a][0].x * cc, lk[sb][a][0].y * cc),
-                     pack_bf16x2(lk[sb][a][1].x * cc, lk[sb][a][1].y * cc),
-                     pack_bf16x2(lk[sb][a][2].x * cc, lk[sb][a][2].y * cc),
-                     pack_bf16x2(lk[sb][a][3].x * cc, lk[sb][a][3].y * cc)};
-      }
-#pragma unroll
-      for (int b = 0; b < TB; ++b)
-#pragma unroll
-        for (int a = 0; a < TA; ++a) acc[a][b] = mfma16(A[a], bf[sb][b], acc[a][b]);
-    }
-    if (c + 1 < nchunks) store_x(ST ^ 1, ST ^ 1);
+    dequant(ST ^ 1, ST ^ 1);
+    store_x(ST ^ 1, ST ^ 1);
+    load_codes(c + 3, ST ^ 1);
+    load_x(c + 3, ST ^ 1);
+    mma(ST);
     __syncthreads();
   };
   for (int c = 0; c < nchunks; c += 2) {
-    step(c, std::integral_constant<int, 0>{});
-    if (c + 1 < nchunks) step(c + 1, std::integral_constant<int, 1>{});
+    iter(c, std::integral_constant<int, 0>{});
+    if (c + 1 < nchunks) iter(c + 1, std::integral_constant<int, 1>{});
   }
 
-  // LoRA update: extra chunks over the rank, hi and lo halves of s.T.
+  // Add the second k half into the first: waves ks = 1 hand their
+  // accumulators over through LDS, half of the row subtiles at a time.
+  f32x4* xch = reinterpret_cast<f32x4*>(dyn);   // [GWT][GTA/2][GTB][64]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (ks == 1) {
+#pragma unroll
+      for (int a = 0; a < GTA / 2; ++a)
+#pragma unroll
+        for (int b = 0; b < GTB; ++b)
+          xch[((wt * (GTA / 2) + a) * GTB + b) * 64 + lane] = acc[h * (GTA / 2) + a][b];
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+      for (int a = 0; a < GTA / 2; ++a)
+#pragma unroll
+        for (int b = 0; b < GTB; ++b)
+          acc[h * (GTA / 2) + a][b] += xch[((wt * (GTA / 2) + a) * GTB + b) * 64 + lane];
+    }
+    __syncthreads();
+  }
+
+  // LoRA update: 64 ranks at a time, B^T tile [128 rows][64 ranks] in LDS,
+  // s.T hi / lo halves per lane from global memory.
   if (r > 0) {
-    uint16_t* bt = smem;                 // [FP][BTS]: B^T rows n, 64 ranks
-    uint16_t* tt = smem + FP * BTS;      // [FQ][XS]: s.T hi (0..63) | lo (64..127)
+    uint16_t* bt = As;
     for (int j0 = 0; j0 < r; j0 += 64) {
-      // B^T tile: 8x8 patches, (FP/8) x 8 of them
-      for (int p = tid; p < FP; p += NT_) {
-        const int rp = p % (FP / 8), kp = p / (FP / 8);
+      if (tid < GP) {   // patch tid: rows 8 (tid % 16) .., ranks j0 + 8 (tid / 16) ..
+        const int rp = tid % (GP / 8), kp = tid / (GP / 8);
         const int64_t n = p0 + rp * 8;
         u32x4 rows[8], cols[8];
 #pragma unroll
@@ -220,36 +242,37 @@ __global__ __launch_bounds__(64 * NW) void k_fwd_gemm2(
         for (int t = 0; t < 8; ++t)
           *reinterpret_cast<u32x4*>(bt + (rp * 8 + t) * BTS + kp * 8) = cols[t];
       }
-      // s.T tile split into bf16 hi / lo
-      for (int idx = tid; idx < FQ * 8; idx += NT_) {
-        const int row = idx >> 3, col = idx & 7;
-        const int64_t m = q0 + row;
-        const int j = j0 + col * 8;
-        uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
-        if (m < M && j < r) {
-          const f32x4 t0 = *reinterpret_cast<const f32x4*>(T + m * r + j);
-          const f32x4 t1 = *reinterpret_cast<const f32x4*>(T + m * r + j + 4);
-          const float v[8] = {t0.x * s, t0.y * s, t0.z * s, t0.w * s,
-                              t1.x * s, t1.y * s, t1.z * s, t1.w * s};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) split_bf16x2(v[2 * e], v[2 * e + 1], hi[e], lo[e]);
-        }
-        *reinterpret_cast<u32x4*>(tt + row * XS + col * 8) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<u32x4*>(tt + row * XS + 64 + col * 8) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-      }
       __syncthreads();
+      if (ks == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = 32 * g + 8 * i;
-        u32x4 A[TA];
+        for (int i = 0; i < 2; ++i) {
+          const int j = j0 + 32 * i + 8 * g;
+          u32x4 th[GTB], tl[GTB];
 #pragma unroll
-        for (int a = 0; a < TA; ++a)
-          A[a] = *reinterpret_cast<const u32x4*>(bt + (wave * RW + 16 * a + li) * BTS + (kk & 63));
+          for (int b = 0; b < GTB; ++b) {
+            const int64_t m = q0 + 64 * wt + 16 * b + li;
+            uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
+            if (m < M && j < r) {
+              const f32x4 t0 = *reinterpret_cast<const f32x4*>(T + m * r + j);
+              const f32x4 t1 = *reinterpret_cast<const f32x4*>(T + m * r + j + 4);
+              const float v[8] = {t0.x * s, t0.y * s, t0.z * s, t0.w * s,
+                                  t1.x * s, t1.y * s, t1.z * s, t1.w * s};
 #pragma unroll
-        for (int b = 0; b < TB; ++b) {
-          const u32x4 Bf = *reinterpret_cast<const u32x4*>(tt + (16 * b + li) * XS + kk);
+              for (int e = 0; e < 4; ++e) split_bf16x2(v[2 * e], v[2 * e + 1], hi[e], lo[e]);
+            }
+            th[b] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            tl[b] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+          }
 #pragma unroll
-          for (int a = 0; a < TA; ++a) acc[a][b] = mfma16(A[a], Bf, acc[a][b]);
+          for (int a = 0; a < GTA; ++a) {
+            const u32x4 af =
+                *reinterpret_cast<const u32x4*>(bt + (16 * a + li) * BTS + 32 * i + 8 * g);
+#pragma unroll
+            for (int b = 0; b < GTB; ++b) {
+              acc[a][b] = mfma16(af, th[b], acc[a][b]);
+              acc[a][b] = mfma16(af, tl[b], acc[a][b]);
+            }
+          }
         }
       }
       __syncthreads();
@@ -257,29 +280,34 @@ __global__ __launch_bounds__(64 * NW) void k_fwd_gemm2(
   }
 
   // Y[m, n..n+3] for the lane's 4 consecutive rows n of each subtile
+  if (ks == 0) {
 #pragma unroll
-  for (int a = 0; a < TA; ++a) {
-    const int64_t n = p0 + wave * RW + 16 * a + 4 * g;
+    for (int a = 0; a < GTA; ++a) {
+      const int64_t n = p0 + 16 * a + 4 * g;
 #pragma unroll
-    for (int b = 0; b < TB; ++b) {
-      const int64_t m = q0 + 16 * b + li;
-      if (m < M && n < N) {
-        const f32x4 v = acc[a][b];
-        *reinterpret_cast<u32x2*>(Y + m * N + n) =
-            u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+      for (int b = 0; b < GTB; ++b) {
+        const int64_t m = q0 + 64 * wt + 16 * b + li;
+        if (m < M && n < N) {
+          const f32x4 v = acc[a][b];
+          *reinterpret_cast<u32x2*>(Y + m * N + n) =
+              u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+        }
       }
     }
   }
 }
 
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
-                           const float* T, const uint16_t* B, int r, float s,
-                           uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
-  constexpr int NW = 8;
-  const int ptiles = static_cast<int>((w.N + FP - 1) / FP);
-  const int qtiles = static_cast<int>((M + FQ - 1) / FQ);
+                            const float* T, const uint16_t* B, int r, float s,
+                            uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_fwd_gemm), hipFuncAttributeMaxDynamicSharedMemorySize,
+      kFwdLds);
+  if (attr != hipSuccess) return attr;
+  const int ptiles = static_cast<int>((w.N + GP - 1) / GP);
+  const int qtiles = static_cast<int>((M + GQ - 1) / GQ);
   prof_begin(0, stream);
-  hipLaunchKernelGGL(k_fwd_gemm2<NW>, dim3(ptiles * qtiles), dim3(64 * NW), 0, stream, X, M,
+  hipLaunchKernelGGL(k_fwd_gemm, dim3(ptiles * qtiles), dim3(GT), kFwdLds, stream, X, M,
                      w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, B, r, s, Y, ptiles,
                      qtiles, tb);
   prof_end(0, stream);

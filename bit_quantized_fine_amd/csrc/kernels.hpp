@@ -30,8 +30,9 @@ struct Nf4View {
 void prof_begin(int family, hipStream_t stream);
 void prof_end(int family, hipStream_t stream);
 
-// Y[M,N] = bf16( X . deq(W)^T + s . T . B ), large-M MFMA path.
-// T [M, r] fp32 (may be null when r == 0).
+// Y[M,N] = bf16( X . deq(W)^T + s . T . B ), large-M MFMA path with the
+// dequantized weight tiles staged in LDS.  T [M, r] fp32 (may be null when
+// r == 0).
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
                            const float* T, const uint16_t* B, int r, float s,
                            uint16_t* Y, const Nf4Tables& tb, hipStream_t stream);
