@@ -72,14 +72,17 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-constexpr int64_t kMaxK = int64_t(1) << 24;        // longest reduction dimension
+// The GEMM kernels address a 256-token tile of X or dY, and the code
+// stream, with 32-bit byte offsets.
+constexpr int64_t kMaxK = int64_t(1) << 22;        // weight columns (in features)
+constexpr int64_t kMaxN = int64_t(1) << 22;        // weight rows (out features)
 constexpr int64_t kMaxElems = int64_t(1) << 32;    // N * K of one weight
 
 int check_weight(const qlora_nf4_weight* w) {
   if (!w || !w->codes || !w->absmax_q || !w->absmax_scale) return QLORA_ERR_NULL;
   if (w->N < 1 || w->K < kBlock || w->K % kBlock != 0) return QLORA_ERR_SHAPE;
   // kernels address the code stream with 32-bit byte offsets
-  if (w->K > kMaxK || w->N > kMaxElems / w->K) return QLORA_ERR_SHAPE;
+  if (w->K > kMaxK || w->N > kMaxN || w->N > kMaxElems / w->K) return QLORA_ERR_SHAPE;
   if (!aligned16(w->codes) || (reinterpret_cast<uintptr_t>(w->absmax_scale) & 3u))
     return QLORA_ERR_ALIGN;
   return QLORA_OK;
@@ -232,7 +235,7 @@ int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
                        uint8_t* absmax_q, float* absmax_scale, qlora_stream_t stream) {
   if (!W || !codes || !absmax_q || !absmax_scale) return QLORA_ERR_NULL;
   if (N < 1 || K < kBlock || K % kBlock != 0) return QLORA_ERR_SHAPE;
-  if (K > kMaxK || N > kMaxElems / K) return QLORA_ERR_SHAPE;
+  if (K > kMaxK || N > kMaxN || N > kMaxElems / K) return QLORA_ERR_SHAPE;
   if (!aligned16(W) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(absmax_scale) & 3u))
     return QLORA_ERR_ALIGN;
   const hipStream_t st = static_cast<hipStream_t>(stream);

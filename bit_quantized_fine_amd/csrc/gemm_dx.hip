@@ -1,21 +1,29 @@
 // Backward dX = dY . deq(W) + s . G . A^T on bf16 MFMA (list item (4) of
 // "DL0087 QLoRA: 4-bit Quantized LoRA": gradients pass through the frozen
-// 4-bit weights; the backward pass dequantizes again).
+// 4-bit weights; the backward pass dequantizes again), with the dequantized
+// weight tile staged in LDS.
 //
 // Here the reduction runs over the weight's rows n while its 64-blocks run
-// along k, so the dequantized weight is needed "transposed".  Workgroup tile:
-// 256 output columns k x 128 tokens; 8 waves each own 32 consecutive k.  In
-// one 32-n MFMA step, lane (rho = l % 16, g = l / 16) loads one code byte --
-// the two codes of columns k = kw + 2 rho + {0, 1} -- from each of the 8 rows
-// n = n0 + 8g + t, t = 0..7, and dequantizes them into the A operands of two
-// 16-row MFMA subtiles (subtile e holds column kw + 2 rho + e in row rho):
-// the 8 values along n for a fixed k are exactly one A fragment.  The
-// dequantized weight never leaves registers.  dY is shared through LDS; the
-// block constants of a chunk (one per row n and 64-column block) are
-// multiplied out once per workgroup into LDS.
+// along k, so the weight enters the MFMA "transposed".  Workgroup = 8 waves,
+// tile = 128 output columns (k) x 256 tokens (m), reduction in chunks of 64
+// rows n.  Every chunk the 512 threads dequantize the tile's 64 x 128
+// weights once -- thread t takes 16 codes of row t/8 -- into one of two LDS
+// buffers in their natural row-major order, and the waves read their A
+// fragments (16 columns k x 32 rows n) with ds_read_b64_tr_b16, which
+// transposes 4 x 16 blocks of 16-bit elements across each group of 16 lanes.
+// dY is staged through LDS by coalesced loads.  Wave w owns tokens
+// 64 (w % 4) .. +63, all 128 columns, and the 32-row half (w / 4) of every
+// chunk; the two halves' accumulators are added through LDS at the end.
 //
-// Output: lane l of a wave ends with columns kw + 8(l/16) .. +7 of token
-// (l % 16) of each 16-token subtile, i.e. one contiguous 16-byte store.
+// LDS layouts: a weight row n holds its 128 k as sixteen 16-byte pieces,
+// piece p at slot p ^ ((n % 2) ^ 2 (n % 4) ^ 8 ((n / 8) % 2)): the rows a
+// transposing read touches use distinct 32-byte slot pairs, and the two rows
+// of a 16-lane dequantizing store use opposite slot parities.  A dY token row
+// holds its 64 n as eight pieces, piece q at slot q ^ ((m / 2) % 8).
+//
+// The LoRA term s . G . A^T is appended as extra reduction steps over the
+// rank: A^T fragments come straight from A [K, r], s.G enters as bf16 hi and
+// lo halves.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -25,14 +33,21 @@ namespace qnf4 {
 
 namespace {
 
-constexpr int DP = 256;          // output columns k per workgroup
-constexpr int DQ = 128;          // tokens per workgroup
-constexpr int DN = 64;           // reduction (n) per chunk (two 32-n MFMA steps)
-constexpr int DNW = 8;           // waves
-constexpr int DRW = DP / DNW;    // k per wave (32)
-constexpr int DT = 256 * 2;      // threads
-constexpr int YS = 128 + 8;      // LDS row stride of the dY tile (also the LoRA tile)
-constexpr int CB = DP / kBlock;  // 64-column blocks per tile (4)
+constexpr int XP = 128;          // output columns k per workgroup
+constexpr int XQ = 256;          // tokens per workgroup
+constexpr int XN = 64;           // weight rows n per chunk
+constexpr int XWT = 4;           // token groups
+constexpr int XKS = 2;           // waves splitting a chunk's two 32-n steps
+constexpr int XW = XWT * XKS;    // waves
+constexpr int XT = 64 * XW;      // threads
+constexpr int XAS = XP;          // LDS row stride of the weight tile (256 B, swizzled)
+constexpr int XYS = XN;          // LDS row stride of the dY tile (128 B, swizzled)
+constexpr int XTA = XP / 16;     // 16-column subtiles (8)
+constexpr int XTB = XQ / XWT / 16;   // 16-token subtiles per wave (4)
+constexpr int kXA = XN * XAS;    // elements of one weight tile buffer
+constexpr int kXY = XQ * XYS;    // elements of one dY tile buffer
+constexpr int kDxLds = kRepTabBytes + 2 * kXA * 2 + 2 * kXY * 2;
+constexpr int XYPT = XQ * XN / 8 / XT;   // 16-byte dY pieces a thread stages per chunk (4)
 
 __device__ __forceinline__ int xcd_remap_dx(int b, int total) {
   const int n8 = total >> 3, rem = total & 7;
@@ -40,196 +55,239 @@ __device__ __forceinline__ int xcd_remap_dx(int b, int total) {
   return x * n8 + min(x, rem) + i;
 }
 
+// Slot of 16-byte piece p of weight-tile row n.
+__device__ __forceinline__ int wslot(int n, int p) {
+  return p ^ ((n & 1) ^ (2 * (n & 3)) ^ (8 * ((n >> 3) & 1)));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 LdsV4i16;
+
 }  // namespace
 
-__global__ __launch_bounds__(DT) void k_dx_gemm2(
+__global__ __launch_bounds__(XT) void k_dx_gemm(
     const uint16_t* __restrict__ dY, int64_t M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
     int64_t N, int64_t K, const float* __restrict__ G, const uint16_t* __restrict__ Al,
     int r, float s, uint16_t* __restrict__ dX, int ptiles, int qtiles, Nf4Tables tb) {
-  constexpr int TB = DQ / 16;                 // token subtiles
-  constexpr int YCH = DQ * DN / 8 / DT;       // 16-byte dY chunks per thread per chunk (2)
-  __shared__ __attribute__((aligned(16))) uint16_t ys[2][DQ * YS];   // dY uses 64 of 136 columns
-  __shared__ __attribute__((aligned(16))) float cs[2][CB * DN];   // block constants [blk][n]
-  __shared__ float2 tab[256];
+  // Dynamic LDS only (the level table sits at address 0): the replicated
+  // table, two weight tiles, two dY tiles; the table's bytes hold the
+  // accumulator exchange after the main loop.
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  char* tab = reinterpret_cast<char*>(dyn);
+  uint16_t* Ws = reinterpret_cast<uint16_t*>(dyn + kRepTabBytes);   // [2][XN][XAS]
+  uint16_t* Ys = Ws + 2 * kXA;                                       // [2][XQ][XYS]
 
   const int tid = threadIdx.x;
   const int wave = wave_id(), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
-  build_pair_table(tab, tb, tid, DT);
+  const int wt = wave % XWT, ks = wave / XWT;
+  build_rep_pair_table(tab, tb, tid);
 
   const int tile = xcd_remap_dx(blockIdx.x, ptiles * qtiles);
   const int qt = tile / ptiles, pt = tile - qt * ptiles;
-  const int64_t p0 = (int64_t)pt * DP, q0 = (int64_t)qt * DQ;
-  const int nchunks = static_cast<int>((N + DN - 1) / DN);
-  const int64_t kw = p0 + wave * DRW;                 // this wave's first column
-  const int wblk = (wave * DRW) / kBlock;             // its block within the tile
+  const int64_t k0 = (int64_t)pt * XP, q0 = (int64_t)qt * XQ;
+  const int nchunks = static_cast<int>((N + XN - 1) / XN);
+  const int KB = static_cast<int>(K / kBlock);
 
-  const uint32_t rowb = static_cast<uint32_t>(K / 2);
+  // Buffer descriptors: rows n >= N and tokens m >= M read as zero.
+  const uint32_t nb = static_cast<uint32_t>(N * K / kBlock);
   const BufRes rc = make_bufres(codes, static_cast<uint32_t>(N * K / 2));
-  // byte of columns kw + 2 li, kw + 2 li + 1 in row 0; rows add rowb each.
-  // Columns past K (possible only in the last tile) get a zero block
-  // constant below, so the bytes read there do not matter.
-  const uint32_t cbase = static_cast<uint32_t>(kw / 2) + li;
+  const BufRes re = make_bufres(absmax_q, nb);
+  const BufRes rd = make_bufres(absmax_scale, ((nb + kGroup - 1) / kGroup) * 4u);
+  // dY is addressed from the tile's first token (its 256 rows span less
+  // than 2^31 bytes for N <= 2^22).  (A plain conditional, not min(): the
+  // 64-bit min is opaque to the compiler's uniformity analysis and would put
+  // the descriptor in vector registers.)
+  const int64_t tile_rows = M - q0 < XQ ? M - q0 : XQ;
+  const BufRes ry = make_bufres(dY + q0 * N, static_cast<uint32_t>(tile_rows * N * 2));
 
-  f32x4 acc[2][TB];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-#pragma unroll
-    for (int b = 0; b < TB; ++b) acc[e][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // ---- staging of dY (registers, two chunks deep) and block constants ----
-  u32x4 yr[2][YCH];
-  uint32_t ce[2];    // each thread: one (block, row) constant per chunk
+  // Dequantization role: row dr of the chunk, columns k0 + 16 dp .. +15.
+  // Columns past K (a half tile when K % 128 == 64) get a zero constant.
+  const int dr = tid >> 3, dp = tid & 7;
+  const bool dkok = k0 + 16 * dp < K;
+  const uint32_t dcode = static_cast<uint32_t>(dr * (K / 2) + k0 / 2 + 8 * dp);   // + c 64 K/2
+  const uint32_t dblk = static_cast<uint32_t>(dr * KB + (k0 + 16 * dp) / kBlock);   // + c 64 KB
+  u32x2 cw[2];
+  uint32_t ce[2];
   float cd[2];
-  auto load_y = [&](int c, int st) {
-#pragma unroll
-    for (int j = 0; j < YCH; ++j) {
-      const int idx = tid + j * DT;
-      const int row = idx >> 3, col = idx & 7;
-      const int64_t m = q0 + row, n = (int64_t)c * DN + col * 8;
-      yr[st][j] = (m < M && n < N) ? *reinterpret_cast<const u32x4*>(dY + m * N + n)
-                                   : u32x4{0, 0, 0, 0};
-    }
-    // constants: thread t < 256 -> block t / 64 of the tile, row n0 + t % 64
-    const int cb = (tid >> 6) & 3, cr = tid & 63;
-    const int64_t n = (int64_t)c * DN + cr;
-    const int64_t kb = (p0 / kBlock) + cb;
-    if (n < N && kb * kBlock < K) {
-      const int64_t blk = n * (K / kBlock) + kb;
-      ce[st] = absmax_q[blk];
-      cd[st] = absmax_scale[blk >> 8];
-    } else {
-      ce[st] = 0;
-      cd[st] = 0.f;
-    }
-  };
-  auto store_y = [&](int buf, int st) {
-#pragma unroll
-    for (int j = 0; j < YCH; ++j) {
-      const int idx = tid + j * DT;
-      *reinterpret_cast<u32x4*>(&ys[buf][(idx >> 3) * YS + (idx & 7) * 8]) = yr[st][j];
-    }
-    if (tid < CB * DN) cs[buf][tid] = static_cast<float>(ce[st]) * cd[st];   // fl32(e * d)
-  };
-
-  // ---- code bytes of one chunk: 2 steps x 8 rows, one byte each ----
-  uint32_t cb8[2][2][8];
   auto load_codes = [&](int c, int st) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t row = static_cast<uint32_t>(c * DN + 32 * i + 8 * g + t);
-        cb8[st][i][t] = buf_load_u8(rc, cbase + row * rowb);
-      }
+    const bool live = c < nchunks && dkok;
+    const uint32_t blk = dblk + static_cast<uint32_t>(c * XN * KB);
+    cw[st] = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                   rc, live ? dcode + static_cast<uint32_t>(c * XN) * static_cast<uint32_t>(K / 2)
+                            : 0x80000000u, 0, 0));
+    ce[st] = buf_load_u8(re, live ? blk : 0x80000000u);
+    cd[st] = buf_load_f32(rd, live ? (blk / kGroup) * 4u : 0x80000000u);
   };
-
-  // dY and its constants are staged two chunks ahead, the code bytes one
-  // chunk ahead (each in stage c & 1).
-  load_y(0, 0);
-  load_codes(0, 0);
-  if (nchunks > 1) load_y(1, 1);
-  __syncthreads();   // pair table
-  store_y(0, 0);
-  __syncthreads();
-
-  auto step = [&](int c, auto stc) {
-    constexpr int ST = decltype(stc)::value;
-    if (c + 1 < nchunks) load_codes(c + 1, ST ^ 1);
-    if (c + 2 < nchunks) load_y(c + 2, ST);
-    const auto& cur = cb8[ST];
-    const uint16_t* yt = ys[ST];
-    const float* ct = cs[ST] + wblk * DN;
+  uint32_t ta[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) ta[b] = rep_lane_base(lane);
+  auto dequant = [&](int st, int buf) {
+    const float chat = static_cast<float>(ce[st]) * cd[st];
+    uint16_t* dst = Ws + buf * kXA + dr * XAS;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      // block constants of rows n0 + 32i + 8g + t, t = 0..7
-      const f32x4 c0 = *reinterpret_cast<const f32x4*>(ct + 32 * i + 8 * g);
-      const f32x4 c1 = *reinterpret_cast<const f32x4*>(ct + 32 * i + 8 * g + 4);
-      const float chat[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      float v[8][2];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float2 q = tab[cur[i][t] & 0xFFu];
-        v[t][0] = q.x * chat[t];
-        v[t][1] = q.y * chat[t];
-      }
-      u32x4 A[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        A[e] = u32x4{pack_bf16x2(v[0][e], v[1][e]), pack_bf16x2(v[2][e], v[3][e]),
-                     pack_bf16x2(v[4][e], v[5][e]), pack_bf16x2(v[6][e], v[7][e])};
-#pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        const u32x4 Bf = *reinterpret_cast<const u32x4*>(yt + (16 * b + li) * YS + 32 * i + 8 * g);
-        acc[0][b] = mfma16(A[0], Bf, acc[0][b]);
-        acc[1][b] = mfma16(A[1], Bf, acc[1][b]);
-      }
+      const uint32_t w = cw[st][i];
+      const f32x2 v0 = rep_lookup<0>(ta[0], w);
+      const f32x2 v1 = rep_lookup<1>(ta[1], w);
+      const f32x2 v2 = rep_lookup<2>(ta[2], w);
+      const f32x2 v3 = rep_lookup<3>(ta[3], w);
+      *reinterpret_cast<u32x4*>(dst + 8 * wslot(dr, 2 * dp + i)) =
+          u32x4{pack_bf16x2(v0.x * chat, v0.y * chat), pack_bf16x2(v1.x * chat, v1.y * chat),
+                pack_bf16x2(v2.x * chat, v2.y * chat), pack_bf16x2(v3.x * chat, v3.y * chat)};
     }
-    if (c + 1 < nchunks) store_y(ST ^ 1, ST ^ 1);
+  };
+
+  // dY staging role: piece j of thread tid is token row yr + 64 j (yr = tid / 8)
+  // of the tile, 16-byte piece tid % 8 of its 128-byte chunk row.
+  const int yr = tid >> 3, yq = tid & 7;
+  const uint32_t ysrc = static_cast<uint32_t>((yr * N + 8 * yq) * 2);   // + 128 c
+  u32x4 yw[2][XYPT];
+  auto load_y = [&](int c, int st) {
+    const bool live = c < nchunks && c * XN + 8 * yq < N;
+#pragma unroll
+    for (int j = 0; j < XYPT; ++j)
+      yw[st][j] = buf_load16(
+          ry, live ? ysrc + static_cast<uint32_t>((64 * j * N + c * XN) * 2) : 0x80000000u);
+  };
+  auto store_y = [&](int st, int buf) {
+#pragma unroll
+    for (int j = 0; j < XYPT; ++j) {
+      const int row = yr + 64 * j;
+      *reinterpret_cast<u32x4*>(Ys + buf * kXY + row * XYS + 8 * (yq ^ ((row >> 1) & 7))) =
+          yw[st][j];
+    }
+  };
+
+  f32x4 acc[XTA][XTB];
+#pragma unroll
+  for (int a = 0; a < XTA; ++a)
+#pragma unroll
+    for (int b = 0; b < XTB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // A fragment (columns 16 a + li, rows 32 ks + 8 g .. +7): two transposing
+  // reads of rows nb4 + t/4, columns 16 a + 4 (t % 4) (t = li).
+  auto mma = [&](int buf) {
+    const uint16_t* yt = Ys + buf * kXY + (64 * wt + li) * XYS + 8 * ((g + 4 * ks) ^ (li >> 1));
+    u32x4 bf[XTB];
+#pragma unroll
+    for (int b = 0; b < XTB; ++b) bf[b] = *reinterpret_cast<const u32x4*>(yt + 16 * b * XYS);
+    const uint16_t* wt0 = Ws + buf * kXA;
+#pragma unroll
+    for (int a = 0; a < XTA; ++a) {
+      v4i16 h[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int n = 32 * ks + 8 * g + 4 * e + (li >> 2);
+        const int col = 16 * a + 4 * (li & 3);
+        const uint16_t* src = wt0 + n * XAS + 8 * wslot(n, col >> 3) + (col & 7);
+        h[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4i16*)(src));
+      }
+      const u32x2 h0 = __builtin_bit_cast(u32x2, h[0]), h1 = __builtin_bit_cast(u32x2, h[1]);
+      const u32x4 af = {h0[0], h0[1], h1[0], h1[1]};
+#pragma unroll
+      for (int b = 0; b < XTB; ++b) acc[a][b] = mfma16(af, bf[b], acc[a][b]);
+    }
+  };
+
+  load_codes(0, 0);
+  load_codes(1, 1);
+  load_y(0, 0);
+  load_y(1, 1);
+  __syncthreads();   // level table
+  dequant(0, 0);
+  store_y(0, 0);
+  load_codes(2, 0);
+  load_y(2, 0);
+  __syncthreads();
+  // iteration c: stage chunk c+1 into buffers (c+1)&1 -- dequantize its
+  // codes and store its dY, both loaded two iterations ago -- and refill
+  // those register stages with chunk c+3; multiply chunk c from buffers c&1.
+  auto iter = [&](int c, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    dequant(ST ^ 1, ST ^ 1);
+    store_y(ST ^ 1, ST ^ 1);
+    load_codes(c + 3, ST ^ 1);
+    load_y(c + 3, ST ^ 1);
+    mma(ST);
     __syncthreads();
   };
   for (int c = 0; c < nchunks; c += 2) {
-    step(c, std::integral_constant<int, 0>{});
-    if (c + 1 < nchunks) step(c + 1, std::integral_constant<int, 1>{});
+    iter(c, std::integral_constant<int, 0>{});
+    if (c + 1 < nchunks) iter(c + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- LoRA term s . G . A^T: extra chunks over the rank.  Columns 0..63
-  // of the staged tile carry bf16(s.G) (hi), 64..127 the remainder (lo); the
-  // A operand row of subtile e, lane rho is A[kw + 2 rho + e][j .. j + 7]. ----
-  if (r > 0) {
-    uint16_t* gt = ys[0];
-    for (int j0 = 0; j0 < r; j0 += 64) {
-      for (int idx = tid; idx < DQ * 8; idx += DT) {
-        const int row = idx >> 3, col = idx & 7;
-        const int64_t m = q0 + row;
-        const int j = j0 + col * 8;
-        uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
-        if (m < M && j < r) {
-          const f32x4 t0 = *reinterpret_cast<const f32x4*>(G + m * r + j);
-          const f32x4 t1 = *reinterpret_cast<const f32x4*>(G + m * r + j + 4);
-          const float vv[8] = {t0.x * s, t0.y * s, t0.z * s, t0.w * s,
-                               t1.x * s, t1.y * s, t1.z * s, t1.w * s};
+  // LoRA term: extra steps over the rank, 32 at a time, alternating
+  // between the two halves before their accumulators are added.
+  for (int j0 = 32 * ks; j0 < r; j0 += 64) {
+    const int j = j0 + 8 * g;
+    u32x4 gh[XTB], gl[XTB];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) split_bf16x2(vv[2 * e], vv[2 * e + 1], hi[e], lo[e]);
-        }
-        *reinterpret_cast<u32x4*>(gt + row * YS + col * 8) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<u32x4*>(gt + row * YS + 64 + col * 8) =
-            u32x4{lo[0], lo[1], lo[2], lo[3]};
+    for (int b = 0; b < XTB; ++b) {
+      const int64_t m = q0 + 64 * wt + 16 * b + li;
+      uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
+      if (m < M && j < r) {
+        const f32x4 t0 = *reinterpret_cast<const f32x4*>(G + m * r + j);
+        const f32x4 t1 = *reinterpret_cast<const f32x4*>(G + m * r + j + 4);
+        const float v[8] = {t0.x * s, t0.y * s, t0.z * s, t0.w * s,
+                            t1.x * s, t1.y * s, t1.z * s, t1.w * s};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16x2(v[2 * e], v[2 * e + 1], hi[e], lo[e]);
       }
-      __syncthreads();
+      gh[b] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      gl[b] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = 32 * i + 8 * g;           // column of the staged tile
-        const int j = j0 + (kk & 63);
-        u32x4 A[2];
+    for (int a = 0; a < XTA; ++a) {
+      const int64_t k = k0 + 16 * a + li;
+      const u32x4 af = (k < K && j < r) ? *reinterpret_cast<const u32x4*>(Al + k * r + j)
+                                        : u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int64_t k = kw + 2 * li + e;
-          A[e] = (k < K && j < r) ? *reinterpret_cast<const u32x4*>(Al + k * r + j)
-                                  : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int b = 0; b < TB; ++b) {
-          const u32x4 Bf = *reinterpret_cast<const u32x4*>(gt + (16 * b + li) * YS + kk);
-          acc[0][b] = mfma16(A[0], Bf, acc[0][b]);
-          acc[1][b] = mfma16(A[1], Bf, acc[1][b]);
-        }
+      for (int b = 0; b < XTB; ++b) {
+        acc[a][b] = mfma16(af, gh[b], acc[a][b]);
+        acc[a][b] = mfma16(af, gl[b], acc[a][b]);
       }
-      __syncthreads();
     }
   }
 
-  // ---- store: lane holds columns kw + 8g + 2 rr + e (rr = 0..3, e = 0..1) ----
-  const int64_t k8 = kw + 8 * g;
+  // Add the second n half into the first through LDS, half of the column
+  // subtiles at a time.
+  f32x4* xch = reinterpret_cast<f32x4*>(dyn);   // [XWT][XTA/2][XTB][64]
 #pragma unroll
-  for (int b = 0; b < TB; ++b) {
-    const int64_t m = q0 + 16 * b + li;
-    if (m < M && k8 < K) {
-      const f32x4 a0 = acc[0][b], a1 = acc[1][b];
-      *reinterpret_cast<u32x4*>(dX + m * K + k8) =
-          u32x4{pack_bf16x2(a0.x, a1.x), pack_bf16x2(a0.y, a1.y), pack_bf16x2(a0.z, a1.z),
-                pack_bf16x2(a0.w, a1.w)};
+  for (int h = 0; h < 2; ++h) {
+    if (ks == 1) {
+#pragma unroll
+      for (int a = 0; a < XTA / 2; ++a)
+#pragma unroll
+        for (int b = 0; b < XTB; ++b)
+          xch[((wt * (XTA / 2) + a) * XTB + b) * 64 + lane] = acc[h * (XTA / 2) + a][b];
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+      for (int a = 0; a < XTA / 2; ++a)
+#pragma unroll
+        for (int b = 0; b < XTB; ++b)
+          acc[h * (XTA / 2) + a][b] += xch[((wt * (XTA / 2) + a) * XTB + b) * 64 + lane];
+    }
+    __syncthreads();
+  }
+  if (ks != 0) return;
+
+  // dX[m, k..k+3] for the lane's 4 consecutive columns k of each subtile
+#pragma unroll
+  for (int a = 0; a < XTA; ++a) {
+    const int64_t k = k0 + 16 * a + 4 * g;
+#pragma unroll
+    for (int b = 0; b < XTB; ++b) {
+      const int64_t m = q0 + 64 * wt + 16 * b + li;
+      if (m < M && k < K) {
+        const f32x4 v = acc[a][b];
+        *reinterpret_cast<u32x2*>(dX + m * K + k) =
+            u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+      }
     }
   }
 }
@@ -237,11 +295,16 @@ __global__ __launch_bounds__(DT) void k_dx_gemm2(
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
                           const float* G, const uint16_t* A, int r, float s,
                           uint16_t* dX, const Nf4Tables& tb, hipStream_t stream) {
-  const int ptiles = static_cast<int>((w.K + DP - 1) / DP);
-  const int qtiles = static_cast<int>((M + DQ - 1) / DQ);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_dx_gemm), hipFuncAttributeMaxDynamicSharedMemorySize,
+      kDxLds);
+  if (attr != hipSuccess) return attr;
+  const int ptiles = static_cast<int>((w.K + XP - 1) / XP);
+  const int qtiles = static_cast<int>((M + XQ - 1) / XQ);
   prof_begin(1, stream);
-  hipLaunchKernelGGL(k_dx_gemm2, dim3(ptiles * qtiles), dim3(DT), 0, stream, dY, M, w.codes,
-                     w.absmax_q, w.absmax_scale, w.N, w.K, G, A, r, s, dX, ptiles, qtiles, tb);
+  hipLaunchKernelGGL(k_dx_gemm, dim3(ptiles * qtiles), dim3(XT), kDxLds, stream, dY, M,
+                     w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, G, A, r, s, dX, ptiles,
+                     qtiles, tb);
   prof_end(1, stream);
   return hipGetLastError();
 }

@@ -87,9 +87,12 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   const BufRes rc = make_bufres(codes, static_cast<uint32_t>(N * K / 2));
   const BufRes re = make_bufres(absmax_q, nb);
   const BufRes rd = make_bufres(absmax_scale, ((nb + kGroup - 1) / kGroup) * 4u);
-  const uint64_t xbytes = static_cast<uint64_t>(M) * K * 2;
-  const BufRes rx = make_bufres(X, xbytes < 0x80000000ull ? static_cast<uint32_t>(xbytes)
-                                                          : 0x80000000u);
+  // X is addressed from the tile's first token (its 256 rows span less
+  // than 2^31 bytes for K <= 2^22).  (A plain conditional, not min(): the
+  // 64-bit min is opaque to the compiler's uniformity analysis and would put
+  // the descriptor in vector registers.)
+  const int64_t tile_rows = M - q0 < GQ ? M - q0 : GQ;
+  const BufRes rx = make_bufres(X + q0 * K, static_cast<uint32_t>(tile_rows * K * 2));
 
   // Dequantization role: row dr of the tile, codes 16 dq .. 16 dq + 15 of the chunk.
   const int dr = tid >> 2, dq = tid & 3;
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   // X staging role: piece j of thread tid is token row xr + 64 j (xr = tid / 8)
   // of the tile, 16-byte piece tid % 8 of its 128-byte chunk row.
   const int xr = tid >> 3, xq = tid & 7;
-  const uint32_t xsrc = static_cast<uint32_t>(((q0 + xr) * K + 8 * xq) * 2);   // + 128 c
+  const uint32_t xsrc = static_cast<uint32_t>((xr * K + 8 * xq) * 2);   // + 128 c
   u32x4 xw[2][XPT];
   auto load_x = [&](int c, int st) {
     const bool live = c < nchunks;

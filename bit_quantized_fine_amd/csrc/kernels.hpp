@@ -48,7 +48,8 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
                              const float* T, int nz, float* Tout, const uint16_t* B, int r,
                              float s, uint16_t* Y, const Nf4Tables& tb, hipStream_t stream);
 
-// dX[M,K] = bf16( dY . deq(W) + s . G . A^T ).
+// dX[M,K] = bf16( dY . deq(W) + s . G . A^T ), MFMA path with the
+// dequantized weight tiles staged in LDS and read back transposed.
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
                           const float* G, const uint16_t* A, int r, float s,
                           uint16_t* dX, const Nf4Tables& tb, hipStream_t stream);

@@ -117,8 +117,9 @@ size_t qlora_nf4_scale_count(int64_t N, int64_t K);
  * clamped to [0, 255] (e = 0 when d = 0).  The codes use the unquantized c.
  * Outputs (device): codes [N*K/2], absmax_q [N*K/64], absmax_scale
  * [ceil(N*K/16384)].  W must be finite.  N >= 1, K >= 64, K % 64 == 0,
- * K <= 2^24 and N*K <= 2^32 (the kernels address a weight's codes with
- * 32-bit byte offsets); the same limits apply to every qlora_nf4_weight.
+ * N <= 2^22, K <= 2^22 and N*K <= 2^32 (the kernels address a weight's
+ * codes, and a 256-token tile of X or dY, with 32-bit byte offsets); the
+ * same limits apply to every qlora_nf4_weight.
  */
 int qlora_nf4_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
                        uint8_t* absmax_q, float* absmax_scale,

@@ -105,6 +105,12 @@ def test_linear_validation_before_launch():
     assert L.qlora_linear_fwd(p, 16, ctypes.byref(bad_k), p, p, 16, 1.0, p, p, p, ws_need, None) == 2
     bad_n = _w(4096, 4096, 4096, 60, 128)
     assert L.qlora_linear_fwd(p, 16, ctypes.byref(bad_n), p, p, 16, 1.0, p, p, p, ws_need, None) == 2
+    # 32-bit tile offsets: N and K at most 2^22, N * K at most 2^32
+    for n, k in ((64, (1 << 22) + 64), ((1 << 22) + 8, 64), (1 << 20, 1 << 13)):
+        big = _w(4096, 4096, 4096, n, k)
+        assert L.qlora_linear_fwd(p, 16, ctypes.byref(big), p, p, 16, 1.0, p, p, p, ws_need,
+                                  None) == 2
+        assert L.qlora_nf4_quantize(p, n, k, p, p, p, None) == 2
     # alignment
     assert L.qlora_linear_fwd(ctypes.c_void_p(4098), 16, ctypes.byref(w), p, p, 16, 1.0, p, p, p,
                               ws_need, None) == 4

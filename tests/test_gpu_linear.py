@@ -63,6 +63,7 @@ FWD_CASES = [
     (300, 520, 448, 64, 0.25),       # ragged M, N, K over several tiles
     (256, 384, 1024, 256, 0.0625),   # maximum rank
     (129, 136, 64, 8, 2.0),          # single reduction tile
+    (520, 264, 192, 40, 0.5),        # rank not a multiple of 32, three token tiles
 ]
 
 
@@ -84,6 +85,8 @@ def test_fwd_parity(M, N, K, r, s):
     (300, 520, 448, 64, 0.25),
     (256, 384, 1024, 256, 0.0625),
     (33, 1000, 64 * 33, 64, 0.25),
+    (520, 264, 192, 40, 0.5),        # rank not a multiple of 32, three token tiles
+    (64, 8, 64, 8, 1.0),             # one 8-row reduction chunk, a half column tile
 ])
 def test_bwd_parity(M, N, K, r, s):
     need_gpu()
