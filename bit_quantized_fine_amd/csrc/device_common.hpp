@@ -125,30 +125,14 @@ __device__ __forceinline__ void build_rep_pair_table(char* tab, const Nf4Tables&
 
 typedef __attribute__((address_space(3))) const f32x2 LdsF32x2;
 
-// Write byte B of w into byte 1 of a (bits 8..15), keeping a's other bytes:
-// a = (byte << 8) | (a & 0xFFFF00FF).  One SDWA move.
+// The level pair of byte B of w from the replicated table.  ta holds the
+// lane's copy offset in byte 0; the address is (byte << 8) | copy offset,
+// built by one v_perm_b32 (byte 0 from ta, byte 1 = byte B of w, bytes 2
+// and 3 zero), which the scheduler can move like any other VALU op.
 template <int B>
-__device__ __forceinline__ void put_byte1(uint32_t& a, uint32_t w) {
-  if constexpr (B == 0)
-    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_0"
-        : "+v"(a) : "v"(w));
-  else if constexpr (B == 1)
-    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
-        : "+v"(a) : "v"(w));
-  else if constexpr (B == 2)
-    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_2"
-        : "+v"(a) : "v"(w));
-  else
-    asm("v_mov_b32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
-        : "+v"(a) : "v"(w));
-}
-
-// The level pair of byte B of w from the replicated table; ta holds the
-// lane's copy offset in byte 0 and is reused as the address register.
-template <int B>
-__device__ __forceinline__ f32x2 rep_lookup(uint32_t& ta, uint32_t w) {
-  put_byte1<B>(ta, w);
-  return *reinterpret_cast<LdsF32x2*>(static_cast<uintptr_t>(ta));
+__device__ __forceinline__ f32x2 rep_lookup(uint32_t ta, uint32_t w) {
+  const uint32_t a = __builtin_amdgcn_perm(w, ta, 0x0C0C0000u | ((4u + B) << 8));
+  return *reinterpret_cast<LdsF32x2*>(static_cast<uintptr_t>(a));
 }
 
 __device__ __forceinline__ uint32_t rep_lane_base(int lane) {

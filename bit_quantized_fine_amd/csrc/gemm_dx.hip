@@ -169,27 +169,47 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
 
   // A fragment (columns 16 a + li, rows 32 ks + 8 g .. +7): two transposing
   // reads of rows nb4 + t/4, columns 16 a + 4 (t % 4) (t = li).
-  auto mma = [&](int buf) {
+  // Operands of one 32-n step are read into registers first; the MFMAs then
+  // touch no memory, so the compiler can interleave them with the staging
+  // work of the next chunk.
+  u32x4 af[XTA], bf[XTB];
+  // Transposing-read address of rows 32 ks + 8 g + 4 e + li / 4, columns
+  // 16 a + 4 (li % 4): rbase[e] + 16 (a ^ rsw[e]) + ... in elements, where
+  // rsw[e] is the row's XOR on the 16-column group.
+  int rbase[2], rsw[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int n = 32 * ks + 8 * g + 4 * e + (li >> 2);
+    const int x = (n & 1) ^ (2 * (n & 3)) ^ (8 * ((n >> 3) & 1));   // slot XOR
+    rbase[e] = n * XAS + 8 * (((li & 3) >> 1) ^ (x & 1)) + 4 * (li & 1);
+    rsw[e] = x >> 1;
+  }
+  auto read_frags = [&](int buf) {
     const uint16_t* yt = Ys + buf * kXY + (64 * wt + li) * XYS + 8 * ((g + 4 * ks) ^ (li >> 1));
-    u32x4 bf[XTB];
 #pragma unroll
     for (int b = 0; b < XTB; ++b) bf[b] = *reinterpret_cast<const u32x4*>(yt + 16 * b * XYS);
     const uint16_t* wt0 = Ws + buf * kXA;
+    // Recomputing the 16 addresses each chunk (one VALU op each) is cheaper
+    // than holding them in registers across the loop.
+    int sw[2] = {rsw[0], rsw[1]};
+    asm volatile("" : "+v"(sw[0]), "+v"(sw[1]));
 #pragma unroll
     for (int a = 0; a < XTA; ++a) {
       v4i16 h[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int n = 32 * ks + 8 * g + 4 * e + (li >> 2);
-        const int col = 16 * a + 4 * (li & 3);
-        const uint16_t* src = wt0 + n * XAS + 8 * wslot(n, col >> 3) + (col & 7);
+        const uint16_t* src = wt0 + rbase[e] + 16 * (a ^ sw[e]);
         h[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4i16*)(src));
       }
       const u32x2 h0 = __builtin_bit_cast(u32x2, h[0]), h1 = __builtin_bit_cast(u32x2, h[1]);
-      const u32x4 af = {h0[0], h0[1], h1[0], h1[1]};
-#pragma unroll
-      for (int b = 0; b < XTB; ++b) acc[a][b] = mfma16(af, bf[b], acc[a][b]);
+      af[a] = u32x4{h0[0], h0[1], h1[0], h1[1]};
     }
+  };
+  auto mma = [&]() {
+#pragma unroll
+    for (int a = 0; a < XTA; ++a)
+#pragma unroll
+      for (int b = 0; b < XTB; ++b) acc[a][b] = mfma16(af[a], bf[b], acc[a][b]);
   };
 
   load_codes(0, 0);
@@ -202,21 +222,27 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
   load_codes(2, 0);
   load_y(2, 0);
   __syncthreads();
-  // iteration c: stage chunk c+1 into buffers (c+1)&1 -- dequantize its
-  // codes and store its dY, both loaded two iterations ago -- and refill
-  // those register stages with chunk c+3; multiply chunk c from buffers c&1.
+  // iteration c: read the operands of chunk c from buffers c&1; stage chunk
+  // c+1 into buffers (c+1)&1 -- dequantize its codes and store its dY, both
+  // loaded two iterations ago -- and refill those register stages with chunk
+  // c+3; multiply chunk c.
   auto iter = [&](int c, auto stc) {
     constexpr int ST = decltype(stc)::value;
+    read_frags(ST);
     dequant(ST ^ 1, ST ^ 1);
     store_y(ST ^ 1, ST ^ 1);
     load_codes(c + 3, ST ^ 1);
     load_y(c + 3, ST ^ 1);
-    mma(ST);
+    mma();
     __syncthreads();
   };
+  // Iterations run in pairs with no exit between them, so the compiler's
+  // load counting sees one path and waits only for the stage it consumes.
+  // An odd chunk count adds one pass over a chunk past the end, whose codes,
+  // constants and activations all read as zero: it adds zeros.
   for (int c = 0; c < nchunks; c += 2) {
     iter(c, std::integral_constant<int, 0>{});
-    if (c + 1 < nchunks) iter(c + 1, std::integral_constant<int, 1>{});
+    iter(c + 1, std::integral_constant<int, 1>{});
   }
 
   // LoRA term: extra steps over the rank, 32 at a time, alternating

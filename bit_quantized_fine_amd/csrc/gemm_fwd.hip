@@ -3,24 +3,22 @@
 // Figure 1 of "DL0087 QLoRA": a bf16 tile of W is rebuilt just before the
 // matmul and discarded).
 //
-// Tile layouts in LDS: a row (weight row n or token m) holds its 64 k as
-// eight 16-byte pieces, piece q stored at slot q ^ ((row / 2) % 8).  The
-// writes (dequantized weights, 4 threads per row; X, 8 lanes per row) and the
-// MFMA fragment reads (16 rows per lane group) then all spread over the 64
-// banks.
-//
 // Workgroup = 8 waves, tile = 128 weight rows (n) x 256 tokens (m), reduction
 // in chunks of 64 k (one NF4 block per row).  Every chunk the 512 threads
-// dequantize the tile's 128 x 64 weights once -- thread t takes 16 codes of
-// row t/4 -- into one of two LDS buffers, while the waves multiply the other
-// buffer.  Wave w owns tokens 64 (w % 4) .. +63 and all 128 rows, and the
-// 32-k half (w / 4) of every chunk: it reads its A fragments (weights) and
-// B fragments (X) from LDS.  X reaches LDS through coalesced 16-byte loads
-// (eight lanes per 128-byte token row) issued two chunks ahead.  Each weight is dequantized once per 256 tokens (about
-// one VALU instruction per MFMA); splitting the chunk's two 32-k steps
-// between two waves puts two waves on every SIMD, so one wave's
-// dequantization and LDS waits overlap the other's MFMAs.  The two halves'
-// accumulators are added through LDS at the end.
+// dequantize the tile's 128 x 64 weights once into one of two LDS buffers,
+// while the waves multiply the other buffer.  Wave w owns tokens
+// 64 (w % 4) .. +63 and all 128 rows, and the 32-k half (w / 4) of every
+// chunk; the two halves' accumulators are added through LDS at the end.
+// Splitting the chunk's two 32-k steps between two waves puts two waves on
+// every SIMD (128 accumulator registers each).
+//
+// The dequantized tile is stored fragment-major: the 16 x 32 MFMA operand of
+// row subtile a and k half s is 1 KB in lane order (lane l = 16 g + i holds
+// row 16 a + i, k 32 s + 8 g .. +7), so a wave reads each operand with one
+// contiguous 1 KB access.  Thread t of wave w produces two of those 16-byte
+// pieces from 16 codes of row 16 w + t % 16.  X reaches LDS through
+// coalesced 16-byte loads (eight lanes per 128-byte token row) issued two
+// chunks ahead, its rows' 16-byte pieces XOR-swizzled by (row / 2) % 8.
 //
 // The LoRA update is appended as extra reduction steps over the rank: B^T is
 // staged in LDS through 8x8 transposes, s.T enters as bf16 hi and lo halves.
@@ -40,14 +38,15 @@ constexpr int GWT = 4;           // token groups
 constexpr int GKS = 2;           // waves splitting a chunk's two 32-k steps
 constexpr int GW = GWT * GKS;    // waves
 constexpr int GT = 64 * GW;      // threads
-constexpr int AS = GK;           // LDS row stride of the A tile (128 B, XOR-swizzled)
 constexpr int GTA = GP / 16;     // 16-row subtiles (8)
 constexpr int GTB = GQ / GWT / 16;   // 16-token subtiles per wave (4)
 constexpr int BTS = 64 + 8;     // LDS row stride of the B^T tile
+constexpr int kAFrag = 64 * 8;   // bf16 elements of one 16 x 32 operand (1 KB)
+constexpr int kATile = GTA * GKS * kAFrag;   // one dequantized 128 x 64 tile (16 KB)
 constexpr int XTS = GK;          // LDS row stride of the X tile (128 B, XOR-swizzled)
 constexpr int kXTile = GQ * XTS;   // elements of one X tile buffer
-constexpr int kFwdLds = kRepTabBytes + 2 * GP * AS * 2 + 2 * kXTile * 2;
 constexpr int XPT = GQ * GK / 8 / GT;   // 16-byte X pieces a thread stages per chunk (4)
+constexpr int kFwdLds = kRepTabBytes + 2 * kATile * 2 + 2 * kXTile * 2;
 
 __device__ __forceinline__ int xcd_remap(int b, int total) {
   const int n8 = total >> 3, rem = total & 7;
@@ -67,8 +66,8 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   // the accumulator exchange and the B^T tile of the LoRA update.
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   char* tab = reinterpret_cast<char*>(dyn);
-  uint16_t* As = reinterpret_cast<uint16_t*>(dyn + kRepTabBytes);
-  uint16_t* Xs = As + 2 * GP * AS;   // two X tile buffers [GQ][XTS]
+  uint16_t* As = reinterpret_cast<uint16_t*>(dyn + kRepTabBytes);   // [2][kATile]
+  uint16_t* Xs = As + 2 * kATile;   // two X tile buffers [GQ][XTS]
 
   const int tid = threadIdx.x;
   const int wave = wave_id(), lane = tid & 63;
@@ -94,11 +93,13 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   const int64_t tile_rows = M - q0 < GQ ? M - q0 : GQ;
   const BufRes rx = make_bufres(X + q0 * K, static_cast<uint32_t>(tile_rows * K * 2));
 
-  // Dequantization role: row dr of the tile, codes 16 dq .. 16 dq + 15 of the chunk.
-  const int dr = tid >> 2, dq = tid & 3;
-  const int64_t dn = p0 + dr;
-  const uint32_t dcode = static_cast<uint32_t>(dn * (K / 2)) + 8u * dq;   // + 32 c
-  const uint32_t dblk = static_cast<uint32_t>(dn * KB);                   // + c
+  // Dequantization role: row 16 wave + li of the tile, codes 32 sd + 16 h ..
+  // +15 of the chunk (sd = lane / 32, h = (lane / 16) % 2): pieces 2 h and
+  // 2 h + 1 of the operand (row subtile wave, k half sd).
+  const int sd = lane >> 5, h = (lane >> 4) & 1;
+  const int64_t dn = p0 + 16 * wave + li;
+  const uint32_t dcode = static_cast<uint32_t>(dn * (K / 2)) + 16u * sd + 8u * h;   // + 32 c
+  const uint32_t dblk = static_cast<uint32_t>(dn * KB);                           // + c
   u32x2 cw[2];
   uint32_t ce[2];
   float cd[2];
@@ -110,14 +111,13 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
     ce[st] = buf_load_u8(re, live ? blk : 0x80000000u);
     cd[st] = buf_load_f32(rd, live ? (blk / kGroup) * 4u : 0x80000000u);
   };
-  // A tile row dr, columns 16 dq .. +15: bf16_rne(fl32(level * fl32(e * d)))
+  // bf16_rne(fl32(level * fl32(e * d))) of 16 codes -> two operand pieces
   uint32_t ta[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) ta[b] = rep_lane_base(lane);
+  uint16_t* const dpiece = As + (2 * wave + sd) * kAFrag + (32 * h + li) * 8;
   auto dequant = [&](int st, int buf) {
     const float chat = static_cast<float>(ce[st]) * cd[st];
-    uint16_t* dst = As + buf * GP * AS + dr * AS;
-    const int swz = (dr >> 1) & 7;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t w = cw[st][i];
@@ -125,14 +125,15 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
       const f32x2 v1 = rep_lookup<1>(ta[1], w);
       const f32x2 v2 = rep_lookup<2>(ta[2], w);
       const f32x2 v3 = rep_lookup<3>(ta[3], w);
-      *reinterpret_cast<u32x4*>(dst + 8 * ((2 * dq + i) ^ swz)) =
+      *reinterpret_cast<u32x4*>(dpiece + buf * kATile + 16 * 8 * i) =
           u32x4{pack_bf16x2(v0.x * chat, v0.y * chat), pack_bf16x2(v1.x * chat, v1.y * chat),
                 pack_bf16x2(v2.x * chat, v2.y * chat), pack_bf16x2(v3.x * chat, v3.y * chat)};
     }
   };
 
   // X staging role: piece j of thread tid is token row xr + 64 j (xr = tid / 8)
-  // of the tile, 16-byte piece tid % 8 of its 128-byte chunk row.
+  // of the tile, 16-byte piece tid % 8 of its 128-byte chunk row, stored at
+  // slot (tid % 8) ^ ((row / 2) % 8).
   const int xr = tid >> 3, xq = tid & 7;
   const uint32_t xsrc = static_cast<uint32_t>((xr * K + 8 * xq) * 2);   // + 128 c
   u32x4 xw[2][XPT];
@@ -158,21 +159,28 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
 #pragma unroll
     for (int b = 0; b < GTB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto mma = [&](int buf) {
-    // rows 16 a + li (weights) and 64 wt + 16 b + li (tokens): swizzle
-    // (li / 2) % 8, piece g + 4 ks
-    const int piece = 8 * ((g + 4 * ks) ^ (li >> 1));
-    const uint16_t* at = As + buf * GP * AS + li * AS + piece;
-    const uint16_t* xt = Xs + buf * kXTile + (64 * wt + li) * XTS + piece;
-    u32x4 bf[GTB];
+  // A operand (row subtile a, k half ks): one contiguous 1 KB read; B
+  // operand: token 64 wt + 16 b + li, piece g + 4 ks (swizzle (li / 2) % 8)
+  const uint16_t* const apiece = As + ks * kAFrag + lane * 8;
+  const uint16_t* const xpiece = Xs + (64 * wt + li) * XTS + 8 * ((g + 4 * ks) ^ (li >> 1));
+  // Operands of one 32-k step are read into registers first; the MFMAs then
+  // touch no memory, so the compiler can interleave them with the staging
+  // work of the next chunk (LDS reads and writes it cannot otherwise move
+  // across, not knowing the two buffers are disjoint).
+  u32x4 af[GTA], bf[GTB];
+  auto read_frags = [&](int buf) {
 #pragma unroll
-    for (int b = 0; b < GTB; ++b) bf[b] = *reinterpret_cast<const u32x4*>(xt + 16 * b * XTS);
+    for (int b = 0; b < GTB; ++b)
+      bf[b] = *reinterpret_cast<const u32x4*>(xpiece + buf * kXTile + 16 * b * XTS);
 #pragma unroll
-    for (int a = 0; a < GTA; ++a) {
-      const u32x4 af = *reinterpret_cast<const u32x4*>(at + 16 * a * AS);
+    for (int a = 0; a < GTA; ++a)
+      af[a] = *reinterpret_cast<const u32x4*>(apiece + buf * kATile + 2 * a * kAFrag);
+  };
+  auto mma = [&]() {
 #pragma unroll
-      for (int b = 0; b < GTB; ++b) acc[a][b] = mfma16(af, bf[b], acc[a][b]);
-    }
+    for (int a = 0; a < GTA; ++a)
+#pragma unroll
+      for (int b = 0; b < GTB; ++b) acc[a][b] = mfma16(af[a], bf[b], acc[a][b]);
   };
 
   load_codes(0, 0);
@@ -185,21 +193,27 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   load_codes(2, 0);
   load_x(2, 0);
   __syncthreads();
-  // iteration c: stage chunk c+1 into buffers (c+1)&1 -- dequantize its
-  // codes and store its X, both loaded two iterations ago -- and refill
-  // those register stages with chunk c+3; multiply chunk c from buffers c&1.
+  // iteration c: read the operands of chunk c from buffers c&1; stage chunk
+  // c+1 into buffers (c+1)&1 -- dequantize its codes and store its X, both
+  // loaded two iterations ago -- and refill those register stages with chunk
+  // c+3; multiply chunk c.
   auto iter = [&](int c, auto stc) {
     constexpr int ST = decltype(stc)::value;
+    read_frags(ST);
     dequant(ST ^ 1, ST ^ 1);
     store_x(ST ^ 1, ST ^ 1);
     load_codes(c + 3, ST ^ 1);
     load_x(c + 3, ST ^ 1);
-    mma(ST);
+    mma();
     __syncthreads();
   };
+  // Iterations run in pairs with no exit between them, so the compiler's
+  // load counting sees one path and waits only for the stage it consumes.
+  // An odd chunk count adds one pass over a chunk past the end, whose codes,
+  // constants and activations all read as zero: it adds zeros.
   for (int c = 0; c < nchunks; c += 2) {
     iter(c, std::integral_constant<int, 0>{});
-    if (c + 1 < nchunks) iter(c + 1, std::integral_constant<int, 1>{});
+    iter(c + 1, std::integral_constant<int, 1>{});
   }
 
   // Add the second k half into the first: waves ks = 1 hand their
