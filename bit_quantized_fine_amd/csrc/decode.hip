@@ -39,8 +39,9 @@ constexpr int kDecMaxK = 32768;                // block constants of the rows fi
 constexpr int kDecXLdsBytes = 48 * 1024;       // X staged in LDS up to this size
 constexpr int kDecXPieces = kDecXLdsBytes / 16 / kDecThreads;   // 16-byte X pieces a thread
 // T partial sums: quad q = (token m, ranks 4jq..4jq+3) is summed by
-// kDecThreads / (M r / 4) threads with kDecTSumLoads loads each, which covers
-// the at most kMaxDownPartials partials when M r <= kDecTSumMaxMR.
+// ceil(nz / kDecTSumLoads) threads with kDecTSumLoads loads each; M r <=
+// kDecTSumMaxMR keeps that within the workgroup for the at most
+// kMaxDownPartials partials.
 constexpr int kDecTSumLoads = 8;
 constexpr int kDecTSumMaxMR = 4 * kDecThreads * kDecTSumLoads / kMaxDownPartials;
 constexpr int kDecEPieces = (kDecRows * kDecMaxK / kBlock / 4 + kDecThreads - 1) / kDecThreads;
@@ -125,9 +126,11 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
       xw[i] = buf_load16(rx, 16 * idx < xrange ? 16u * idx : kDecOffNone);
     }
   }
-  // (nz > 0 only with M r <= kDecTSumMaxMR, so tpq * kDecTSumLoads >= nz.)
+  // Quad q is summed by tpq threads (kDecTSumLoads partials each, in
+  // registers), then by one thread over those tpq (nz > 0 only with
+  // M r <= kDecTSumMaxMR, so nq * tpq <= kDecThreads).
   const int nq = M * r / 4;
-  const int tpq = nz > 0 ? kDecThreads / nq : 1;
+  const int tpq = nz > 0 ? (nz + kDecTSumLoads - 1) / kDecTSumLoads : 1;
   const int myq = tid / tpq, sub = tid % tpq;
   f32x4 tp = {0.f, 0.f, 0.f, 0.f};
   if (nz > 0) {
@@ -209,13 +212,6 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   }
   if (tid < ROWS) et[KB * ROWS + tid] = 0;
   if (tid < dmax) dsc[tid] = dv;
-  __syncthreads();
-  if (nz > 0 && tid < nq) {   // fixed order: deterministic
-    f32x4 t = red[tid * tpq];
-    for (int u = 1; u < tpq; ++u) t += red[tid * tpq + u];
-    tfin[tid] = t;
-    if (blockIdx.x == 0) *reinterpret_cast<f32x4*>(Tout + 4 * tid) = t;   // [M][r]
-  }
 
   // Lanes past M read X from the zero slot with stride 0; past K (the second
   // half of a chunk when K % 128 == 64) they meet the zero block constant,
@@ -275,6 +271,16 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     }
   }
 
+  // T's partial sums are added after the main loop, off its critical path.
+  __syncthreads();
+  if (nz > 0 && tid < nq) {   // fixed order: deterministic
+    f32x4 t = red[tid * tpq];
+    for (int u = 1; u < tpq; ++u) t += red[tid * tpq + u];
+    tfin[tid] = t;
+    if (blockIdx.x == 0) *reinterpret_cast<f32x4*>(Tout + 4 * tid) = t;   // [M][r]
+  }
+  __syncthreads();
+
   if (kw < nsteps) {
     const int j = 32 * kw + 8 * g;
     f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;
@@ -297,8 +303,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     acc = mfma16(bw, u32x4{l[0], l[1], l[2], l[3]}, acc);
   }
 
-  __syncthreads();   // the T partial sums in red are no longer read
-  red[wave * 64 + lane] = acc;
+  red[wave * 64 + lane] = acc;   // the T partial sums in red were read before the barrier above
   __syncthreads();
   if (kw == 0) {
     f32x4 t = red[(p * kDecKSlots) * 64 + lane];
@@ -345,9 +350,11 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
                              const float* T, int nz, float* Tout, const uint16_t* B, int r,
                              float s, uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
   prof_begin(2, stream);
+  // Two chunks in flight per wave: with all 16 waves of every CU streaming,
+  // deeper rings (measured up to 8) only delay the first products.
   hipError_t e;
   if (M * w.K * 2 <= kDecXLdsBytes)
-    e = launch_decode_variant<8, true>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+    e = launch_decode_variant<2, true>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
   else
     e = launch_decode_variant<2, false>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
   prof_end(2, stream);
