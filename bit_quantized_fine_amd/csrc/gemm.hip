@@ -1,15 +1,17 @@
 // MFMA GEMMs of the QLoRA NF4 linear layer on gfx950.
 //
 // The rank-r products (T = X.A, G = dY.B^T, dA, dB) have the form C[q, p] = sum_k P[p, k] . Q[q, k]: the
-// workgroup stages a P tile [BP x 64] and a Q tile [BQ x 64] in LDS, both
-// laid out reduction-contiguous ("MFMA ready": a lane's 8 reduction elements
-// are one 16-byte LDS read), and four waves (2 x 2) accumulate their
-// (BP/2 x BQ/2) share with v_mfma_f32_16x16x32_bf16.  Loaders bring each
-// operand into that layout whatever its layout in HBM:
+// workgroup stages a P tile (BP rows x 64 reduction elements) and a Q tile
+// (BQ x 64) in LDS, and four waves (2 x 2) accumulate their (BP/2 x BQ/2)
+// share with v_mfma_f32_16x16x32_bf16.  Each loader fixes its tile's LDS
+// layout and how a lane reads its 8 reduction elements from it:
 //   Bf16Nat  bf16 rows, reduction contiguous          (X, dY, B as [r,N], A as [K,r])
-//   Bf16Tr   bf16 with the reduction as the row index (X^T, dY^T, B^T)
-//   F32Nat / F32Tr  fp32 (T, G) split into bf16 hi and lo passes, so the
-//            fp32 factor keeps ~16 bits through the bf16 MFMA
+//   Bf16Tr   bf16 with the reduction as the row index, transposed in
+//            registers (A^T of T = X.A)
+//   Bf16RedMajor / F32RedMajor  reduction-major tiles kept as they lie in
+//            memory and read with transposing LDS reads (X^T, dY^T, G^T, T^T
+//            of dA and dB); fp32 sources are split into bf16 hi and lo
+//            passes, so the fp32 factor keeps ~16 bits through the bf16 MFMA
 // The weight-streaming GEMMs (forward and dX) have kernels of their own.
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -47,6 +49,11 @@ __device__ __forceinline__ void st_lds16(uint16_t* p, u32x4 v) {
 
 template <int ROWS>
 struct Bf16Nat {   // element (row, k) = src[row * ld + k]
+  static constexpr int TILE = ROWS * LDS_STRIDE;
+  __device__ static u32x4 frag(const uint16_t* tile, int c0, int ks, int lane) {
+    return *reinterpret_cast<const u32x4*>(tile + (c0 + (lane & 15)) * LDS_STRIDE + 32 * ks +
+                                           8 * (lane >> 4));
+  }
   static constexpr int CH = ROWS * BK / 8;              // 16-byte chunks
   static constexpr int CPT = (CH + NT - 1) / NT;
   OpParams o;
@@ -74,6 +81,11 @@ struct Bf16Nat {   // element (row, k) = src[row * ld + k]
 
 template <int ROWS>
 struct Bf16Tr {    // element (row, k) = src[k * ld + row]; rows come in 8s
+  static constexpr int TILE = ROWS * LDS_STRIDE;
+  __device__ static u32x4 frag(const uint16_t* tile, int c0, int ks, int lane) {
+    return *reinterpret_cast<const u32x4*>(tile + (c0 + (lane & 15)) * LDS_STRIDE + 32 * ks +
+                                           8 * (lane >> 4));
+  }
   static constexpr int NP = ROWS;                 // 8x8 patches per tile
   static constexpr int PPT = (NP + NT - 1) / NT;
   static constexpr int RS = ROWS / 8;             // row slabs
@@ -110,125 +122,104 @@ struct Bf16Tr {    // element (row, k) = src[k * ld + row]; rows come in 8s
   }
 };
 
-// fp32 -> bf16 conversion of 8 values, hi part (pass 0) or lo part (pass 1).
-__device__ __forceinline__ u32x4 f32x8_to_bf16(const f32x4& a, const f32x4& b,
-                                               float scale, int pass) {
-  const float v[8] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale,
-                      b.x * scale, b.y * scale, b.z * scale, b.w * scale};
-  uint32_t out[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t hi, lo;
-    split_bf16x2(v[2 * i], v[2 * i + 1], hi, lo);
-    out[i] = pass ? lo : hi;
-  }
-  return u32x4{out[0], out[1], out[2], out[3]};
+// ---------------------------------------------------------------------------
+// Reduction-major operands (element (row, k) = src[k * ld + row]: X^T, dY^T,
+// and the fp32 G^T, T^T of the adapter gradients).  The tile is stored as it
+// lies in memory, [BK reduction rows][COLS] (coalesced 16-byte loads, no
+// register transposes), and the MFMA fragment -- 8 consecutive reduction
+// elements of one row per lane -- is read with ds_read_b64_tr_b16, which
+// transposes 4 x 16 blocks of 16-bit elements across each 16-lane group.
+// 16-byte pieces are XOR-swizzled in 32-byte units so the 8 tile rows of a
+// half-wave transposing read (rows 8g + 4e + i, g = 0, 1) hit distinct banks.
+// ---------------------------------------------------------------------------
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 LdsV4i16;
+
+template <int COLS>
+__device__ __forceinline__ int rm_slot(int row, int piece) {
+  static_assert(COLS == 64 || COLS == 128, "tile width");
+  const int f = COLS == 64 ? (((row >> 1) & 1) | (((row >> 3) & 1) << 1))   // 128-byte rows
+                           : ((row & 3) | (((row >> 3) & 1) << 2));          // 256-byte rows
+  return piece ^ (2 * f);
 }
 
-template <int ROWS>
-struct F32Nat {    // element (row, k) = scale * src[row * ld + k], fp32 source
-  static constexpr int CH = ROWS * BK / 8;
-  static constexpr int CPT = (CH + NT - 1) / NT;
+// Fragment of tile rows (columns) c0 .. c0+15, reduction step ks.
+template <int COLS>
+__device__ __forceinline__ u32x4 rm_frag(const uint16_t* tile, int c0, int ks, int lane) {
+  const int li = lane & 15, g = lane >> 4;
+  const int col = c0 + 4 * (li & 3);
+  u32x2 h[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int red = 32 * ks + 8 * g + 4 * e + (li >> 2);
+    const uint16_t* p = tile + red * COLS + 8 * rm_slot<COLS>(red, col >> 3) + (col & 7);
+    h[e] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4i16*)(p)));
+  }
+  return u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+}
+
+template <int COLS>
+struct Bf16RedMajor {   // element (row, k) = src[k * ld + row], bf16
+  static constexpr int TILE = BK * COLS;
+  static constexpr int PCS = COLS / 8;                 // 16-byte pieces per tile row
+  static constexpr int CPT = BK * PCS / NT;            // pieces a thread
   OpParams o;
   int64_t row0;
-  int pass;
-  f32x4 r[CPT][2];
+  u32x4 r[CPT];
   __device__ void load(int kt, int tid) {
-    const float* src = static_cast<const float*>(o.ptr);
+    const uint16_t* src = static_cast<const uint16_t*>(o.ptr);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      const int row = idx >> 3, kc = idx & 7;
-      const int64_t gr = row0 + row, gk = (int64_t)kt * BK + kc * 8;
-      const bool ok = idx < CH && gr < o.nrows && gk < o.nred;
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      r[c][0] = ok ? *reinterpret_cast<const f32x4*>(src + gr * o.ld + gk) : z;
-      r[c][1] = ok ? *reinterpret_cast<const f32x4*>(src + gr * o.ld + gk + 4) : z;
+      const int idx = tid + c * NT, red = idx / PCS, pc = idx % PCS;
+      const int64_t gk = (int64_t)kt * BK + red, gr = row0 + 8 * pc;
+      r[c] = (gk < o.nred && gr < o.nrows) ? ld16(src + gk * o.ld + gr) : u32x4{0, 0, 0, 0};
     }
   }
   __device__ void store(uint16_t* lds, int tid) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      if (idx < CH)
-        st_lds16(lds + (idx >> 3) * LDS_STRIDE + (idx & 7) * 8,
-                 f32x8_to_bf16(r[c][0], r[c][1], o.scale, pass));
+      const int idx = tid + c * NT, red = idx / PCS, pc = idx % PCS;
+      st_lds16(lds + red * COLS + 8 * rm_slot<COLS>(red, pc), r[c]);
     }
   }
-  // both halves at once: hi into `hi`, lo into `lo`
-  __device__ void store2(uint16_t* hi, uint16_t* lo, int tid) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      if (idx < CH) {
-        const int off = (idx >> 3) * LDS_STRIDE + (idx & 7) * 8;
-        st_lds16(hi + off, f32x8_to_bf16(r[c][0], r[c][1], o.scale, 0));
-        st_lds16(lo + off, f32x8_to_bf16(r[c][0], r[c][1], o.scale, 1));
-      }
-    }
+  __device__ static u32x4 frag(const uint16_t* tile, int c0, int ks, int lane) {
+    return rm_frag<COLS>(tile, c0, ks, lane);
   }
 };
 
-template <int ROWS>
-struct F32Tr {     // element (row, k) = scale * src[k * ld + row], fp32 source
-  static constexpr int NP = ROWS;
-  static constexpr int PPT = (NP + NT - 1) / NT;
-  static constexpr int RS = ROWS / 8;
+template <int COLS>
+struct F32RedMajor {    // element (row, k) = scale * src[k * ld + row], fp32 -> bf16 hi, lo
+  static constexpr int TILE = BK * COLS;
+  static constexpr int QCS = COLS / 4;                 // 4-float pieces per tile row
+  static constexpr int CPT = BK * QCS / NT;
   OpParams o;
   int64_t row0;
-  int pass;
-  f32x4 r[PPT][8][2];
+  f32x4 r[CPT];
   __device__ void load(int kt, int tid) {
     const float* src = static_cast<const float*>(o.ptr);
 #pragma unroll
-    for (int c = 0; c < PPT; ++c) {
-      const int p = tid + c * NT;
-      const int rp = p % RS, kp = p / RS;
-      const int64_t gr = row0 + rp * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t gk = (int64_t)kt * BK + kp * 8 + i;
-        const bool ok = p < NP && gr < o.nrows && gk < o.nred;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        r[c][i][0] = ok ? *reinterpret_cast<const f32x4*>(src + gk * o.ld + gr) : z;
-        r[c][i][1] = ok ? *reinterpret_cast<const f32x4*>(src + gk * o.ld + gr + 4) : z;
-      }
-    }
-  }
-  __device__ void store(uint16_t* lds, int tid) {
-#pragma unroll
-    for (int c = 0; c < PPT; ++c) {
-      const int p = tid + c * NT;
-      if (p < NP) {
-        const int rp = p % RS, kp = p / RS;
-        u32x4 rows[8], t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rows[i] = f32x8_to_bf16(r[c][i][0], r[c][i][1], o.scale, pass);
-        transpose8x8_b16(rows, t);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st_lds16(lds + (rp * 8 + j) * LDS_STRIDE + kp * 8, t[j]);
-      }
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT, red = idx / QCS, qc = idx % QCS;
+      const int64_t gk = (int64_t)kt * BK + red, gr = row0 + 4 * qc;
+      r[c] = (gk < o.nred && gr < o.nrows) ? *reinterpret_cast<const f32x4*>(src + gk * o.ld + gr)
+                                           : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   __device__ void store2(uint16_t* hi, uint16_t* lo, int tid) {
 #pragma unroll
-    for (int c = 0; c < PPT; ++c) {
-      const int p = tid + c * NT;
-      if (p < NP) {
-        const int rp = p % RS, kp = p / RS;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 rows[8], t[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            rows[i] = f32x8_to_bf16(r[c][i][0], r[c][i][1], o.scale, half);
-          transpose8x8_b16(rows, t);
-          uint16_t* dst = half ? lo : hi;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) st_lds16(dst + (rp * 8 + j) * LDS_STRIDE + kp * 8, t[j]);
-        }
-      }
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT, red = idx / QCS, qc = idx % QCS;
+      uint32_t h0, l0, h1, l1;
+      split_bf16x2(r[c].x * o.scale, r[c].y * o.scale, h0, l0);
+      split_bf16x2(r[c].z * o.scale, r[c].w * o.scale, h1, l1);
+      const int off = red * COLS + 8 * rm_slot<COLS>(red, qc >> 1) + 4 * (qc & 1);
+      *reinterpret_cast<u32x2*>(hi + off) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(lo + off) = u32x2{l0, l1};
     }
+  }
+  __device__ static u32x4 frag(const uint16_t* tile, int c0, int ks, int lane) {
+    return rm_frag<COLS>(tile, c0, ks, lane);
   }
 };
 
@@ -246,18 +237,17 @@ struct Mma {
 #pragma unroll
       for (int j = 0; j < TQ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // FP, FQ: the operands' tile layouts (their loaders' frag readers)
+  template <class FP, class FQ>
   __device__ void step(const uint16_t* ldsP, const uint16_t* ldsQ, int wave, int lane) {
     const int wp = (wave & 1) * (BP / 2), wq = (wave >> 1) * (BQ / 2);
-    const int lr = lane & 15, lk = 8 * (lane >> 4);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       u32x4 a[TP], b[TQ];
 #pragma unroll
-      for (int i = 0; i < TP; ++i)
-        a[i] = *reinterpret_cast<const u32x4*>(ldsP + (wp + 16 * i + lr) * LDS_STRIDE + ks * 32 + lk);
+      for (int i = 0; i < TP; ++i) a[i] = FP::frag(ldsP, wp + 16 * i, ks, lane);
 #pragma unroll
-      for (int j = 0; j < TQ; ++j)
-        b[j] = *reinterpret_cast<const u32x4*>(ldsQ + (wq + 16 * j + lr) * LDS_STRIDE + ks * 32 + lk);
+      for (int j = 0; j < TQ; ++j) b[j] = FQ::frag(ldsQ, wq + 16 * j, ks, lane);
 #pragma unroll
       for (int i = 0; i < TP; ++i)
 #pragma unroll
@@ -272,8 +262,8 @@ template <int BP, int BQ, class LP, class LQ>
 __device__ void run_tiles(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mma,
                           uint16_t* lds, int tid) {
   if (kt0 >= kt1) return;
-  uint16_t* bufP[2] = {lds, lds + (BP + BQ) * LDS_STRIDE};
-  uint16_t* bufQ[2] = {lds + BP * LDS_STRIDE, lds + (2 * BP + BQ) * LDS_STRIDE};
+  uint16_t* bufP[2] = {lds, lds + LP::TILE + LQ::TILE};
+  uint16_t* bufQ[2] = {lds + LP::TILE, lds + 2 * LP::TILE + LQ::TILE};
   const int wave = wave_id(), lane = tid & 63;
   lp.load(kt0, tid);
   lq.load(kt0, tid);
@@ -288,7 +278,7 @@ __device__ void run_tiles(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mma,
       lp.load(kt + 1, tid);
       lq.load(kt + 1, tid);
     }
-    mma.step(bufP[cur], bufQ[cur], wave, lane);
+    mma.template step<LP, LQ>(bufP[cur], bufQ[cur], wave, lane);
     if (more) {
       lp.store(bufP[cur ^ 1], tid);
       lq.store(bufQ[cur ^ 1], tid);
@@ -305,12 +295,12 @@ template <int BP, int BQ, int HL, class LP, class LQ>
 __device__ void run_tiles_hilo(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mma,
                                uint16_t* lds, int tid) {
   if (kt0 >= kt1) return;
-  constexpr int XR = HL == 1 ? BP : BQ;   // rows of the extra (lo) tile
-  constexpr int BUF = (BP + BQ + XR) * LDS_STRIDE;
+  constexpr int XT = HL == 1 ? LP::TILE : LQ::TILE;   // the extra (lo) tile
+  constexpr int BUF = LP::TILE + LQ::TILE + XT;
   const int wave = wave_id(), lane = tid & 63;
   auto P = [&](int b) { return lds + b * BUF; };
-  auto Q = [&](int b) { return lds + b * BUF + BP * LDS_STRIDE; };
-  auto X = [&](int b) { return lds + b * BUF + (BP + BQ) * LDS_STRIDE; };
+  auto Q = [&](int b) { return lds + b * BUF + LP::TILE; };
+  auto X = [&](int b) { return lds + b * BUF + LP::TILE + LQ::TILE; };
   auto store = [&](int b) {
     if constexpr (HL == 1) {
       lp.store2(P(b), X(b), tid);
@@ -332,11 +322,11 @@ __device__ void run_tiles_hilo(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mm
       lp.load(kt + 1, tid);
       lq.load(kt + 1, tid);
     }
-    mma.step(P(cur), Q(cur), wave, lane);
+    mma.template step<LP, LQ>(P(cur), Q(cur), wave, lane);
     if constexpr (HL == 1)
-      mma.step(X(cur), Q(cur), wave, lane);
+      mma.template step<LP, LQ>(X(cur), Q(cur), wave, lane);
     else
-      mma.step(P(cur), X(cur), wave, lane);
+      mma.template step<LP, LQ>(P(cur), X(cur), wave, lane);
     if (more) store(cur ^ 1);
     __syncthreads();
   }
@@ -387,8 +377,8 @@ __device__ void store_f32(const Mma<BP, BQ>& mma, float* out, int64_t ldo,
 template <int BP, int BQ, class LP, class LQ, int HL>
 __global__ __launch_bounds__(NT) void k_rank(OpParams po, OpParams qo, int ntiles,
                                              int tps, float* ws, int64_t P, int64_t Q) {
-  constexpr int XR = HL == 0 ? 0 : (HL == 1 ? BP : BQ);
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (BP + BQ + XR) * LDS_STRIDE];
+  constexpr int XT = HL == 0 ? 0 : (HL == 1 ? LP::TILE : LQ::TILE);
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (LP::TILE + LQ::TILE + XT)];
   const int tid = threadIdx.x;
   const int64_t p0 = (int64_t)blockIdx.x * BP, q0 = (int64_t)blockIdx.y * BQ;
   const int z = blockIdx.z;
@@ -629,7 +619,7 @@ hipError_t launch_grad_a(const uint16_t* X, int64_t M, int64_t K, const float* G
   const int64_t pt = (r + RB_R - 1) / RB_R, qt = (K + RB_X - 1) / RB_X;
   const Split sp = choose_split(M, pt, qt);
   prof_begin(4, stream);
-  hipLaunchKernelGGL((k_rank<RB_R, RB_X, F32Tr<RB_R>, Bf16Tr<RB_X>, 1>),
+  hipLaunchKernelGGL((k_rank<RB_R, RB_X, F32RedMajor<RB_R>, Bf16RedMajor<RB_X>, 1>),
                      dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(G, r, r, M),
                      op(X, K, K, M), sp.ntiles, sp.tps, ws, (int64_t)r, K);
   hipError_t e = hipGetLastError();
@@ -643,7 +633,7 @@ hipError_t launch_grad_b(const uint16_t* dY, int64_t M, int64_t N, const float* 
   const int64_t pt = (N + RB_X - 1) / RB_X, qt = (r + RB_R - 1) / RB_R;
   const Split sp = choose_split(M, pt, qt);
   prof_begin(4, stream);
-  hipLaunchKernelGGL((k_rank<RB_X, RB_R, Bf16Tr<RB_X>, F32Tr<RB_R>, 2>),
+  hipLaunchKernelGGL((k_rank<RB_X, RB_R, Bf16RedMajor<RB_X>, F32RedMajor<RB_R>, 2>),
                      dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(dY, N, N, M),
                      op(T, r, r, M), sp.ntiles, sp.tps, ws, N, (int64_t)r);
   hipError_t e = hipGetLastError();
