@@ -5,12 +5,10 @@
 // (BQ x 64) in LDS, and four waves (2 x 2) accumulate their (BP/2 x BQ/2)
 // share with v_mfma_f32_16x16x32_bf16.  Each loader fixes its tile's LDS
 // layout and how a lane reads its 8 reduction elements from it:
-//   Bf16Nat  bf16 rows, reduction contiguous          (X, dY, B as [r,N], A as [K,r])
-//   Bf16Tr   bf16 with the reduction as the row index, transposed in
-//            registers (A^T of T = X.A)
+//   Bf16Nat  bf16 rows, reduction contiguous (X and dY of T and G, B as [r,N])
 //   Bf16RedMajor / F32RedMajor  reduction-major tiles kept as they lie in
-//            memory and read with transposing LDS reads (X^T, dY^T, G^T, T^T
-//            of dA and dB); fp32 sources are split into bf16 hi and lo
+//            memory and read with transposing LDS reads (A as [K,r]; X, dY,
+//            G, T of dA and dB); fp32 sources are split into bf16 hi and lo
 //            passes, so the fp32 factor keeps ~16 bits through the bf16 MFMA
 // The weight-streaming GEMMs (forward and dX) have kernels of their own.
 #include "device_common.hpp"
@@ -75,49 +73,6 @@ struct Bf16Nat {   // element (row, k) = src[row * ld + k]
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * NT;
       if (idx < CH) st_lds16(lds + (idx >> 3) * LDS_STRIDE + (idx & 7) * 8, r[c]);
-    }
-  }
-};
-
-template <int ROWS>
-struct Bf16Tr {    // element (row, k) = src[k * ld + row]; rows come in 8s
-  static constexpr int TILE = ROWS * LDS_STRIDE;
-  __device__ static u32x4 frag(const uint16_t* tile, int c0, int ks, int lane) {
-    return *reinterpret_cast<const u32x4*>(tile + (c0 + (lane & 15)) * LDS_STRIDE + 32 * ks +
-                                           8 * (lane >> 4));
-  }
-  static constexpr int NP = ROWS;                 // 8x8 patches per tile
-  static constexpr int PPT = (NP + NT - 1) / NT;
-  static constexpr int RS = ROWS / 8;             // row slabs
-  OpParams o;
-  int64_t row0;
-  u32x4 r[PPT][8];
-  __device__ void load(int kt, int tid) {
-    const uint16_t* src = static_cast<const uint16_t*>(o.ptr);
-#pragma unroll
-    for (int c = 0; c < PPT; ++c) {
-      const int p = tid + c * NT;
-      const int rp = p % RS, kp = p / RS;
-      const int64_t gr = row0 + rp * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t gk = (int64_t)kt * BK + kp * 8 + i;
-        r[c][i] = (p < NP && gr < o.nrows && gk < o.nred) ? ld16(src + gk * o.ld + gr)
-                                                          : u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-  __device__ void store(uint16_t* lds, int tid) {
-#pragma unroll
-    for (int c = 0; c < PPT; ++c) {
-      const int p = tid + c * NT;
-      if (p < NP) {
-        const int rp = p % RS, kp = p / RS;
-        u32x4 t[8];
-        transpose8x8_b16(r[c], t);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st_lds16(lds + (rp * 8 + j) * LDS_STRIDE + kp * 8, t[j]);
-      }
     }
   }
 };
@@ -590,7 +545,7 @@ hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint1
   const int64_t pt = (r + RB_R - 1) / RB_R, qt = (M + RB_X - 1) / RB_X;
   const Split sp = choose_split(K, pt, qt);
   prof_begin(4, stream);
-  hipLaunchKernelGGL((k_rank<RB_R, RB_X, Bf16Tr<RB_R>, Bf16Nat<RB_X>, 0>),
+  hipLaunchKernelGGL((k_rank<RB_R, RB_X, Bf16RedMajor<RB_R>, Bf16Nat<RB_X>, 0>),
                      dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(A, r, r, K),
                      op(X, K, M, K), sp.ntiles, sp.tps, ws, (int64_t)r, M);
   hipError_t e = hipGetLastError();
