@@ -211,79 +211,72 @@ struct Mma {
   }
 };
 
-// Runs reduction tiles [kt0, kt1) through the two LDS buffers:
-// prefetch tile t+1 into registers, multiply tile t, store t+1, barrier.
-template <int BP, int BQ, class LP, class LQ>
-__device__ void run_tiles(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mma,
+// Runs reduction tiles [kt0, kt1) through two LDS buffers with a ring of D
+// register stages (tiles are loaded D ahead; a depth of 4 measured no faster
+// than 2 for these memory-light tiles).  HL selects
+// an fp32 operand split into bf16 hi and lo halves (1: P, 2: Q): both halves
+// are staged per tile and multiplied against the other operand, which is
+// loaded once.  Buffer layout: [P or P_hi][Q or Q_hi][second half].
+template <int BP, int BQ, int HL, int D, class LP, class LQ>
+__device__ void run_tiles(const LP& lp0, const LQ& lq0, int kt0, int kt1, Mma<BP, BQ>& mma,
                           uint16_t* lds, int tid) {
+  static_assert(D % 2 == 0, "the ring depth keeps the LDS buffer of a slot fixed");
   if (kt0 >= kt1) return;
-  uint16_t* bufP[2] = {lds, lds + LP::TILE + LQ::TILE};
-  uint16_t* bufQ[2] = {lds + LP::TILE, lds + 2 * LP::TILE + LQ::TILE};
-  const int wave = wave_id(), lane = tid & 63;
-  lp.load(kt0, tid);
-  lq.load(kt0, tid);
-  __syncthreads();
-  lp.store(bufP[0], tid);
-  lq.store(bufQ[0], tid);
-  __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int cur = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) {
-      lp.load(kt + 1, tid);
-      lq.load(kt + 1, tid);
-    }
-    mma.template step<LP, LQ>(bufP[cur], bufQ[cur], wave, lane);
-    if (more) {
-      lp.store(bufP[cur ^ 1], tid);
-      lq.store(bufQ[cur ^ 1], tid);
-    }
-    __syncthreads();
-  }
-}
-
-// Same tile loop with one operand an fp32 source split into bf16 hi and lo
-// halves (HL = 1: the P operand, HL = 2: the Q operand): both halves are
-// staged per tile and multiplied against the other operand, which is loaded
-// once.  Buffer layout: [P or P_hi][Q or Q_hi][second half].
-template <int BP, int BQ, int HL, class LP, class LQ>
-__device__ void run_tiles_hilo(LP& lp, LQ& lq, int kt0, int kt1, Mma<BP, BQ>& mma,
-                               uint16_t* lds, int tid) {
-  if (kt0 >= kt1) return;
-  constexpr int XT = HL == 1 ? LP::TILE : LQ::TILE;   // the extra (lo) tile
+  constexpr int XT = HL == 0 ? 0 : (HL == 1 ? LP::TILE : LQ::TILE);   // the extra (lo) tile
   constexpr int BUF = LP::TILE + LQ::TILE + XT;
   const int wave = wave_id(), lane = tid & 63;
+  LP lp[D];
+  LQ lq[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    lp[d] = lp0;
+    lq[d] = lq0;
+  }
   auto P = [&](int b) { return lds + b * BUF; };
   auto Q = [&](int b) { return lds + b * BUF + LP::TILE; };
   auto X = [&](int b) { return lds + b * BUF + LP::TILE + LQ::TILE; };
-  auto store = [&](int b) {
-    if constexpr (HL == 1) {
-      lp.store2(P(b), X(b), tid);
-      lq.store(Q(b), tid);
-    } else {
-      lp.store(P(b), tid);
-      lq.store2(Q(b), X(b), tid);
+  auto load = [&](int t, int d) {
+    if (t < kt1) {
+      lp[d].load(t, tid);
+      lq[d].load(t, tid);
     }
   };
-  lp.load(kt0, tid);
-  lq.load(kt0, tid);
-  __syncthreads();
-  store(0);
-  __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int cur = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) {
-      lp.load(kt + 1, tid);
-      lq.load(kt + 1, tid);
+  auto store = [&](int d, int b) {
+    if constexpr (HL == 0) {
+      lp[d].store(P(b), tid);
+      lq[d].store(Q(b), tid);
+    } else if constexpr (HL == 1) {
+      lp[d].store2(P(b), X(b), tid);
+      lq[d].store(Q(b), tid);
+    } else {
+      lp[d].store(P(b), tid);
+      lq[d].store2(Q(b), X(b), tid);
     }
-    mma.template step<LP, LQ>(P(cur), Q(cur), wave, lane);
-    if constexpr (HL == 1)
-      mma.template step<LP, LQ>(X(cur), Q(cur), wave, lane);
-    else
-      mma.template step<LP, LQ>(P(cur), X(cur), wave, lane);
-    if (more) store(cur ^ 1);
-    __syncthreads();
+  };
+  auto step = [&](int b) {
+    mma.template step<LP, LQ>(P(b), Q(b), wave, lane);
+    if constexpr (HL == 1) mma.template step<LP, LQ>(X(b), Q(b), wave, lane);
+    if constexpr (HL == 2) mma.template step<LP, LQ>(P(b), X(b), wave, lane);
+  };
+  // tile t lives in register slot (t - kt0) % D and LDS buffer (t - kt0) % 2
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(kt0 + d, d);
+  store(0, 0);
+  load(kt0 + D, 0);
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; kt += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int t = kt + u;
+      if (t < kt1) {
+        step(u & 1);
+        if (t + 1 < kt1) {
+          store((u + 1) % D, (u & 1) ^ 1);
+          load(t + 1 + D, (u + 1) % D);
+        }
+        __syncthreads();
+      }
+    }
   }
 }
 
@@ -342,10 +335,7 @@ __global__ __launch_bounds__(NT) void k_rank(OpParams po, OpParams qo, int ntile
   mma.zero();
   LP lp{po, p0};
   LQ lq{qo, q0};
-  if constexpr (HL == 0)
-    run_tiles<BP, BQ>(lp, lq, kt0, kt1, mma, lds, tid);
-  else
-    run_tiles_hilo<BP, BQ, HL>(lp, lq, kt0, kt1, mma, lds, tid);
+  run_tiles<BP, BQ, HL, 2>(lp, lq, kt0, kt1, mma, lds, tid);
   store_f32(mma, ws + (int64_t)z * P * Q, P, p0, q0, P, Q, tid);
 }
 
