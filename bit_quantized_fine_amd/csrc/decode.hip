@@ -36,7 +36,8 @@ constexpr int kDecRows = 16 * kDecR;
 // limited to N*K <= 2^32, so their code buffers hold at most 2^31 bytes).
 constexpr uint32_t kDecOffNone = 0x80000000u;
 constexpr int kDecMaxK = 32768;                // block constants of the rows fit in LDS
-constexpr int kDecXLdsBytes = 48 * 1024;       // X staged in LDS up to this size
+constexpr int kDecXLdsBytes = 64 * 1024;       // X staged in LDS up to this size
+constexpr int kDecLdsMax = 160 * 1024;         // LDS of one workgroup
 constexpr int kDecXPieces = kDecXLdsBytes / 16 / kDecThreads;   // 16-byte X pieces a thread
 // T partial sums: quad q = (token m, ranks 4jq..4jq+3) is summed by
 // ceil(nz / kDecTSumLoads) threads with kDecTSumLoads loads each; M r <=
@@ -327,7 +328,7 @@ hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w,
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_fwd_decode<D, XLDS>),
       hipFuncAttributeMaxDynamicSharedMemorySize,
-      DecLds(1, kDecMaxK, false).total + (XLDS ? kDecXLdsBytes + 128 : 0));
+      XLDS ? kDecLdsMax : DecLds(1, kDecMaxK, false).total);
   if (attr != hipSuccess) return attr;
   const DecLds L(M, w.K, XLDS);
   const unsigned grid = static_cast<unsigned>((w.N + kDecRows - 1) / kDecRows);
@@ -353,7 +354,9 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
   // Two chunks in flight per wave: with all 16 waves of every CU streaming,
   // deeper rings (measured up to 8) only delay the first products.
   hipError_t e;
-  if (M * w.K * 2 <= kDecXLdsBytes)
+  // X goes to LDS when it fits next to the rest (M = 1 always; M = 4 up to
+  // K = 8192); otherwise each wave reads its X fragments from global memory.
+  if (M * w.K * 2 <= kDecXLdsBytes && DecLds(M, w.K, true).total <= kDecLdsMax)
     e = launch_decode_variant<2, true>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
   else
     e = launch_decode_variant<2, false>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
