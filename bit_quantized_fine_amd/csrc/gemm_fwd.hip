@@ -216,31 +216,9 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
     iter(c + 1, std::integral_constant<int, 1>{});
   }
 
-  // Add the second k half into the first: waves ks = 1 hand their
-  // accumulators over through LDS, half of the row subtiles at a time.
-  f32x4* xch = reinterpret_cast<f32x4*>(dyn);   // [GWT][GTA/2][GTB][64]
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (ks == 1) {
-#pragma unroll
-      for (int a = 0; a < GTA / 2; ++a)
-#pragma unroll
-        for (int b = 0; b < GTB; ++b)
-          xch[((wt * (GTA / 2) + a) * GTB + b) * 64 + lane] = acc[h * (GTA / 2) + a][b];
-    }
-    __syncthreads();
-    if (ks == 0) {
-#pragma unroll
-      for (int a = 0; a < GTA / 2; ++a)
-#pragma unroll
-        for (int b = 0; b < GTB; ++b)
-          acc[h * (GTA / 2) + a][b] += xch[((wt * (GTA / 2) + a) * GTB + b) * 64 + lane];
-    }
-    __syncthreads();
-  }
-
   // LoRA update: 64 ranks at a time, B^T tile [128 rows][64 ranks] in LDS,
-  // s.T hi / lo halves per lane from global memory.
+  // s.T hi / lo halves per lane from global memory.  Each k half takes one
+  // of the chunk's two 32-rank steps, before the halves are added.
   if (r > 0) {
     uint16_t* bt = As;
     for (int j0 = 0; j0 < r; j0 += 64) {
@@ -260,9 +238,9 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
           *reinterpret_cast<u32x4*>(bt + (rp * 8 + t) * BTS + kp * 8) = cols[t];
       }
       __syncthreads();
-      if (ks == 0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
+      {
+        const int i = ks;
+        {
           const int j = j0 + 32 * i + 8 * g;
           u32x4 th[GTB], tl[GTB];
 #pragma unroll
@@ -294,6 +272,29 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
       }
       __syncthreads();
     }
+  }
+
+  // Add the second k half into the first: waves ks = 1 hand their
+  // accumulators over through LDS, half of the row subtiles at a time.
+  f32x4* xch = reinterpret_cast<f32x4*>(dyn);   // [GWT][GTA/2][GTB][64]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (ks == 1) {
+#pragma unroll
+      for (int a = 0; a < GTA / 2; ++a)
+#pragma unroll
+        for (int b = 0; b < GTB; ++b)
+          xch[((wt * (GTA / 2) + a) * GTB + b) * 64 + lane] = acc[h * (GTA / 2) + a][b];
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+      for (int a = 0; a < GTA / 2; ++a)
+#pragma unroll
+        for (int b = 0; b < GTB; ++b)
+          acc[h * (GTA / 2) + a][b] += xch[((wt * (GTA / 2) + a) * GTB + b) * 64 + lane];
+    }
+    __syncthreads();
   }
 
   // Y[m, n..n+3] for the lane's 4 consecutive rows n of each subtile
