@@ -17,7 +17,7 @@
 // workgroup's rows, and X itself when it is small, are staged in LDS once.
 // The byte-pair level table sits in LDS as 32 copies interleaved at 8-byte
 // steps in 256-byte rows, so lane l reads copy (l % 32) and a lookup never
-// meets a bank conflict; its address is one SDWA byte move.  The waves'
+// meets a bank conflict; its address is one byte permute.  The waves'
 // partial sums meet in LDS; the LoRA update is added as extra MFMA steps
 // over the rank before that reduction.
 #include "device_common.hpp"
@@ -38,14 +38,15 @@ constexpr uint32_t kDecOffNone = 0x80000000u;
 constexpr int kDecMaxK = 32768;                // block constants of the rows fit in LDS
 constexpr int kDecXLdsBytes = 64 * 1024;       // X staged in LDS up to this size
 constexpr int kDecLdsMax = 160 * 1024;         // LDS of one workgroup
-constexpr int kDecXPieces = kDecXLdsBytes / 16 / kDecThreads;   // 16-byte X pieces a thread
-// T partial sums: quad q = (token m, ranks 4jq..4jq+3) is summed by
-// ceil(nz / kDecTSumLoads) threads with kDecTSumLoads loads each; M r <=
-// kDecTSumMaxMR keeps that within the workgroup for the at most
-// kMaxDownPartials partials.
-constexpr int kDecTSumLoads = 8;
-constexpr int kDecTSumMaxMR = 4 * kDecThreads * kDecTSumLoads / kMaxDownPartials;
-constexpr int kDecEPieces = (kDecRows * kDecMaxK / kBlock / 4 + kDecThreads - 1) / kDecThreads;
+constexpr int kDecXPieces = kDecXLdsBytes / 16 / kDecThreads;   // at most 4 16-byte X pieces a thread
+// T partial sums (at most kMaxDownPartials of them) are added up by
+// half-waves: half-wave h takes quads (4 ranks of one token) h and h + 32,
+// its lane z partial z.  M r <= kDecTSumMaxMR keeps that within two quads
+// per half-wave.
+constexpr int kDecTQuads = 2;
+constexpr int kDecTSumMaxMR = 4 * (kDecThreads / 32) * kDecTQuads;
+static_assert(kMaxDownPartials <= 32, "one partial per lane of a half-wave");
+constexpr int kDecEPieces = (kDecRows * kDecMaxK / kBlock / 8 + kDecThreads - 1) / kDecThreads;   // 8-byte pieces
 
 int round16(int64_t v) { return static_cast<int>((v + 15) / 16 * 16); }
 
@@ -68,7 +69,7 @@ struct DecLds {
 
 }  // namespace
 
-template <int D, bool XLDS>
+template <int D, int XP>
 __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
@@ -76,13 +77,16 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const uint16_t* __restrict__ Bl, int r, float s, uint16_t* __restrict__ Y,
     Nf4Tables tb, int eoff, int doff, int xoff, int dmax, float inv_kb) {
   constexpr int ROWS = kDecRows;
+  constexpr bool XLDS = XP > 0;   // X staged in LDS, XP 16-byte pieces per thread
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   char* tab = reinterpret_cast<char*>(dyn);                          // level pairs
   f32x4* red = reinterpret_cast<f32x4*>(dyn + kRepTabBytes);            // [kDecThreads]
   f32x4* tfin = red + kDecThreads;                                   // [kDecTSumMaxMR / 4]
+  uint16_t* bst = reinterpret_cast<uint16_t*>(red);                  // B columns [r][ROWS] until the exchange
   uint8_t* et = dyn + eoff;                                          // [KB + 1][ROWS]
   float* dsc = reinterpret_cast<float*>(dyn + doff);                 // [dmax]
   uint16_t* xs = reinterpret_cast<uint16_t*>(dyn + xoff);            // [M][K], zeros
+  const Levels lv = load_levels(tb);
   const int tid = threadIdx.x;
   const int wave = wave_id(), lane = tid & 63;
   const int p = wave / kDecKSlots, kw = wave % kDecKSlots;           // fragment, K slot
@@ -106,45 +110,65 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // Staging loads first, a fixed number per thread, so that waiting for them
   // does not wait for the code stream issued after them: the block constants
   // of the workgroup's rows (one contiguous byte range, read as dwords), their
-  // group scales, X, and the partial sums of T.
+  // group scales, X, and for the LoRA update (used only after the main loop)
+  // the partial sums of T and this lane's column of B.
   const uint32_t e0 = static_cast<uint32_t>(n0) * KB;   // first block of the workgroup
   const uint32_t g0 = e0 / kGroup;
   const int erange = ROWS * KB;                         // bytes, a multiple of 4
-  uint32_t ev[kDecEPieces];
+  uint32_t ev[2 * kDecEPieces];
 #pragma unroll
   for (int i = 0; i < kDecEPieces; ++i) {
     const int idx = tid + i * kDecThreads;
-    ev[i] = __builtin_amdgcn_raw_buffer_load_b32(re, 4 * idx < erange ? e0 + 4u * idx
-                                                                      : kDecOffNone, 0, 0);
+    const u32x2 v = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(re, 8 * idx < erange ? e0 + 8u * idx
+                                                                        : kDecOffNone, 0, 0));
+    ev[2 * i] = v.x;
+    ev[2 * i + 1] = v.y;
   }
   const float dv = buf_load_f32(rd, tid < dmax ? (g0 + tid) * 4u : kDecOffNone);
-  u32x4 xw[XLDS ? kDecXPieces : 1];
+  // X: XP pieces per thread, as many as M K 2 bytes need (a load whose lanes
+  // all fall outside the range still occupies the address unit, and at kernel
+  // start the staging loads of 16 waves queue there ahead of the code stream)
+  u32x4 xw[XLDS ? XP : 1];
   const int xrange = M * K32 * 2;
   if constexpr (XLDS) {
 #pragma unroll
-    for (int i = 0; i < kDecXPieces; ++i) {
+    for (int i = 0; i < XP; ++i) {
       const int idx = tid + i * kDecThreads;
       xw[i] = buf_load16(rx, 16 * idx < xrange ? 16u * idx : kDecOffNone);
     }
   }
-  // Quad q is summed by tpq threads (kDecTSumLoads partials each, in
-  // registers), then by one thread over those tpq (nz > 0 only with
-  // M r <= kDecTSumMaxMR, so nq * tpq <= kDecThreads).
+  // T for the LoRA update, used only after the main loop.  With nz > 0,
+  // half-wave h sums quads (4 ranks of one token) h and h + 32 over the
+  // partials, lane z loading partial z; with nz == 0 T is final and the lanes
+  // of the LoRA waves load their own 8 values of it.
+  const int nsteps = (r + 31) / 32;
   const int nq = M * r / 4;
-  const int tpq = nz > 0 ? (nz + kDecTSumLoads - 1) / kDecTSumLoads : 1;
-  const int myq = tid / tpq, sub = tid % tpq;
-  f32x4 tp = {0.f, 0.f, 0.f, 0.f};
-  if (nz > 0) {
-    const BufRes rt = make_bufres(T, static_cast<uint32_t>(nz * M * r) * 4u);
-    const int m = myq / (r / 4), jq = myq % (r / 4);
+  const int hw = tid >> 5, hl = tid & 31;
+  f32x4 tq[kDecTQuads];
+  {
+    // (one load sequence for both cases: a branch here would make the
+    // compiler wait for the loads of one side before those of the other)
+    const BufRes rt = make_bufres(T, static_cast<uint32_t>((nz > 0 ? nz : 1) * M * r) * 4u);
+    const int j = 32 * kw + 8 * g;
+    const bool lora_lane = kw < nsteps && li < M && j < r;
 #pragma unroll
-    for (int i = 0; i < kDecTSumLoads; ++i) {
-      const int z = sub + tpq * i;
-      const bool ok = myq < nq && z < nz;
-      tp += __builtin_bit_cast(
-          f32x4, buf_load16(rt, ok ? static_cast<uint32_t>(((z * M + m) * r + 4 * jq) * 4)
-                                   : kDecOffNone));
+    for (int i = 0; i < kDecTQuads; ++i) {
+      const int q = hw + (kDecThreads / 32) * i;
+      const bool ok = nz > 0 ? (q < nq && hl < nz) : lora_lane;
+      const int idx = nz > 0 ? hl * M * r + 4 * q : li * r + j + 4 * i;
+      tq[i] = __builtin_bit_cast(
+          f32x4, buf_load16(rt, ok ? static_cast<uint32_t>(idx * 4) : kDecOffNone));
     }
+  }
+  // The workgroup's 32 columns of B [r][N] (one 16-byte piece per thread for
+  // r <= 256), staged in LDS for the LoRA update after the main loop.
+  u32x4 bpiece;
+  {
+    const BufRes rbl = make_bufres(Bl, static_cast<uint32_t>(r) * static_cast<uint32_t>(N) * 2u);
+    const int j = tid >> 2, c = tid & 3;
+    const bool ok = j < r && n0 + 8 * c < N;
+    bpiece = buf_load16(rbl, ok ? static_cast<uint32_t>((j * N + n0 + 8 * c) * 2) : kDecOffNone);
   }
 
   // The code ring: every call issues the same loads, so the compiler can
@@ -167,52 +191,33 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 #pragma unroll
   for (int u = 0; u < D; ++u) load(u, u);
 
-  // LoRA update: step q of this wave's fragment (wave kw takes step kw)
-  // contributes P[n, j] = B[j, n] times Q[m, j] = s*T[m, j] split into bf16
-  // hi and lo; its B operand is loaded now so the tail waits on no fresh load.
-  const int nsteps = (r + 31) / 32;
-  const int64_t nrow = n0 + 16 * p + li;
-  uint32_t lb[4] = {0, 0, 0, 0};
-  if (kw < nsteps) {
-    const int j = 32 * kw + 8 * g;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = 0, hi = 0;
-      if (nrow < N && j < r) {
-        lo = Bl[(int64_t)(j + 2 * i) * N + nrow];
-        hi = Bl[(int64_t)(j + 2 * i + 1) * N + nrow];
-      }
-      lb[i] = lo | (hi << 16);
-    }
-  }
-
-  // Stage into LDS: level table, X, the T partial sums.
-  build_rep_pair_table(tab, tb, tid);
+  // Stage into LDS: level table, X, block constants and group scales.
+  build_rep_pair_table<kDecThreads>(tab, lv, tid);
   if constexpr (XLDS) {
 #pragma unroll
-    for (int i = 0; i < kDecXPieces; ++i) {
+    for (int i = 0; i < XP; ++i) {
       const int idx = tid + i * kDecThreads;
       if (16 * idx < xrange) *reinterpret_cast<u32x4*>(xs + 8 * idx) = xw[i];
     }
     if (tid < 8) *reinterpret_cast<u32x4*>(xs + M * K32 + 8 * tid) = u32x4{0, 0, 0, 0};
   }
-  red[tid] = tp;
   // Block constants, transposed so that a fragment's 16 rows read 16
   // consecutive bytes; column KB is zero for the half chunk past K.
 #pragma unroll
   for (int i = 0; i < kDecEPieces; ++i) {
     const int idx = tid + i * kDecThreads;
-    if (4 * idx < erange) {
+    if (8 * idx < erange) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int f = 4 * idx + b;   // row-major index: row f / KB, column f % KB
+      for (int b = 0; b < 8; ++b) {
+        const int f = 8 * idx + b;   // row-major index: row f / KB, column f % KB
         const int row = static_cast<int>((static_cast<float>(f) + 0.5f) * inv_kb);
-        et[(f - row * KB) * ROWS + row] = static_cast<uint8_t>(ev[i] >> (8 * b));
+        et[(f - row * KB) * ROWS + row] = static_cast<uint8_t>(ev[2 * i + b / 4] >> (8 * (b % 4)));
       }
     }
   }
   if (tid < ROWS) et[KB * ROWS + tid] = 0;
   if (tid < dmax) dsc[tid] = dv;
+  if ((tid >> 2) < r) reinterpret_cast<u32x4*>(bst)[tid] = bpiece;
 
   // Lanes past M read X from the zero slot with stride 0; past K (the second
   // half of a chunk when K % 128 == 64) they meet the zero block constant,
@@ -272,39 +277,62 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     }
   }
 
-  // T's partial sums are added after the main loop, off its critical path.
-  __syncthreads();
-  if (nz > 0 && tid < nq) {   // fixed order: deterministic
-    f32x4 t = red[tid * tpq];
-    for (int u = 1; u < tpq; ++u) t += red[tid * tpq + u];
-    tfin[tid] = t;
-    if (blockIdx.x == 0) *reinterpret_cast<f32x4*>(Tout + 4 * tid) = t;   // [M][r]
+  // The LoRA step's B operand, B[j .. j+7, n] for the lane's row n, read
+  // before the barrier below (after it the same LDS holds the exchange).
+  u32x4 bw = {0, 0, 0, 0};
+  if (kw < nsteps) {
+    const int j = 32 * kw + 8 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = j + 2 * i < r ? bst[(j + 2 * i) * ROWS + 16 * p + li] : 0u;
+      const uint32_t hi = j + 2 * i + 1 < r ? bst[(j + 2 * i + 1) * ROWS + 16 * p + li] : 0u;
+      bw[i] = lo | (hi << 16);
+    }
+  }
+
+  // T's partial sums are added after the main loop, off its critical path:
+  // a butterfly over each half-wave, in a fixed order (deterministic).
+  if (nz > 0) {
+#pragma unroll
+    for (int i = 0; i < kDecTQuads; ++i) {
+      f32x4 v = tq[i];
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) {
+        v.x += __shfl_xor(v.x, o, 32);
+        v.y += __shfl_xor(v.y, o, 32);
+        v.z += __shfl_xor(v.z, o, 32);
+        v.w += __shfl_xor(v.w, o, 32);
+      }
+      const int q = hw + (kDecThreads / 32) * i;
+      if (hl == 0 && q < nq) {
+        tfin[q] = v;
+        if (blockIdx.x == 0) *reinterpret_cast<f32x4*>(Tout + 4 * q) = v;   // [M][r]
+      }
+    }
   }
   __syncthreads();
 
+  // LoRA update: step kw of the fragment (rank block 32 kw .. 32 kw + 31)
+  // adds P[n, j] = B[j, n] times Q[m, j] = s T[m, j], with Q split into bf16
+  // hi and lo halves.
   if (kw < nsteps) {
     const int j = 32 * kw + 8 * g;
-    f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = t0;
-    if (li < M && j < r) {
-      if (nz > 0) {
-        t0 = tfin[(li * r + j) / 4];
-        t1 = tfin[(li * r + j) / 4 + 1];
-      } else {
-        t0 = *reinterpret_cast<const f32x4*>(T + (int64_t)li * r + j);
-        t1 = *reinterpret_cast<const f32x4*>(T + (int64_t)li * r + j + 4);
-      }
+    f32x4 t0 = tq[0], t1 = tq[1];
+    if (nz > 0) {
+      const bool ok = li < M && j < r;
+      t0 = ok ? tfin[(li * r + j) / 4] : f32x4{0.f, 0.f, 0.f, 0.f};
+      t1 = ok ? tfin[(li * r + j) / 4 + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float v[8] = {t0.x * s, t0.y * s, t0.z * s, t0.w * s,
                         t1.x * s, t1.y * s, t1.z * s, t1.w * s};
     uint32_t h[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) split_bf16x2(v[2 * i], v[2 * i + 1], h[i], l[i]);
-    const u32x4 bw = {lb[0], lb[1], lb[2], lb[3]};
     acc = mfma16(bw, u32x4{h[0], h[1], h[2], h[3]}, acc);
     acc = mfma16(bw, u32x4{l[0], l[1], l[2], l[3]}, acc);
   }
 
-  red[wave * 64 + lane] = acc;   // the T partial sums in red were read before the barrier above
+  red[wave * 64 + lane] = acc;
   __syncthreads();
   if (kw == 0) {
     f32x4 t = red[(p * kDecKSlots) * 64 + lane];
@@ -320,20 +348,20 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 
 namespace {
 
-template <int D, bool XLDS>
+template <int D, int XP>
 hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w, const float* T,
                                  int nz, float* Tout, const uint16_t* B, int r, float s,
                                  uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
   // allow the largest dynamic LDS this variant takes (once per variant)
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_fwd_decode<D, XLDS>),
+      reinterpret_cast<const void*>(&k_fwd_decode<D, XP>),
       hipFuncAttributeMaxDynamicSharedMemorySize,
-      XLDS ? kDecLdsMax : DecLds(1, kDecMaxK, false).total);
+      XP > 0 ? kDecLdsMax : DecLds(1, kDecMaxK, false).total);
   if (attr != hipSuccess) return attr;
-  const DecLds L(M, w.K, XLDS);
+  const DecLds L(M, w.K, XP > 0);
   const unsigned grid = static_cast<unsigned>((w.N + kDecRows - 1) / kDecRows);
   const float inv_kb = 1.0f / static_cast<float>(w.K / kBlock);
-  hipLaunchKernelGGL((k_fwd_decode<D, XLDS>), dim3(grid), dim3(kDecThreads), L.total, stream,
+  hipLaunchKernelGGL((k_fwd_decode<D, XP>), dim3(grid), dim3(kDecThreads), L.total, stream,
                      X, (int)M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, nz, Tout, B,
                      r, s, Y, tb, L.eoff, L.doff, L.xoff, L.dmax, inv_kb);
   return hipGetLastError();
@@ -355,11 +383,20 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
   // deeper rings (measured up to 8) only delay the first products.
   hipError_t e;
   // X goes to LDS when it fits next to the rest (M = 1 always; M = 4 up to
-  // K = 8192); otherwise each wave reads its X fragments from global memory.
-  if (M * w.K * 2 <= kDecXLdsBytes && DecLds(M, w.K, true).total <= kDecLdsMax)
-    e = launch_decode_variant<2, true>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
-  else
-    e = launch_decode_variant<2, false>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+  // K = 8192), in as few 16-byte pieces per thread as it needs; otherwise each
+  // wave reads its X fragments from global memory.
+  const int64_t xbytes = M * w.K * 2;
+  if (xbytes <= kDecXLdsBytes && DecLds(M, w.K, true).total <= kDecLdsMax) {
+    const int64_t per_piece = 16 * kDecThreads;
+    if (xbytes <= per_piece)
+      e = launch_decode_variant<2, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+    else if (xbytes <= 2 * per_piece)
+      e = launch_decode_variant<2, 2>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+    else
+      e = launch_decode_variant<2, kDecXPieces>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+  } else {
+    e = launch_decode_variant<2, 0>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+  }
   prof_end(2, stream);
   return e;
 }

@@ -109,18 +109,41 @@ __device__ __forceinline__ void dequant8_f32(uint32_t w, float c_hat,
 // (byte << 8) | ((lane % 32) << 3) with no base to add.
 constexpr int kRepTabBytes = 256 * 256;
 
-__device__ __forceinline__ void build_rep_pair_table(char* tab, const Nf4Tables& tb, int tid) {
-  if (tid < 256) {
-    float lo = 0.f, hi = 0.f;
+// The 16 levels, read from the kernel arguments into scalar registers at
+// kernel entry.  The empty asm consumes them there, so their scalar loads go
+// out with the first batch of argument loads; otherwise the compiler issues
+// them just before the table is built, behind the kernel's first weight
+// loads, and the table build then waits for those to drain.
+struct Levels {
+  float v[16];
+};
+__device__ __forceinline__ Levels load_levels(const Nf4Tables& tb) {
+  Levels l;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      lo = ((tid & 15) == j) ? tb.q[j] : lo;
-      hi = ((tid >> 4) == j) ? tb.q[j] : hi;
-    }
+  for (int j = 0; j < 16; ++j) l.v[j] = tb.q[j];
+  asm volatile("" ::"s"(l.v[0]), "s"(l.v[1]), "s"(l.v[2]), "s"(l.v[3]), "s"(l.v[4]),
+               "s"(l.v[5]), "s"(l.v[6]), "s"(l.v[7]), "s"(l.v[8]), "s"(l.v[9]), "s"(l.v[10]),
+               "s"(l.v[11]), "s"(l.v[12]), "s"(l.v[13]), "s"(l.v[14]), "s"(l.v[15]));
+  return l;
+}
+
+// Every thread of an NT-thread workgroup writes entry (tid % 256) into
+// 32 * 256 / NT of its copies; the copy order is rotated by the entry, so
+// the 32 lanes of a half-wave write distinct bank pairs.
+template <int NT>
+__device__ __forceinline__ void build_rep_pair_table(char* tab, const Levels& lv, int tid) {
+  static_assert(NT % 256 == 0 && NT <= 8192, "whole copies per thread");
+  constexpr int kCopies = 32 * 256 / NT;
+  const int e = tid & 255, c0 = (tid >> 8) * kCopies;
+  float lo = 0.f, hi = 0.f;
 #pragma unroll
-    for (int c = 0; c < 32; ++c)   // lanes start at different copies: no bank conflict
-      reinterpret_cast<float2*>(tab)[32 * tid + ((c + tid) & 31)] = make_float2(lo, hi);
+  for (int j = 0; j < 16; ++j) {
+    lo = ((e & 15) == j) ? lv.v[j] : lo;
+    hi = ((e >> 4) == j) ? lv.v[j] : hi;
   }
+#pragma unroll
+  for (int c = 0; c < kCopies; ++c)
+    reinterpret_cast<float2*>(tab)[32 * e + ((c0 + c + e) & 31)] = make_float2(lo, hi);
 }
 
 typedef __attribute__((address_space(3))) const f32x2 LdsF32x2;

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
   const int wave = wave_id(), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int wt = wave % XWT, ks = wave / XWT;
-  build_rep_pair_table(tab, tb, tid);
+  build_rep_pair_table<XT>(tab, load_levels(tb), tid);
 
   const int tile = xcd_remap_dx(blockIdx.x, ptiles * qtiles);
   const int qt = tile / ptiles, pt = tile - qt * ptiles;

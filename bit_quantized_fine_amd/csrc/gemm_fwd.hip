@@ -73,7 +73,7 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   const int wave = wave_id(), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int wt = wave % GWT, ks = wave / GWT;
-  build_rep_pair_table(tab, tb, tid);
+  build_rep_pair_table<GT>(tab, load_levels(tb), tid);
 
   const int tile = xcd_remap(blockIdx.x, ptiles * qtiles);
   const int qt = tile / ptiles, pt = tile - qt * ptiles;
