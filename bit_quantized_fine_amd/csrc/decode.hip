@@ -3,23 +3,35 @@
 // Y = X . deq(W)^T + s . T . B with T = X . A computed beforehand.  At small
 // M the layer is a stream over the NF4 weight (0.516 bytes per weight), so
 // the kernel is organised around the code stream: every lane issues 16-byte
-// loads of 32 consecutive codes, dequantizes them in registers (Mathematical
-// Formulation of "DL0087 QLoRA": the bf16 tile is rebuilt just before the
-// matmul and discarded) and feeds them straight to v_mfma_f32_16x16x32_bf16
-// with the token dimension padded to 16.
+// loads of 32 consecutive codes, turns them into bf16 levels in registers
+// and feeds them straight to v_mfma_f32_16x16x32_bf16 with the token
+// dimension padded to 16.
+//
+// The weight of a code is c_b . q (Mathematical Formulation of "DL0087
+// QLoRA": the block constant dequantized from the 8-bit constant and its
+// group scale, times the NF4 level).  Since c_b is shared by the 64 weights
+// of a block, this kernel multiplies the levels by X first and the block's
+// partial sum by c_b after: every MFMA covers the codes of one block only,
+// and four FMAs per block apply its scale to the lane's four outputs.  The
+// per-weight work is then one table lookup, with no multiply and no
+// conversion (the levels are rounded to bf16 once, in the table).
 //
 // Workgroup = 16 waves on two fragments of 16 weight rows; eight waves share
 // a fragment and split its reduction dimension in chunks of 128 k (wave kw
-// takes chunks kw, kw+8, ...).  Lane l works on row (l % 16) and on the 32 k
-// starting at 32 (l / 16) inside each chunk.  The code loads are the only
-// vector-memory traffic of the main loop; they run D chunks ahead in a
-// register ring.  The 8-bit block constants and fp32 group scales of the
-// workgroup's rows, and X itself when it is small, are staged in LDS once.
-// The byte-pair level table sits in LDS as 32 copies interleaved at 8-byte
-// steps in 256-byte rows, so lane l reads copy (l % 32) and a lookup never
-// meets a bank conflict; its address is one byte permute.  The waves'
-// partial sums meet in LDS; the LoRA update is added as extra MFMA steps
-// over the rank before that reduction.
+// takes chunks kw, kw+8, ...).  A chunk is two blocks.  Lane l loads the 16
+// bytes at 16 (l / 16) of row (l % 16)'s 64-byte chunk segment: lanes 0-31
+// hold the first block, lanes 32-63 the second.  One cross-half swap of two
+// of the four dwords (v_permlane32_swap) leaves every lane with two dwords of
+// each block; MFMA s of a block takes dword s of each lane, and X is read at
+// the matching k.  The code loads are the only vector-memory traffic of the
+// main loop; they run D chunks ahead in a register ring.
+//
+// Staged in LDS once: the bf16 level-pair table (64 copies, one per lane, so
+// lookups never meet a bank conflict), the block scales c_b of the
+// workgroup's rows as fp32 [K/64 + 1][32] (the extra column is zero), the
+// workgroup's columns of B, and X itself when it fits.  The waves' partial
+// sums meet in LDS; the LoRA update is added as extra MFMA steps over the
+// rank before that reduction.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -35,10 +47,12 @@ constexpr int kDecRows = 16 * kDecR;
 // A buffer offset past the end of every buffer the kernel reads (weights are
 // limited to N*K <= 2^32, so their code buffers hold at most 2^31 bytes).
 constexpr uint32_t kDecOffNone = 0x80000000u;
-constexpr int kDecMaxK = 32768;                // block constants of the rows fit in LDS
+constexpr int kDecMaxK = 32768;                // block scales of the rows fit in LDS
+constexpr int kDecMaxR = 256;
 constexpr int kDecXLdsBytes = 64 * 1024;       // X staged in LDS up to this size
 constexpr int kDecLdsMax = 160 * 1024;         // LDS of one workgroup
 constexpr int kDecXPieces = kDecXLdsBytes / 16 / kDecThreads;   // at most 4 16-byte X pieces a thread
+constexpr int kDecXZero = 256;                 // zero bytes after X (lanes past M read there)
 // T partial sums (at most kMaxDownPartials of them) are added up by
 // half-waves: half-wave h takes quads (4 ranks of one token) h and h + 32,
 // its lane z partial z.  M r <= kDecTSumMaxMR keeps that within two quads
@@ -46,24 +60,25 @@ constexpr int kDecXPieces = kDecXLdsBytes / 16 / kDecThreads;   // at most 4 16-
 constexpr int kDecTQuads = 2;
 constexpr int kDecTSumMaxMR = 4 * (kDecThreads / 32) * kDecTQuads;
 static_assert(kMaxDownPartials <= 32, "one partial per lane of a half-wave");
-constexpr int kDecEPieces = (kDecRows * kDecMaxK / kBlock / 8 + kDecThreads - 1) / kDecThreads;   // 8-byte pieces
+// Block constants of the workgroup's rows, read as 8-byte pieces.
+constexpr int kDecEPieces = (kDecRows * kDecMaxK / kBlock / 8 + kDecThreads - 1) / kDecThreads;
 
 int round16(int64_t v) { return static_cast<int>((v + 15) / 16 * 16); }
 
-// Dynamic LDS of one workgroup, in order: the level table, the waves'
-// partial sums (first the partial sums of T), the summed T, the block
-// constants transposed to [K/64 + 1][32] bytes (the extra column is zero),
-// the group scales [dmax] of the workgroup's blocks, and (XLDS) X [M][K]
-// followed by 128 zero bytes.
+// Dynamic LDS of one workgroup, in order: the level table, B's columns
+// [r][32], the summed T, the block scales [K/64 + 1][32] fp32, and (XLDS) X
+// [M][K] followed by kDecXZero zero bytes.  After the main loop the waves'
+// partial sums [kDecThreads] f32x4 reuse the bytes from the block scales on.
 struct DecLds {
-  int eoff, doff, xoff, dmax, total;
-  DecLds(int64_t M, int64_t K, bool xlds) {
+  int boff, toff, coff, xoff, total;
+  DecLds(int64_t M, int64_t K, int r, bool xlds) {
     const int64_t kb = K / kBlock;
-    eoff = kRepTabBytes + kDecThreads * 16 + kDecTSumMaxMR * 4;
-    doff = eoff + round16(kDecRows * (kb + 1));
-    dmax = static_cast<int>(kDecRows * kb / kGroup + 2);
-    xoff = doff + round16(4 * dmax);
-    total = xoff + (xlds ? round16(M * K * 2) + 128 : 0);
+    boff = kRepTabBytes;
+    toff = boff + round16(int64_t(64) * r);
+    coff = toff + kDecTSumMaxMR * 4;
+    xoff = coff + round16(kDecRows * (kb + 1) * 4);
+    const int end = xoff + (xlds ? round16(M * K * 2) + kDecXZero : 0);
+    total = end > coff + kDecThreads * 16 ? end : coff + kDecThreads * 16;
   }
 };
 
@@ -75,16 +90,15 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
     int64_t N, int64_t K, const float* __restrict__ T, int nz, float* __restrict__ Tout,
     const uint16_t* __restrict__ Bl, int r, float s, uint16_t* __restrict__ Y,
-    Nf4Tables tb, int eoff, int doff, int xoff, int dmax, float inv_kb) {
+    Nf4Tables tb, int boff, int toff, int coff, int xoff, float inv_kb) {
   constexpr int ROWS = kDecRows;
   constexpr bool XLDS = XP > 0;   // X staged in LDS, XP 16-byte pieces per thread
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
-  char* tab = reinterpret_cast<char*>(dyn);                          // level pairs
-  f32x4* red = reinterpret_cast<f32x4*>(dyn + kRepTabBytes);            // [kDecThreads]
-  f32x4* tfin = red + kDecThreads;                                   // [kDecTSumMaxMR / 4]
-  uint16_t* bst = reinterpret_cast<uint16_t*>(red);                  // B columns [r][ROWS] until the exchange
-  uint8_t* et = dyn + eoff;                                          // [KB + 1][ROWS]
-  float* dsc = reinterpret_cast<float*>(dyn + doff);                 // [dmax]
+  char* tab = reinterpret_cast<char*>(dyn);                          // bf16 level pairs
+  uint16_t* bst = reinterpret_cast<uint16_t*>(dyn + boff);           // B columns [r][ROWS]
+  f32x4* tfin = reinterpret_cast<f32x4*>(dyn + toff);                // [kDecTSumMaxMR / 4]
+  float* csc = reinterpret_cast<float*>(dyn + coff);                 // [KB + 1][ROWS]
+  f32x4* red = reinterpret_cast<f32x4*>(dyn + coff);                 // after the main loop
   uint16_t* xs = reinterpret_cast<uint16_t*>(dyn + xoff);            // [M][K], zeros
   const Levels lv = load_levels(tb);
   const int tid = threadIdx.x;
@@ -98,9 +112,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   const int nmine = nchunks > kw ? (nchunks - kw + kDecKSlots - 1) / kDecKSlots : 0;
 
   // Buffer descriptors: rows n >= N fall outside the code / constant buffers
-  // and read as zero, and so do token rows li >= M of X.  The second half of
-  // a chunk past K (K % 128 == 64) gets a zero block constant instead, so the
-  // code bytes it reads from the next row contribute nothing.
+  // and read as zero, and so do token rows li >= M of X.  The second block of
+  // a chunk past K (K % 128 == 64) gets a zero scale instead, so the code
+  // bytes it reads from the next row contribute nothing.
   const uint32_t nb = static_cast<uint32_t>(N * K / kBlock);
   const BufRes rc = make_bufres(codes, static_cast<uint32_t>(N * K / 2));
   const BufRes re = make_bufres(absmax_q, nb);
@@ -109,23 +123,23 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 
   // Staging loads first, a fixed number per thread, so that waiting for them
   // does not wait for the code stream issued after them: the block constants
-  // of the workgroup's rows (one contiguous byte range, read as dwords), their
-  // group scales, X, and for the LoRA update (used only after the main loop)
-  // the partial sums of T and this lane's column of B.
+  // of the workgroup's rows (one contiguous byte range, in 8-byte pieces) and
+  // the group scale of each piece (a piece never straddles two groups: both
+  // the range start and the group size are multiples of 8), X, and for the
+  // LoRA update (used only after the main loop) the partial sums of T and
+  // the workgroup's columns of B.
   const uint32_t e0 = static_cast<uint32_t>(n0) * KB;   // first block of the workgroup
-  const uint32_t g0 = e0 / kGroup;
-  const int erange = ROWS * KB;                         // bytes, a multiple of 4
-  uint32_t ev[2 * kDecEPieces];
+  const int erange = ROWS * KB;                         // bytes, a multiple of 8
+  u32x2 ev[kDecEPieces];
+  float dv[kDecEPieces];
 #pragma unroll
   for (int i = 0; i < kDecEPieces; ++i) {
     const int idx = tid + i * kDecThreads;
-    const u32x2 v = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_raw_buffer_load_b64(re, 8 * idx < erange ? e0 + 8u * idx
-                                                                        : kDecOffNone, 0, 0));
-    ev[2 * i] = v.x;
-    ev[2 * i + 1] = v.y;
+    const bool ok = 8 * idx < erange;
+    ev[i] = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(re, ok ? e0 + 8u * idx : kDecOffNone, 0, 0));
+    dv[i] = buf_load_f32(rd, ok ? ((e0 + 8u * idx) / kGroup) * 4u : kDecOffNone);
   }
-  const float dv = buf_load_f32(rd, tid < dmax ? (g0 + tid) * 4u : kDecOffNone);
   // X: XP pieces per thread, as many as M K 2 bytes need (a load whose lanes
   // all fall outside the range still occupies the address unit, and at kernel
   // start the staging loads of 16 waves queue there ahead of the code stream)
@@ -174,9 +188,14 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // The code ring: every call issues the same loads, so the compiler can
   // count them and wait for exactly one chunk at a time; chunks past the
   // wave's last one get an offset beyond every buffer and read zeros without
-  // memory traffic.
+  // memory traffic.  Without X in LDS, each lane also loads the X pieces its
+  // four MFMAs take.
   const uint32_t cb = static_cast<uint32_t>((n0 + 16 * p + li) * (K / 2)) + 64u * kw + 16u * g;
-  const uint32_t xb = (static_cast<uint32_t>(li) * K32 + 128u * kw + 32u * g) * 2u;
+  // k offset (inside a block) of the 8 codes that lane group g supplies to
+  // step 0 of a block after the swap (dword 4 (g % 2) + 2 (g / 2); step 1
+  // takes the next dword).
+  const int xo0 = 8 * (4 * (g & 1) + 2 * (g >> 1));
+  const uint32_t xb = (static_cast<uint32_t>(li) * K32 + 128u * kw + xo0) * 2u;
   u32x4 cw[D];
   u32x4 xv[XLDS ? 1 : D][4];
   auto load = [&](int t, int st) {
@@ -184,25 +203,27 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     cw[st] = buf_load16(rc, live ? cb + 64u * kDecKSlots * t : kDecOffNone);
     if constexpr (!XLDS) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xv[st][i] = buf_load16(rx, live ? xb + 256u * kDecKSlots * t + 16u * i : kDecOffNone);
+      for (int i = 0; i < 4; ++i)   // block i / 2, step i % 2
+        xv[st][i] = buf_load16(
+            rx, live ? xb + 256u * kDecKSlots * t + 128u * (i >> 1) + 16u * (i & 1) : kDecOffNone);
     }
   };
 #pragma unroll
   for (int u = 0; u < D; ++u) load(u, u);
 
-  // Stage into LDS: level table, X, block constants and group scales.
-  build_rep_pair_table<kDecThreads>(tab, lv, tid);
+  // Stage into LDS: level table, X, block scales, B.
+  build_rep_bf16_pair_table<kDecThreads>(tab, lv, tid);
   if constexpr (XLDS) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int idx = tid + i * kDecThreads;
       if (16 * idx < xrange) *reinterpret_cast<u32x4*>(xs + 8 * idx) = xw[i];
     }
-    if (tid < 8) *reinterpret_cast<u32x4*>(xs + M * K32 + 8 * tid) = u32x4{0, 0, 0, 0};
+    if (tid < kDecXZero / 16)
+      *reinterpret_cast<u32x4*>(xs + M * K32 + 8 * tid) = u32x4{0, 0, 0, 0};
   }
-  // Block constants, transposed so that a fragment's 16 rows read 16
-  // consecutive bytes; column KB is zero for the half chunk past K.
+  // Block scales c = e . d, transposed so that the four rows of a lane's
+  // outputs read 16 consecutive bytes; column KB is zero.
 #pragma unroll
   for (int i = 0; i < kDecEPieces; ++i) {
     const int idx = tid + i * kDecThreads;
@@ -211,61 +232,64 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
       for (int b = 0; b < 8; ++b) {
         const int f = 8 * idx + b;   // row-major index: row f / KB, column f % KB
         const int row = static_cast<int>((static_cast<float>(f) + 0.5f) * inv_kb);
-        et[(f - row * KB) * ROWS + row] = static_cast<uint8_t>(ev[2 * i + b / 4] >> (8 * (b % 4)));
+        const uint32_t w = b < 4 ? ev[i].x : ev[i].y;
+        const float e = static_cast<float>((w >> (8 * (b % 4))) & 0xFFu);
+        csc[(f - row * KB) * ROWS + row] = e * dv[i];
       }
     }
   }
-  if (tid < ROWS) et[KB * ROWS + tid] = 0;
-  if (tid < dmax) dsc[tid] = dv;
+  if (tid < ROWS) csc[KB * ROWS + tid] = 0.f;
   if ((tid >> 2) < r) reinterpret_cast<u32x4*>(bst)[tid] = bpiece;
 
-  // Lanes past M read X from the zero slot with stride 0; past K (the second
-  // half of a chunk when K % 128 == 64) they meet the zero block constant,
-  // and their X reads stay inside the next token row or the zero slot.
-  const uint16_t* xlane = li < M ? xs + li * K32 + 32 * g : xs + M * K32;
+  // Lanes past M read X from the zero bytes with stride 0; past K (the second
+  // block of a chunk when K % 128 == 64) they meet a zero scale, and their X
+  // reads stay inside the next token row or the zero bytes.
+  const uint16_t* xlane = li < M ? xs + li * K32 + xo0 : xs + M * K32 + xo0;
   const int xstep = li < M ? 128 : 0;
-  const int row = 16 * p + li;
-  // Table addresses: copy (lane % 32) in byte 0, entry in byte 1.  The
+  const float* clane = csc + 16 * p + 4 * g;   // scales of the lane's output rows
+  // Table addresses: the lane's copy offset in byte 0, entry in byte 1.  The
   // kernel declares no static LDS, so the dynamic block, and the table at its
   // start, begins at LDS address 0 and the address needs no base added.
-  uint32_t ta[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) ta[b] = rep_lane_base(lane);
+  const uint32_t ta = static_cast<uint32_t>(lane) << 2;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  // All LDS reads of a chunk (constant, table lookups, X) are issued before
-  // any of their products, so one LDS round trip serves the chunk's MFMAs.
+  // All LDS reads of a chunk (scales, table lookups, X) are issued before any
+  // of their products, so one LDS round trip serves the chunk's MFMAs.
   auto compute = [&](int t, int st) {
     const int c = kw + kDecKSlots * t;
-    const int j = 2 * c + (g >> 1);   // block of the lane inside its row (KB: zero)
-    const float e = static_cast<float>(et[j * ROWS + row]);
-    const float d = dsc[(e0 + static_cast<uint32_t>(row * KB + j)) / kGroup - g0];
-    f32x2 lk[4][4];
+    // Regroup: dwords 0, 1 of lanes 0-31 and 2, 3 of lanes 32-63 stay; the
+    // others trade places across the two halves.  After it, dwords 0, 1 hold
+    // codes of the first block and 2, 3 of the second, in every lane.
+    uint32_t d[4] = {cw[st].x, cw[st].y, cw[st].z, cw[st].w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w = cw[st][i];
-      lk[i][0] = rep_lookup<0>(ta[0], w);
-      lk[i][1] = rep_lookup<1>(ta[1], w);
-      lk[i][2] = rep_lookup<2>(ta[2], w);
-      lk[i][3] = rep_lookup<3>(ta[3], w);
+    for (int u = 0; u < 2; ++u) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(d[u], d[2 + u], false, false);
+      d[u] = sw[0];
+      d[2 + u] = sw[1];
     }
-    u32x4 xf[4];
+    const f32x4 cA = *reinterpret_cast<const f32x4*>(clane + (2 * c) * ROWS);
+    const f32x4 cB = *reinterpret_cast<const f32x4*>(clane + (2 * c + 1) * ROWS);
+    u32x4 a[4], xf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      a[i][0] = rep_bf16_lookup<0>(ta, d[i]);
+      a[i][1] = rep_bf16_lookup<1>(ta, d[i]);
+      a[i][2] = rep_bf16_lookup<2>(ta, d[i]);
+      a[i][3] = rep_bf16_lookup<3>(ta, d[i]);
       if constexpr (XLDS)
-        xf[i] = *reinterpret_cast<const u32x4*>(xlane + c * xstep + 8 * i);
+        xf[i] = *reinterpret_cast<const u32x4*>(xlane + c * xstep + 64 * (i >> 1) + 8 * (i & 1));
       else
         xf[i] = xv[st][i];
     }
     __builtin_amdgcn_sched_barrier(0);
-    const float chat = e * d;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 pA = mfma16(a[0], xf[0], zero);
+    pA = mfma16(a[1], xf[1], pA);
+    f32x4 pB = mfma16(a[2], xf[2], zero);
+    pB = mfma16(a[3], xf[3], pB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 a;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) a[b] = pack_bf16x2(lk[i][b].x * chat, lk[i][b].y * chat);
-      acc = mfma16(a, xf[i], acc);
-    }
+    for (int j = 0; j < 4; ++j)
+      acc[j] = __builtin_fmaf(cB[j], pB[j], __builtin_fmaf(cA[j], pA[j], acc[j]));
   };
   __syncthreads();
   for (int t0 = 0; t0 < nmine; t0 += D) {
@@ -277,8 +301,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     }
   }
 
-  // The LoRA step's B operand, B[j .. j+7, n] for the lane's row n, read
-  // before the barrier below (after it the same LDS holds the exchange).
+  // The LoRA step's B operand, B[j .. j+7, n] for the lane's row n.
   u32x4 bw = {0, 0, 0, 0};
   if (kw < nsteps) {
     const int j = 32 * kw + 8 * g;
@@ -332,7 +355,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     acc = mfma16(bw, u32x4{l[0], l[1], l[2], l[3]}, acc);
   }
 
-  red[wave * 64 + lane] = acc;
+  red[wave * 64 + lane] = acc;   // the block scales and X are no longer read
   __syncthreads();
   if (kw == 0) {
     f32x4 t = red[(p * kDecKSlots) * 64 + lane];
@@ -352,18 +375,18 @@ template <int D, int XP>
 hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w, const float* T,
                                  int nz, float* Tout, const uint16_t* B, int r, float s,
                                  uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
-  // allow the largest dynamic LDS this variant takes (once per variant)
+  // allow the largest dynamic LDS (once per variant)
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_fwd_decode<D, XP>),
-      hipFuncAttributeMaxDynamicSharedMemorySize,
-      XP > 0 ? kDecLdsMax : DecLds(1, kDecMaxK, false).total);
+      hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
   if (attr != hipSuccess) return attr;
-  const DecLds L(M, w.K, XP > 0);
+  const DecLds L(M, w.K, r, XP > 0);
+  if (L.total > kDecLdsMax) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>((w.N + kDecRows - 1) / kDecRows);
   const float inv_kb = 1.0f / static_cast<float>(w.K / kBlock);
   hipLaunchKernelGGL((k_fwd_decode<D, XP>), dim3(grid), dim3(kDecThreads), L.total, stream,
                      X, (int)M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, nz, Tout, B,
-                     r, s, Y, tb, L.eoff, L.doff, L.xoff, L.dmax, inv_kb);
+                     r, s, Y, tb, L.boff, L.toff, L.coff, L.xoff, inv_kb);
   return hipGetLastError();
 }
 
@@ -382,11 +405,11 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
   // Two chunks in flight per wave: with all 16 waves of every CU streaming,
   // deeper rings (measured up to 8) only delay the first products.
   hipError_t e;
-  // X goes to LDS when it fits next to the rest (M = 1 always; M = 4 up to
-  // K = 8192), in as few 16-byte pieces per thread as it needs; otherwise each
-  // wave reads its X fragments from global memory.
+  // X goes to LDS when it fits next to the rest (M = 1 up to K = 22016 with
+  // r <= 64; M = 4 up to K = 8192), in as few 16-byte pieces per thread as it
+  // needs; otherwise each wave reads its X pieces from global memory.
   const int64_t xbytes = M * w.K * 2;
-  if (xbytes <= kDecXLdsBytes && DecLds(M, w.K, true).total <= kDecLdsMax) {
+  if (xbytes <= kDecXLdsBytes && DecLds(M, w.K, r, true).total <= kDecLdsMax) {
     const int64_t per_piece = 16 * kDecThreads;
     if (xbytes <= per_piece)
       e = launch_decode_variant<2, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
@@ -400,5 +423,9 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
   prof_end(2, stream);
   return e;
 }
+
+static_assert(kRepTabBytes + 64 * kDecMaxR + kDecTSumMaxMR * 4 +
+                      kDecRows * (kDecMaxK / kBlock + 1) * 4 <= kDecLdsMax,
+              "block scales of the largest K fit next to the table without X");
 
 }  // namespace qnf4

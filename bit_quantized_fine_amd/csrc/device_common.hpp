@@ -162,6 +162,38 @@ __device__ __forceinline__ uint32_t rep_lane_base(int lane) {
   return static_cast<uint32_t>(lane & 31) << 3;
 }
 
+// The same 256 byte pairs as bf16 level pairs (4 bytes: the level of the low
+// nibble in the low half), 64 copies: copy c of entry b at byte 256 b + 4 c,
+// so lane l reads copy l and the 64 lanes of a wave always hit distinct
+// banks.  64 KB at LDS address 0, like the table above.  It holds the levels
+// themselves, unscaled: a kernel using it applies the block scale to the
+// products instead of to each weight.
+template <int NT>
+__device__ __forceinline__ void build_rep_bf16_pair_table(char* tab, const Levels& lv, int tid) {
+  static_assert(NT % 256 == 0 && NT <= 4096, "whole 16-byte groups of copies per thread");
+  constexpr int kGroups = 16 * 256 / NT;   // 16-byte groups (4 copies) written per thread
+  const int e = tid & 255, j0 = (tid >> 8) * kGroups;
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    lo = ((e & 15) == j) ? lv.v[j] : lo;
+    hi = ((e >> 4) == j) ? lv.v[j] : hi;
+  }
+  const uint32_t v = pack_bf16x2(lo, hi);
+#pragma unroll
+  for (int j = 0; j < kGroups; ++j)   // rotated by the entry: 16 lanes cover all banks
+    reinterpret_cast<u32x4*>(tab)[16 * e + ((j0 + j + e) & 15)] = u32x4{v, v, v, v};
+}
+
+typedef __attribute__((address_space(3))) const uint32_t LdsU32;
+
+// The bf16 level pair of byte B of w; ta holds (lane % 64) * 4 in byte 0.
+template <int B>
+__device__ __forceinline__ uint32_t rep_bf16_lookup(uint32_t ta, uint32_t w) {
+  const uint32_t a = __builtin_amdgcn_perm(w, ta, 0x0C0C0000u | ((4u + B) << 8));
+  return *reinterpret_cast<LdsU32*>(static_cast<uintptr_t>(a));
+}
+
 // Raw buffer access: a descriptor over [p, p + nbytes) in scalar registers
 // and 32-bit byte offsets; reads outside the range return zero.
 typedef __amdgpu_buffer_rsrc_t BufRes;
