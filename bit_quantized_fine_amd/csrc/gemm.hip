@@ -11,6 +11,8 @@
 //            G, T of dA and dB); fp32 sources are split into bf16 hi and lo
 //            passes, so the fp32 factor keeps ~16 bits through the bf16 MFMA
 // The weight-streaming GEMMs (forward and dX) have kernels of their own.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -386,40 +388,56 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
   const int wave = wave_id(), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const bool m_ok = li < M;
+  const int jp = tid & 7, kp = tid >> 3;   // A patch: ranks j0 + 8 jp .., k rows 8 kp ..
+  const int K32 = static_cast<int>(K);     // K <= 2^22 and M K, K r < 2^30 here
+  const BufRes rx = make_bufres(X, static_cast<uint32_t>(M * K32 * 2));
+  const BufRes ra = make_bufres(A, static_cast<uint32_t>(K32 * r * 2));
+  // Slices run as a two-stage pipeline: the loads of slice sub + 1 are in
+  // flight while slice sub is transposed and multiplied.
+  u32x4 xf[2][8];     // token fragments for the 8 k32 steps of a slice
+  u32x4 rows[2][8];   // this thread's 8x8 patch of the slice's A rows
   for (int j0 = 0; j0 < r; j0 += 64) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int sub = 0; sub < spw; ++sub) {
-      const int64_t k0 = ((int64_t)blockIdx.x * spw + sub) * LDS_K;
-      u32x4 xf[8];   // token fragments for the 8 k32 steps of this slice
+    // (buffer loads with out-of-range offsets instead of branches, so the
+    // compiler can wait for one stage while the other is in flight)
+    auto load = [&](int sub, int b) {   // past the workgroup's slices: reads nothing
+      const int k0 = sub < spw ? (blockIdx.x * spw + sub) * LDS_K : K32;
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const int64_t k = k0 + 32 * st + 8 * g;
-        xf[st] = (m_ok && k < K) ? *reinterpret_cast<const u32x4*>(X + (int64_t)li * K + k)
-                                 : u32x4{0, 0, 0, 0};
+        const int k = k0 + 32 * st + 8 * g;
+        xf[b][st] = buf_load16(rx, m_ok && k < K ? static_cast<uint32_t>((li * K32 + k) * 2)
+                                                 : 0x80000000u);
       }
-      {  // patch p: ranks j0 + 8*(p % 8) .. +8, k rows k0 + 8*(p / 8) .. +8
-        const int jp = tid & 7, kp = tid >> 3;
-        u32x4 rows[8], cols[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int64_t k = k0 + kp * 8 + t;
-          const int j = j0 + jp * 8;
-          rows[t] = (k < K && j < r) ? *reinterpret_cast<const u32x4*>(A + k * r + j)
-                                     : u32x4{0, 0, 0, 0};
-        }
-        transpose8x8_b16(rows, cols);
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          *reinterpret_cast<u32x4*>(at + (jp * 8 + t) * LDS_KS + kp * 8) = cols[t];
+      for (int t = 0; t < 8; ++t) {
+        const int k = k0 + kp * 8 + t;
+        const int j = j0 + jp * 8;
+        rows[b][t] = buf_load16(ra, k < K && j < r ? static_cast<uint32_t>((k * r + j) * 2)
+                                                   : 0x80000000u);
       }
+    };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto step = [&](int sub, auto bc) {
+      constexpr int b = decltype(bc)::value;
+      if (sub >= spw) return;   // uniform
+      load(sub + 1, b ^ 1);
+      u32x4 cols[8];
+      transpose8x8_b16(rows[b], cols);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        *reinterpret_cast<u32x4*>(at + (jp * 8 + t) * LDS_KS + kp * 8) = cols[t];
       __syncthreads();
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const u32x4 af =
             *reinterpret_cast<const u32x4*>(at + (16 * wave + li) * LDS_KS + 32 * st + 8 * g);
-        acc = mfma16(af, xf[st], acc);
+        acc = mfma16(af, xf[b][st], acc);
       }
       __syncthreads();
+    };
+    load(0, 0);
+    for (int sub = 0; sub < spw; sub += 2) {
+      step(sub, std::integral_constant<int, 0>{});
+      step(sub + 1, std::integral_constant<int, 1>{});
     }
     const int j = j0 + 16 * wave + 4 * g;
     if (m_ok && j < r)
