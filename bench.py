@@ -57,22 +57,32 @@ def stored_traffic(kernel, src_hash):
     return rec.get("bytes_per_launch")
 
 
+def linear_flops(M, N, K, r):
+    """Algorithmic flops of one linear's forward + backward: 4MKN + 6Mr(K+N)
+    (base products of Y and dX, and the rank-r products T, LoRA-up, G, dA, dB,
+    the LoRA term of dX); dequantization and recomputation are not counted."""
+    return 4 * M * K * N + 6 * M * r * (K + N)
+
+
 def bf16_dev(bits, dev):
     import numpy as np
     import torch
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def run_training(q, torch, steps, warmup, dev):
+def run_training(q, torch, steps, warmup, dev, cfg_idx=1):
+    """One step = fwd + bwd of the config's seven linears.  Config 3 runs the
+    backward as under gradient checkpointing: T is not kept, the backward
+    recomputes it (and dequantizes W again, as every backward does)."""
     import numpy as np
 
     import workloads
-    import oracle
-    cfg = workloads.CONFIGS[1]
+    cfg = workloads.CONFIGS[cfg_idx]
     M, r, s = cfg.M[0], cfg.r, cfg.s
+    recompute = cfg_idx == 3
     layers = []
     t0 = time.time()
-    for lin, inp in workloads.config_inputs(1):
+    for lin, inp in workloads.config_inputs(cfg_idx):
         w = q.qlora_nf4_quantize(torch.from_numpy(inp.W).to(dev))
         L = dict(lin=lin, w=w, X=bf16_dev(inp.X, dev), A=bf16_dev(inp.A, dev),
                  B=bf16_dev(inp.B, dev), dY=bf16_dev(inp.dY, dev))
@@ -87,13 +97,14 @@ def run_training(q, torch, steps, warmup, dev):
                                dtype=torch.uint8, device=dev)
         layers.append(L)
     torch.cuda.synchronize()
-    log(f"setup (draw + upload + quantize 7 linears): {time.time() - t0:.1f}s")
+    log(f"setup (draw + upload + quantize {len(layers)} linears): {time.time() - t0:.1f}s")
 
     def step():
         for L in layers:
             q.qlora_linear_fwd(L["X"], L["w"], L["A"], L["B"], s, Y=L["Y"], T=L["T"],
                                workspace=L["wsf"])
-            q.qlora_linear_bwd(L["dY"], L["X"], L["w"], L["A"], L["B"], s, T=L["T"],
+            q.qlora_linear_bwd(L["dY"], L["X"], L["w"], L["A"], L["B"], s,
+                               T=None if recompute else L["T"],
                                dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["wsb"])
 
     for _ in range(warmup):
@@ -111,11 +122,119 @@ def run_training(q, torch, steps, warmup, dev):
     ms_step = (t1 - t0) * 1e3 / steps
     fam = {FAMILIES[f]: q.qlora_profile_read(f) for f in FAMILIES}
 
-    flops_step = sum(oracle.linear_flops(M, L["lin"].N, L["lin"].K, r) for L in layers)
+    flops_step = sum(linear_flops(M, L["lin"].N, L["lin"].K, r) for L in layers)
     fwd_flops = sum(2 * M * L["lin"].K * L["lin"].N + 2 * M * r * L["lin"].N for L in layers)
     dx_flops = sum(2 * M * L["lin"].K * L["lin"].N + 2 * M * r * L["lin"].K for L in layers)
     return dict(layers=layers, M=M, r=r, s=s, ms_step=ms_step, flops_step=flops_step,
                 fam=fam, fwd_flops=fwd_flops, dx_flops=dx_flops, cfg=cfg)
+
+
+def run_stack(q, torch, dev, steps=2, warmup=1):
+    """The 65B-shaped stack with the whole NF4 base resident: 80 layers x 7
+    linears (hidden 8192, FFN 22016), every weight drawn and quantized on the
+    device, r = 64 adapters on every linear.  A training step runs the
+    linears in a chain, per layer h = o(v(k(q(x)))), a = gate(h) + up(h),
+    x' = down(a), with every linear output scaled by 1/(0.02 sqrt(K)) (a
+    torch op outside the library) to keep values O(1); the backward runs the
+    chain in reverse.  Also one decode token (M = 1, forward only) through
+    the whole chain, so the 33 GB of codes stream from HBM once per token."""
+    import workloads
+    cfg = workloads.CONFIGS[4]
+    M, r, s = cfg.M[0], cfg.r, cfg.s
+    t0 = time.time()
+    lins = []
+    for idx, lin in enumerate(cfg.linears):
+        W = workloads.device_weight(torch, dev, lin.N, lin.K, seed=4000 + idx)
+        w = q.qlora_nf4_quantize(W)
+        del W
+        A, B = workloads.device_adapters(torch, dev, lin.N, lin.K, r, seed=5000 + idx)
+        lins.append(dict(lin=lin, w=w, A=A, B=B))
+    torch.cuda.synchronize()
+    nf4_bytes = sum(L["w"].codes.numel() + L["w"].absmax_q.numel() + 4 * L["w"].absmax_scale.numel()
+                    for L in lins)
+    log(f"setup (draw + quantize {len(lins)} linears on the device): {time.time() - t0:.1f}s, "
+        f"NF4 resident {nf4_bytes / 1e9:.2f} GB, device memory in use "
+        f"{torch.cuda.memory_allocated() / 1e9:.1f} GB")
+    scale = {K: 1.0 / (0.02 * K ** 0.5) for K in (8192, 22016)}
+    ws_f = torch.empty(max(q.lib().qlora_linear_fwd_workspace_bytes(M, L["lin"].N, L["lin"].K, r)
+                           for L in lins[:7]), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(q.lib().qlora_linear_bwd_workspace_bytes(M, L["lin"].N, L["lin"].K, r)
+                           for L in lins[:7]), dtype=torch.uint8, device=dev)
+    for L in lins:
+        L["dA"] = torch.empty_like(L["A"])
+        L["dB"] = torch.empty_like(L["B"])
+    x0 = workloads.device_activations(torch, dev, M, 8192, seed=4900)
+    dx_top = workloads.device_activations(torch, dev, M, 8192, seed=4901)
+
+    def lin_fwd(L, x):
+        y, T = q.qlora_linear_fwd(x, L["w"], L["A"], L["B"], s, workspace=ws_f)
+        y.mul_(scale[L["lin"].K])
+        L["X"], L["T"] = x, T
+        return y
+
+    def lin_bwd(L, dy):
+        dy = dy * scale[L["lin"].K]
+        dX, _, _ = q.qlora_linear_bwd(dy, L["X"], L["w"], L["A"], L["B"], s, T=L["T"],
+                                      dA=L["dA"], dB=L["dB"], workspace=ws_b)
+        return dX
+
+    def step():
+        x = x0
+        for l in range(0, len(lins), 7):
+            Lq, Lk, Lv, Lo, Lg, Lu, Ld = lins[l:l + 7]
+            h = lin_fwd(Lo, lin_fwd(Lv, lin_fwd(Lk, lin_fwd(Lq, x))))
+            a = lin_fwd(Lg, h) + lin_fwd(Lu, h)
+            x = lin_fwd(Ld, a)
+        dx = dx_top
+        for l in range(len(lins) - 7, -1, -7):
+            Lq, Lk, Lv, Lo, Lg, Lu, Ld = lins[l:l + 7]
+            da = lin_bwd(Ld, dx)
+            dh = lin_bwd(Lg, da) + lin_bwd(Lu, da)
+            dx = lin_bwd(Lq, lin_bwd(Lk, lin_bwd(Lv, lin_bwd(Lo, dh))))
+        for L in lins:   # saved inputs are freed after the backward
+            L.pop("X", None)
+            L.pop("T", None)
+        return dx
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    flops = sum(linear_flops(M, L["lin"].N, L["lin"].K, r) for L in lins)
+
+    # decode: one token through the chain, forward only
+    x1 = workloads.device_activations(torch, dev, 1, 8192, seed=4902)
+    ws_d = torch.empty(max(q.lib().qlora_linear_fwd_workspace_bytes(1, L["lin"].N, L["lin"].K, r)
+                           for L in lins[:7]), dtype=torch.uint8, device=dev)
+
+    def token():
+        x = x1
+        for l in range(0, len(lins), 7):
+            Lq, Lk, Lv, Lo, Lg, Lu, Ld = lins[l:l + 7]
+            f = lambda L, v: q.qlora_linear_fwd(v, L["w"], L["A"], L["B"], s, workspace=ws_d)[0] \
+                .mul_(scale[L["lin"].K])
+            h = f(Lo, f(Lv, f(Lk, f(Lq, x))))
+            x = f(Ld, f(Lg, h) + f(Lu, h))
+        return x
+
+    token()
+    torch.cuda.synchronize()
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        token()
+    torch.cuda.synchronize()
+    ms_token = (time.perf_counter() - t0) * 1e3 / reps
+    alg = sum(L["w"].codes.numel() + L["w"].absmax_q.numel() + 4 * L["w"].absmax_scale.numel()
+              + 2 * (L["lin"].K + L["lin"].N + L["lin"].K * r + r * L["lin"].N) for L in lins)
+    return dict(ms_step=ms_step, tflops=flops / (ms_step * 1e-3) / 1e12, flops_step=flops,
+                nf4_gb=nf4_bytes / 1e9, peak_mem_gb=peak / 1e9, ms_token=ms_token,
+                token_gbs=alg / (ms_token * 1e-3) / 1e9)
 
 
 def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
@@ -305,6 +424,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--config", type=int, default=1, choices=(1, 3, 4),
+                    help="1: the headline (LLaMA-7B linears, M=2048); 3: the 33B layer at "
+                         "M=4096 with recompute backward; 4: the 65B stack of 560 linears "
+                         "resident on the GPU (training step and one decode token)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg) of this many MiB before "
                          "the step, as the yardstick for rocprofv3 FETCH_SIZE/WRITE_SIZE")
@@ -336,7 +459,25 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    tr = run_training(q, torch, args.steps, args.warmup, dev)
+    if args.config == 4:
+        st = run_stack(q, torch, dev)
+        log(f"65B stack step: {st['ms_step']:.1f} ms, {st['tflops']:.1f} TFLOP/s; one decode token "
+            f"through all 560 linears: {st['ms_token']:.2f} ms, {st['token_gbs']:.0f} GB/s")
+        print(json.dumps({
+            "metric": "QLoRA fwd+bwd TFLOP/s, 65B-shaped stack resident on one GPU",
+            "value": st["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": 2, "warmup": 1,
+            "ms_per_step": st["ms_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "80 layers x 7 linears (hidden 8192, FFN 22016), NF4 base "
+                                   "quantized on the device, r=64 LoRA on every linear, chained "
+                                   "fwd + reverse bwd, M=2048 tokens",
+                       "tokens": 2048, "rank": 64, "lora_scale": 0.25},
+            "nf4_resident_gb": st["nf4_gb"], "peak_device_memory_gb": st["peak_mem_gb"],
+            "decode_token_ms": st["ms_token"], "decode_token_gbs": st["token_gbs"],
+        }), flush=True)
+        return
+
+    tr = run_training(q, torch, args.steps, args.warmup, dev, cfg_idx=args.config)
     value = tr["flops_step"] / (tr["ms_step"] * 1e-3) / 1e12
     log(f"train step: {tr['ms_step']:.3f} ms, {value:.1f} TFLOP/s; kernels: {tr['fam']}")
 
@@ -385,10 +526,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "LLaMA-7B-shaped QLoRA linears q,k,v,o [4096x4096], gate,up "
-                        "[11008x4096], down [4096x11008]; NF4 base (block 64, DQ 256); "
-                        "fwd + bwd (dX, dA, dB)",
-            "global_batch": cfg.M[0], "seq_len": 512, "batch": 4, "tokens": cfg.M[0],
+            "workload": ("LLaMA-7B-shaped QLoRA linears q,k,v,o [4096x4096], gate,up "
+                         "[11008x4096], down [4096x11008]; NF4 base (block 64, DQ 256); "
+                         "fwd + bwd (dX, dA, dB)") if args.config == 1 else
+                        ("33B-shaped QLoRA linears q,k,v,o [6656x6656], gate,up "
+                         "[17920x6656], down [6656x17920]; NF4 base; fwd + recompute bwd"),
+            "global_batch": cfg.M[0], "seq_len": 512 if args.config == 1 else 2048,
+            "batch": 4 if args.config == 1 else 2, "tokens": cfg.M[0],
             "rank": cfg.r, "lora_scale": cfg.s, "parallelism": "single GPU",
         },
         "roofline": roofline,

@@ -277,3 +277,80 @@ def test_workspace_contents_do_not_matter(fill):
     Yr, Tr = c.ref_fwd()
     assert_close("Y", oracle.bf16_bits_to_f64(Y1), Yr)
     assert_close("T", T1, Tr)
+
+
+def _device_config4_linear(idx, M):
+    """Linear idx of the 65B stack, drawn on the device as the stack is
+    (seeds 4000 + idx for W, 5000 + idx for A and B), with X and dY drawn on
+    the device too; returns device tensors and their host copies (the same
+    bytes on both sides)."""
+    cfg = workloads.CONFIGS[4]
+    lin = cfg.linears[idx]
+    W = workloads.device_weight(torch, dev(), lin.N, lin.K, seed=4000 + idx)
+    A, B = workloads.device_adapters(torch, dev(), lin.N, lin.K, cfg.r, seed=5000 + idx)
+    X = workloads.device_activations(torch, dev(), M, lin.K, seed=6000 + idx)
+    dY = workloads.device_activations(torch, dev(), M, lin.N, seed=7000 + idx)
+    host = dict(W=W.cpu().numpy(), X=bits(X), A=bits(A), B=bits(B), dY=bits(dY))
+    return cfg, lin, W, A, B, X, dY, host
+
+
+def test_config4_first_linear():
+    """65B stack, layer 0's q projection (8192 x 8192, M = 2048) drawn on the
+    device: codes and constants in full, sampled rows of Y and dX, full dA
+    and dB."""
+    need_gpu()
+    say("config 4 linear 0 (q, 8192x8192), M=2048")
+    cfg, lin, W, A, B, X, dY, h = _device_config4_linear(0, 2048)
+    w = q.qlora_nf4_quantize(W)
+    Y, T = q.qlora_linear_fwd(X, w, A, B, cfg.s)
+    dX, dA, dB = q.qlora_linear_bwd(dY, X, w, A, B, cfg.s, T=T)
+    torch.cuda.synchronize()
+    codes, e, d, _ = oracle.quantize(h["W"])
+    np.testing.assert_array_equal(w.codes.cpu().numpy(), codes)
+    np.testing.assert_array_equal(w.absmax_q.cpu().numpy(), e)
+    np.testing.assert_array_equal(w.absmax_scale.cpu().numpy(), d)
+    What = oracle.dequantize(codes, e, d, lin.N, lin.K)
+    rows = np.random.default_rng(4).choice(2048, 128, replace=False)
+    Yr, _ = oracle.linear_fwd(h["X"][rows], What, h["A"], h["B"], cfg.s)
+    assert_close("Y[rows]", Y.float().cpu().numpy()[rows], Yr)
+    dXr, _, _ = oracle.linear_bwd(h["dY"][rows], h["X"][rows], What, h["A"], h["B"], cfg.s)
+    assert_close("dX[rows]", dX.float().cpu().numpy()[rows], dXr)
+    _, dAr, dBr = oracle.linear_bwd(h["dY"], h["X"], What, h["A"], h["B"], cfg.s, need_dx=False)
+    assert_close("dA", dA.float().cpu().numpy(), dAr)
+    assert_close("dB", dB.float().cpu().numpy(), dBr)
+
+
+def test_config4_last_linear_row_groups():
+    """65B stack, layer 79's down projection (8192 x 22016, M = 2048): the
+    first and last 32 rows (43 whole groups of 256 block constants each,
+    so the oracle can quantize them alone) bit-exact, Y on those rows for
+    sampled tokens, full dA, and dB on those rows' columns."""
+    need_gpu()
+    idx = 559
+    say("config 4 linear 559 (down, 8192x22016), M=2048")
+    cfg, lin, W, A, B, X, dY, h = _device_config4_linear(idx, 2048)
+    assert lin.name == "down" and (32 * lin.K // 64) % 256 == 0
+    w = q.qlora_nf4_quantize(W)
+    Y, T = q.qlora_linear_fwd(X, w, A, B, cfg.s)
+    _, dA, dB = q.qlora_linear_bwd(dY, X, w, A, B, cfg.s, T=T, need_dx=False)
+    torch.cuda.synchronize()
+    codes_all = w.codes.cpu().numpy().reshape(lin.N, lin.K // 2)
+    e_all = w.absmax_q.cpu().numpy().reshape(lin.N, lin.K // 64)
+    d_all = w.absmax_scale.cpu().numpy()
+    toks = np.random.default_rng(5).choice(2048, 128, replace=False)
+    Yg = Y.float().cpu().numpy()
+    for r0 in (0, lin.N - 32):
+        rs = slice(r0, r0 + 32)
+        codes, e, d, _ = oracle.quantize(h["W"][rs])
+        g0 = r0 * (lin.K // 64) // 256
+        np.testing.assert_array_equal(codes_all[rs].reshape(-1), codes)
+        np.testing.assert_array_equal(e_all[rs].reshape(-1), e)
+        np.testing.assert_array_equal(d_all[g0:g0 + len(d)], d)
+        What = oracle.dequantize(codes, e, d, 32, lin.K)
+        Yr, _ = oracle.linear_fwd(h["X"][toks], What, h["A"], h["B"][:, rs], cfg.s)
+        assert_close(f"Y[toks, {r0}:+32]", Yg[toks][:, rs], Yr)
+        _, _, dBr = oracle.linear_bwd(h["dY"][:, rs], h["X"], What, h["A"], h["B"][:, rs],
+                                      cfg.s, need_dx=False)
+        assert_close(f"dB[:, {r0}:+32]", dB.float().cpu().numpy()[:, rs], dBr)
+    _, dAr, _ = oracle.linear_bwd(h["dY"], h["X"], None, h["A"], h["B"], cfg.s, need_dx=False)
+    assert_close("dA", dA.float().cpu().numpy(), dAr)

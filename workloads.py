@@ -126,3 +126,33 @@ def config_inputs(cfg_idx: int, M: int = None, seed: int = None,
         lin = cfg.linears[i]
         yield lin, draw_linear(linear_rng(cfg_idx, i, seed), lin.N, lin.K, m, cfg.r,
                                with_grad=with_grad)
+
+
+def device_weight(torch, dev, N: int, K: int, seed: int):
+    """Config 4's weights, drawn on the device (the 65B stack is too large
+    to draw on the host): torch.Generator(device).manual_seed(seed), W =
+    standard normal x 0.02, outliers (uniform < 0.001) x 10, float32 [N, K]."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    W = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02
+    mask = torch.rand((N, K), generator=g, device=dev) < 0.001
+    W[mask] *= 10.0
+    return W
+
+
+def device_adapters(torch, dev, N: int, K: int, r: int, seed: int, b_std: float = 0.01):
+    """A [K, r] ~ N(0, 1/r) and B [r, N] ~ N(0, b_std), bf16, drawn on the
+    device with torch.Generator(device).manual_seed(seed)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    A = (torch.randn((K, r), generator=g, device=dev) / r).to(torch.bfloat16)
+    B = (torch.randn((r, N), generator=g, device=dev) * b_std).to(torch.bfloat16)
+    return A, B
+
+
+def device_activations(torch, dev, M: int, K: int, seed: int):
+    """X [M, K] standard normal, bf16, drawn on the device."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+
