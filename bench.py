@@ -379,11 +379,13 @@ def _rocprof_csvs(root, suffix):
     return sorted(out)
 
 
-def summarize_rocprof(root, copy_mib, top=16):
+def summarize_rocprof(root, copy_mib, top=16, by_grid=False):
     """Text summary of a rocprofv3 output folder (csv format): the kernel
-    statistics table, and per-dispatch counter means per kernel.  With a
-    calibration copy of `copy_mib` MiB in the run, the FETCH_SIZE/WRITE_SIZE
-    scale factors (bytes moved / counter bytes) are printed too."""
+    statistics table, and per-dispatch counter means per kernel (per kernel
+    and grid size with by_grid, which tells shapes of one kernel apart).
+    With a calibration copy of `copy_mib` MiB in the run, the
+    FETCH_SIZE/WRITE_SIZE scale factors (bytes moved / counter bytes) are
+    printed too."""
     import csv
     lines = []
     for path in _rocprof_csvs(root, "kernel_stats.csv"):
@@ -399,7 +401,11 @@ def summarize_rocprof(root, copy_mib, top=16):
     for path in _rocprof_csvs(root, "counter_collection.csv"):
         agg = {}
         for r in csv.DictReader(open(path)):
-            key = (r["Kernel_Name"], r["Counter_Name"])
+            name = r["Kernel_Name"]
+            if by_grid:   # (the calibration copy keeps its name's "neg" in front)
+                tag = "neg_kernel " if "neg_kernel" in name else ""
+                name = f"{(tag + name.split('(')[0])[:52]} grid={r['Grid_Size']}"
+            key = (name, r["Counter_Name"])
             agg.setdefault(key, []).append(float(r["Counter_Value"]))
         lines.append(f"{'kernel':70s} {'counter':>12s} {'dispatches':>10s} {'mean_per_dispatch':>18s}")
         for (k, c), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
@@ -424,6 +430,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the decode leg (65B shapes, M in {1, 4, 16}) and print its "
+                         "numbers (for profiling it on its own)")
+    ap.add_argument("--decode-reps", type=int, default=20,
+                    help="graph replays per shape in the decode leg")
     ap.add_argument("--config", type=int, default=1, choices=(1, 3, 4),
                     help="1: the headline (LLaMA-7B linears, M=2048); 3: the 33B layer at "
                          "M=4096 with recompute backward; 4: the 65B stack of 560 linears "
@@ -433,9 +444,12 @@ def main():
                          "the step, as the yardstick for rocprofv3 FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print a text summary of a rocprofv3 csv output folder and exit")
+    ap.add_argument("--by-grid", action="store_true",
+                    help="with --summarize-rocprof: counter means per kernel and grid size")
     args = ap.parse_args()
     if args.summarize_rocprof:
-        print(summarize_rocprof(args.summarize_rocprof, args.copy_calibration_mib))
+        print(summarize_rocprof(args.summarize_rocprof, args.copy_calibration_mib,
+                                by_grid=args.by_grid))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -459,6 +473,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.decode_only:
+        dec = run_decode(q, torch, dev, reps=args.decode_reps)
+        print(json.dumps({"metric": "QLoRA decode (M=1) effective HBM GB/s, 65B shapes",
+                          "value": dec["M=1"]["gbs_call"], "unit": "GB/s", "n_gpus": 1,
+                          "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                          "decode": dec}), flush=True)
+        return
     if args.config == 4:
         st = run_stack(q, torch, dev)
         log(f"65B stack step: {st['ms_step']:.1f} ms, {st['tflops']:.1f} TFLOP/s; one decode token "
@@ -504,7 +525,7 @@ def main():
 
     decode = None
     if not args.no_decode:
-        decode = run_decode(q, torch, dev)
+        decode = run_decode(q, torch, dev, reps=args.decode_reps)
 
     cpu = None
     if not args.no_cpu_baseline:
