@@ -335,8 +335,7 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
       e = launch_lora_down(X, M, w->K, A, r, Tr, part, hs);
       T = Tr;
     }
-    if (e == hipSuccess) e = launch_lora_grad_in(dY, M, w->N, B, r, G, part, hs);
-    if (e == hipSuccess) e = launch_grad_b(dY, M, w->N, T, r, s, dB, part, hs);
+    if (e == hipSuccess) e = launch_grad_in_and_b(dY, M, w->N, B, T, r, s, G, dB, part, hs);
     if (e == hipSuccess) e = launch_grad_a(X, M, w->K, G, r, s, dA, part, hs);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }

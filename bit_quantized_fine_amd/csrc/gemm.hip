@@ -325,20 +325,57 @@ __device__ void store_f32(const Mma<BP, BQ>& mma, float* out, int64_t ldo,
 
 // HL: 0 = both operands bf16; 1 = P is fp32 (hi/lo); 2 = Q is fp32 (hi/lo).
 template <int BP, int BQ, class LP, class LQ, int HL>
-__global__ __launch_bounds__(NT) void k_rank(OpParams po, OpParams qo, int ntiles,
-                                             int tps, float* ws, int64_t P, int64_t Q) {
-  constexpr int XT = HL == 0 ? 0 : (HL == 1 ? LP::TILE : LQ::TILE);
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (LP::TILE + LQ::TILE + XT)];
-  const int tid = threadIdx.x;
-  const int64_t p0 = (int64_t)blockIdx.x * BP, q0 = (int64_t)blockIdx.y * BQ;
-  const int z = blockIdx.z;
-  const int kt0 = z * tps, kt1 = min(ntiles, kt0 + tps);
+struct RankKind {
+  static constexpr int XT = HL == 0 ? 0 : (HL == 1 ? LP::TILE : LQ::TILE);
+  static constexpr int LDS = 2 * (LP::TILE + LQ::TILE + XT);   // bf16 elements
+};
+
+// One product: tile (x, y) of C and reduction split z.
+struct RankJob {
+  OpParams po, qo;
+  int ntiles, tps;
+  float* ws;
+  int64_t P, Q;
+  int px, qy, nblk;   // tiles along P and Q; workgroups (px qy splits)
+};
+
+template <int BP, int BQ, class LP, class LQ, int HL>
+__device__ __forceinline__ void rank_tile(const RankJob& j, int x, int y, int z, uint16_t* lds,
+                                          int tid) {
+  const int64_t p0 = (int64_t)x * BP, q0 = (int64_t)y * BQ;
+  const int kt0 = z * j.tps, kt1 = min(j.ntiles, kt0 + j.tps);
   Mma<BP, BQ> mma;
   mma.zero();
-  LP lp{po, p0};
-  LQ lq{qo, q0};
+  LP lp{j.po, p0};
+  LQ lq{j.qo, q0};
   run_tiles<BP, BQ, HL, 2>(lp, lq, kt0, kt1, mma, lds, tid);
-  store_f32(mma, ws + (int64_t)z * P * Q, P, p0, q0, P, Q, tid);
+  store_f32(mma, j.ws + (int64_t)z * j.P * j.Q, j.P, p0, q0, j.P, j.Q, tid);
+}
+
+template <int BP, int BQ, class LP, class LQ, int HL>
+__global__ __launch_bounds__(NT) void k_rank(RankJob j) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[RankKind<BP, BQ, LP, LQ, HL>::LDS];
+  rank_tile<BP, BQ, LP, LQ, HL>(j, blockIdx.x, blockIdx.y, blockIdx.z, lds, threadIdx.x);
+}
+
+// Two independent products in one launch (workgroups [0, a.nblk) run the
+// first, the rest the second), so they share the machine instead of running
+// one after the other.
+template <int BPA, int BQA, class LPA, class LQA, int HLA, int BPB, int BQB, class LPB, class LQB,
+          int HLB>
+__global__ __launch_bounds__(NT) void k_rank_pair(RankJob a, RankJob b) {
+  constexpr int LA = RankKind<BPA, BQA, LPA, LQA, HLA>::LDS;
+  constexpr int LB = RankKind<BPB, BQB, LPB, LQB, HLB>::LDS;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LA > LB ? LA : LB];
+  int blk = blockIdx.x;   // uniform: the branch is a scalar one
+  if (blk < a.nblk) {
+    rank_tile<BPA, BQA, LPA, LQA, HLA>(a, blk % a.px, (blk / a.px) % a.qy, blk / (a.px * a.qy),
+                                       lds, threadIdx.x);
+  } else {
+    blk -= a.nblk;
+    rank_tile<BPB, BQB, LPB, LQB, HLB>(b, blk % b.px, (blk / b.px) % b.qy, blk / (b.px * b.qy),
+                                       lds, threadIdx.x);
+  }
 }
 
 // out[i] = scale * sum_z ws[z][i]; fp32 or bf16 output; 4 elements a thread.
@@ -366,6 +403,40 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* ws, int split
         u32x2{pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w)};
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(out) + i) = s;
+  }
+}
+
+// Two split reductions in one launch: blocks [0, ga) reduce the first.
+struct ReduceJob {
+  const float* ws;
+  int splits;
+  int64_t count;
+  float scale;
+  void* out;
+};
+
+template <bool BF16_A, bool BF16_B>
+__global__ __launch_bounds__(256) void k_split_reduce_pair(ReduceJob a, ReduceJob b, int ga) {
+  const bool first = static_cast<int>(blockIdx.x) < ga;
+  const ReduceJob& j = first ? a : b;
+  const int64_t i = 4 * ((int64_t)(first ? blockIdx.x : blockIdx.x - ga) * blockDim.x + threadIdx.x);
+  if (i >= j.count) return;
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
+  int z = 0;
+  for (; z + 4 <= j.splits; z += 4) {
+    s0 += *reinterpret_cast<const f32x4*>(j.ws + (int64_t)(z + 0) * j.count + i);
+    s1 += *reinterpret_cast<const f32x4*>(j.ws + (int64_t)(z + 1) * j.count + i);
+    s2 += *reinterpret_cast<const f32x4*>(j.ws + (int64_t)(z + 2) * j.count + i);
+    s3 += *reinterpret_cast<const f32x4*>(j.ws + (int64_t)(z + 3) * j.count + i);
+  }
+  for (; z < j.splits; ++z) s0 += *reinterpret_cast<const f32x4*>(j.ws + (int64_t)z * j.count + i);
+  f32x4 s = (s0 + s1) + (s2 + s3);
+  s *= j.scale;
+  if (first ? BF16_A : BF16_B) {
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(j.out) + i) =
+        u32x2{pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w)};
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(j.out) + i) = s;
   }
 }
 
@@ -489,6 +560,22 @@ Split choose_split(int64_t nred, int64_t ptiles, int64_t qtiles) {
   return s;
 }
 
+RankJob job(const OpParams& po, const OpParams& qo, const Split& sp, float* ws, int64_t P,
+            int64_t Q, int64_t px, int64_t qy) {
+  RankJob j;
+  j.po = po;
+  j.qo = qo;
+  j.ntiles = sp.ntiles;
+  j.tps = sp.tps;
+  j.ws = ws;
+  j.P = P;
+  j.Q = Q;
+  j.px = static_cast<int>(px);
+  j.qy = static_cast<int>(qy);
+  j.nblk = static_cast<int>(px * qy * sp.splits);
+  return j;
+}
+
 template <bool BF16>
 hipError_t reduce(const float* ws, int splits, int64_t count, float scale, void* out,
                   hipStream_t stream) {
@@ -514,9 +601,8 @@ size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r) {
   const Split b = choose_split(M, (N + RB_X - 1) / RB_X, rt);
   size_t m = 0;
   m = std::max<size_t>(m, (size_t)t.splits * M * r);
-  m = std::max<size_t>(m, (size_t)g.splits * M * r);
+  m = std::max<size_t>(m, (size_t)g.splits * M * r + (size_t)b.splits * r * N);   // together
   m = std::max<size_t>(m, (size_t)a.splits * K * r);
-  m = std::max<size_t>(m, (size_t)b.splits * r * N);
   return m;
 }
 
@@ -554,25 +640,39 @@ hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint1
   const Split sp = choose_split(K, pt, qt);
   prof_begin(4, stream);
   hipLaunchKernelGGL((k_rank<RB_R, RB_X, Bf16RedMajor<RB_R>, Bf16Nat<RB_X>, 0>),
-                     dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(A, r, r, K),
-                     op(X, K, M, K), sp.ntiles, sp.tps, ws, (int64_t)r, M);
+                     dim3(pt, qt, sp.splits), dim3(NT), 0, stream,
+                     job(op(A, r, r, K), op(X, K, M, K), sp, ws, r, M, pt, qt));
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = reduce<false>(ws, sp.splits, M * r, 1.f, T, stream);
   prof_end(4, stream);
   return e;
 }
 
-hipError_t launch_lora_grad_in(const uint16_t* dY, int64_t M, int64_t N,
-                               const uint16_t* B, int r, float* G, float* ws,
-                               hipStream_t stream) {
-  const int64_t pt = (r + RB_R - 1) / RB_R, qt = (M + RB_X - 1) / RB_X;
-  const Split sp = choose_split(N, pt, qt);
+hipError_t launch_grad_in_and_b(const uint16_t* dY, int64_t M, int64_t N, const uint16_t* B,
+                                const float* T, int r, float s, float* G, uint16_t* dB,
+                                float* ws, hipStream_t stream) {
+  // G = dY . B^T: tiles (ranks, tokens), split over N
+  const int64_t gpt = (r + RB_R - 1) / RB_R, gqt = (M + RB_X - 1) / RB_X;
+  const Split gs = choose_split(N, gpt, gqt);
+  // dB partials: tiles (N, ranks), split over M; after G's partials in ws
+  const int64_t bpt = (N + RB_X - 1) / RB_X, bqt = (r + RB_R - 1) / RB_R;
+  const Split bs = choose_split(M, bpt, bqt);
+  float* wsb = ws + (size_t)gs.splits * M * r;
+  const RankJob jg = job(op(B, N, r, N), op(dY, N, M, N), gs, ws, r, M, gpt, gqt);
+  const RankJob jb = job(op(dY, N, N, M), op(T, r, r, M), bs, wsb, N, r, bpt, bqt);
   prof_begin(4, stream);
-  hipLaunchKernelGGL((k_rank<RB_R, RB_X, Bf16Nat<RB_R>, Bf16Nat<RB_X>, 0>),
-                     dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(B, N, r, N),
-                     op(dY, N, M, N), sp.ntiles, sp.tps, ws, (int64_t)r, M);
+  hipLaunchKernelGGL((k_rank_pair<RB_R, RB_X, Bf16Nat<RB_R>, Bf16Nat<RB_X>, 0, RB_X, RB_R,
+                                  Bf16RedMajor<RB_X>, F32RedMajor<RB_R>, 2>),
+                     dim3(jg.nblk + jb.nblk), dim3(NT), 0, stream, jg, jb);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess) e = reduce<false>(ws, sp.splits, M * r, 1.f, G, stream);
+  if (e == hipSuccess) {
+    const ReduceJob rg{ws, gs.splits, M * r, 1.f, G};
+    const ReduceJob rb{wsb, bs.splits, r * N, s, dB};
+    const unsigned ga = cdiv(rg.count / 4, 256), gb = cdiv(rb.count / 4, 256);
+    hipLaunchKernelGGL((k_split_reduce_pair<false, true>), dim3(ga + gb), dim3(256), 0, stream,
+                       rg, rb, static_cast<int>(ga));
+    e = hipGetLastError();
+  }
   prof_end(4, stream);
   return e;
 }
@@ -583,24 +683,10 @@ hipError_t launch_grad_a(const uint16_t* X, int64_t M, int64_t K, const float* G
   const Split sp = choose_split(M, pt, qt);
   prof_begin(4, stream);
   hipLaunchKernelGGL((k_rank<RB_R, RB_X, F32RedMajor<RB_R>, Bf16RedMajor<RB_X>, 1>),
-                     dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(G, r, r, M),
-                     op(X, K, K, M), sp.ntiles, sp.tps, ws, (int64_t)r, K);
+                     dim3(pt, qt, sp.splits), dim3(NT), 0, stream,
+                     job(op(G, r, r, M), op(X, K, K, M), sp, ws, r, K, pt, qt));
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) e = reduce<true>(ws, sp.splits, K * r, s, dA, stream);
-  prof_end(4, stream);
-  return e;
-}
-
-hipError_t launch_grad_b(const uint16_t* dY, int64_t M, int64_t N, const float* T,
-                         int r, float s, uint16_t* dB, float* ws, hipStream_t stream) {
-  const int64_t pt = (N + RB_X - 1) / RB_X, qt = (r + RB_R - 1) / RB_R;
-  const Split sp = choose_split(M, pt, qt);
-  prof_begin(4, stream);
-  hipLaunchKernelGGL((k_rank<RB_X, RB_R, Bf16RedMajor<RB_X>, F32RedMajor<RB_R>, 2>),
-                     dim3(pt, qt, sp.splits), dim3(NT), 0, stream, op(dY, N, N, M),
-                     op(T, r, r, M), sp.ntiles, sp.tps, ws, N, (int64_t)r);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess) e = reduce<true>(ws, sp.splits, r * N, s, dB, stream);
   prof_end(4, stream);
   return e;
 }

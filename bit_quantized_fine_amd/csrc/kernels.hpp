@@ -68,15 +68,13 @@ hipError_t launch_lora_down_partials(const uint16_t* X, int64_t M, int64_t K, co
 hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K,
                             const uint16_t* A, int r, float* T, float* ws,
                             hipStream_t stream);
-// G[M,r] = dY . B^T (fp32 out).
-hipError_t launch_lora_grad_in(const uint16_t* dY, int64_t M, int64_t N,
-                               const uint16_t* B, int r, float* G, float* ws,
-                               hipStream_t stream);
+// G[M,r] = dY . B^T (fp32 out) and dB[r,N] = bf16( s . T^T . dY ), both
+// products in one launch and both split reductions in one more.
+hipError_t launch_grad_in_and_b(const uint16_t* dY, int64_t M, int64_t N, const uint16_t* B,
+                                const float* T, int r, float s, float* G, uint16_t* dB,
+                                float* ws, hipStream_t stream);
 // dA[K,r] = bf16( s . X^T . G ).
 hipError_t launch_grad_a(const uint16_t* X, int64_t M, int64_t K, const float* G,
                          int r, float s, uint16_t* dA, float* ws, hipStream_t stream);
-// dB[r,N] = bf16( s . T^T . dY ).
-hipError_t launch_grad_b(const uint16_t* dY, int64_t M, int64_t N, const float* T,
-                         int r, float s, uint16_t* dB, float* ws, hipStream_t stream);
 
 }  // namespace qnf4
