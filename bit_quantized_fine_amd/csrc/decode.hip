@@ -53,6 +53,7 @@ constexpr int kDecXLdsBytes = 64 * 1024;       // X staged in LDS up to this siz
 constexpr int kDecLdsMax = 160 * 1024;         // LDS of one workgroup
 constexpr int kDecXPieces = kDecXLdsBytes / 16 / kDecThreads;   // at most 4 16-byte X pieces a thread
 constexpr int kDecXZero = 256;                 // zero bytes after X (lanes past M read there)
+constexpr int kDecXPad = 8;                    // X rows in LDS are K + 8 elements apart
 // T partial sums (at most kMaxDownPartials of them) are added up by
 // half-waves: half-wave h takes quads (4 ranks of one token) h and h + 32,
 // its lane z partial z.  M r <= kDecTSumMaxMR keeps that within two quads
@@ -67,7 +68,8 @@ int round16(int64_t v) { return static_cast<int>((v + 15) / 16 * 16); }
 
 // Dynamic LDS of one workgroup, in order: the level table, B's columns
 // [r][32], the summed T, the block scales [K/64 + 1][32] fp32, and (XLDS) X
-// [M][K] followed by kDecXZero zero bytes.  After the main loop the waves'
+// [M][K + kDecXPad] (the padding puts the rows' equal columns in different
+// banks) followed by kDecXZero zero bytes.  After the main loop the waves'
 // partial sums [kDecThreads] f32x4 reuse the bytes from the block scales on.
 struct DecLds {
   int boff, toff, coff, xoff, total;
@@ -77,7 +79,7 @@ struct DecLds {
     toff = boff + round16(int64_t(64) * r);
     coff = toff + kDecTSumMaxMR * 4;
     xoff = coff + round16(kDecRows * (kb + 1) * 4);
-    const int end = xoff + (xlds ? round16(M * K * 2) + kDecXZero : 0);
+    const int end = xoff + (xlds ? round16(M * (K + kDecXPad) * 2) + kDecXZero : 0);
     total = end > coff + kDecThreads * 16 ? end : coff + kDecThreads * 16;
   }
 };
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   f32x4* tfin = reinterpret_cast<f32x4*>(dyn + toff);                // [kDecTSumMaxMR / 4]
   float* csc = reinterpret_cast<float*>(dyn + coff);                 // [KB + 1][ROWS]
   f32x4* red = reinterpret_cast<f32x4*>(dyn + coff);                 // after the main loop
-  uint16_t* xs = reinterpret_cast<uint16_t*>(dyn + xoff);            // [M][K], zeros
+  uint16_t* xs = reinterpret_cast<uint16_t*>(dyn + xoff);            // [M][K + pad], zeros
   const Levels lv = load_levels(tb);
   const int tid = threadIdx.x;
   const int wave = wave_id(), lane = tid & 63;
@@ -217,10 +219,11 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int idx = tid + i * kDecThreads;
-      if (16 * idx < xrange) *reinterpret_cast<u32x4*>(xs + 8 * idx) = xw[i];
+      const int row = idx / (K32 / 8);   // piece idx holds elements 8 idx .. of X [M][K]
+      if (16 * idx < xrange) *reinterpret_cast<u32x4*>(xs + 8 * idx + kDecXPad * row) = xw[i];
     }
     if (tid < kDecXZero / 16)
-      *reinterpret_cast<u32x4*>(xs + M * K32 + 8 * tid) = u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(xs + M * (K32 + kDecXPad) + 8 * tid) = u32x4{0, 0, 0, 0};
   }
   // Block scales c = e . d, transposed so that the four rows of a lane's
   // outputs read 16 consecutive bytes; column KB is zero.
@@ -244,7 +247,8 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // Lanes past M read X from the zero bytes with stride 0; past K (the second
   // block of a chunk when K % 128 == 64) they meet a zero scale, and their X
   // reads stay inside the next token row or the zero bytes.
-  const uint16_t* xlane = li < M ? xs + li * K32 + xo0 : xs + M * K32 + xo0;
+  const int xrow = K32 + kDecXPad;
+  const uint16_t* xlane = li < M ? xs + li * xrow + xo0 : xs + M * xrow + xo0;
   const int xstep = li < M ? 128 : 0;
   const float* clane = csc + 16 * p + 4 * g;   // scales of the lane's output rows
   // Table addresses: the lane's copy offset in byte 0, entry in byte 1.  The
