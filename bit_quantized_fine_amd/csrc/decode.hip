@@ -54,13 +54,13 @@ constexpr int kDecLdsMax = 160 * 1024;         // LDS of one workgroup
 constexpr int kDecXPieces = kDecXLdsBytes / 16 / kDecThreads;   // at most 4 16-byte X pieces a thread
 constexpr int kDecXZero = 256;                 // zero bytes after X (lanes past M read there)
 constexpr int kDecXPad = 8;                    // X rows in LDS are K + 8 elements apart
-// T partial sums (at most kMaxDownPartials of them) are added up by
-// half-waves: half-wave h takes quads (4 ranks of one token) h and h + 32,
-// its lane z partial z.  M r <= kDecTSumMaxMR keeps that within two quads
-// per half-wave.
-constexpr int kDecTQuads = 2;
-constexpr int kDecTSumMaxMR = 4 * (kDecThreads / 32) * kDecTQuads;
-static_assert(kMaxDownPartials <= 32, "one partial per lane of a half-wave");
+// T partial sums (at most kMaxDownPartials of them) are added up by rows of
+// 16 lanes: row h takes the quad (4 ranks of one token) h, its lane z the
+// partials z and z + 16.  M r <= kDecTSumMaxMR keeps that within one quad
+// per row.
+constexpr int kDecTQuads = 2;   // loads per lane (two partials, or 8 values of a final T)
+constexpr int kDecTSumMaxMR = 4 * (kDecThreads / 16);
+static_assert(kMaxDownPartials <= 2 * 16, "two partials per lane of a 16-lane row");
 // Block constants of the workgroup's rows, read as 8-byte pieces.
 constexpr int kDecEPieces = (kDecRows * kDecMaxK / kBlock / 8 + kDecThreads - 1) / kDecThreads;
 
@@ -115,8 +115,8 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 
   // Buffer descriptors: rows n >= N fall outside the code / constant buffers
   // and read as zero, and so do token rows li >= M of X.  The second block of
-  // a chunk past K (K % 128 == 64) gets a zero scale instead, so the code
-  // bytes it reads from the next row contribute nothing.
+  // a chunk past K (K % 128 == 64) reads the next row's codes; its products
+  // are dropped.
   const uint32_t nb = static_cast<uint32_t>(N * K / kBlock);
   const BufRes rc = make_bufres(codes, static_cast<uint32_t>(N * K / 2));
   const BufRes re = make_bufres(absmax_q, nb);
@@ -154,13 +154,13 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
       xw[i] = buf_load16(rx, 16 * idx < xrange ? 16u * idx : kDecOffNone);
     }
   }
-  // T for the LoRA update, used only after the main loop.  With nz > 0,
-  // half-wave h sums quads (4 ranks of one token) h and h + 32 over the
-  // partials, lane z loading partial z; with nz == 0 T is final and the lanes
-  // of the LoRA waves load their own 8 values of it.
+  // T for the LoRA update, used only after the main loop.  With nz > 0, the
+  // 16-lane row h sums quad h (4 ranks of one token) over the partials, lane
+  // z loading partials z and z + 16; with nz == 0 T is final and the lanes of
+  // the LoRA waves load their own 8 values of it.
   const int nsteps = (r + 31) / 32;
   const int nq = M * r / 4;
-  const int hw = tid >> 5, hl = tid & 31;
+  const int hr = tid >> 4, hl = tid & 15;
   f32x4 tq[kDecTQuads];
   {
     // (one load sequence for both cases: a branch here would make the
@@ -170,9 +170,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const bool lora_lane = kw < nsteps && li < M && j < r;
 #pragma unroll
     for (int i = 0; i < kDecTQuads; ++i) {
-      const int q = hw + (kDecThreads / 32) * i;
-      const bool ok = nz > 0 ? (q < nq && hl < nz) : lora_lane;
-      const int idx = nz > 0 ? hl * M * r + 4 * q : li * r + j + 4 * i;
+      const int z = hl + 16 * i;
+      const bool ok = nz > 0 ? (hr < nq && z < nz) : lora_lane;
+      const int idx = nz > 0 ? z * M * r + 4 * hr : li * r + j + 4 * i;
       tq[i] = __builtin_bit_cast(
           f32x4, buf_load16(rt, ok ? static_cast<uint32_t>(idx * 4) : kDecOffNone));
     }
@@ -224,6 +224,8 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     }
     if (tid < kDecXZero / 16)
       *reinterpret_cast<u32x4*>(xs + M * (K32 + kDecXPad) + 8 * tid) = u32x4{0, 0, 0, 0};
+    if (tid < M)   // the row padding, which the half chunk past K reads
+      *reinterpret_cast<u32x4*>(xs + tid * (K32 + kDecXPad) + K32) = u32x4{0, 0, 0, 0};
   }
   // Block scales c = e . d, transposed so that the four rows of a lane's
   // outputs read 16 consecutive bytes; column KB is zero.
@@ -245,8 +247,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   if ((tid >> 2) < r) reinterpret_cast<u32x4*>(bst)[tid] = bpiece;
 
   // Lanes past M read X from the zero bytes with stride 0; past K (the second
-  // block of a chunk when K % 128 == 64) they meet a zero scale, and their X
-  // reads stay inside the next token row or the zero bytes.
+  // block of a chunk when K % 128 == 64) their X reads stay inside the row
+  // padding, the next token row or the zero bytes, and the products are
+  // dropped.
   const int xrow = K32 + kDecXPad;
   const uint16_t* xlane = li < M ? xs + li * xrow + xo0 : xs + M * xrow + xo0;
   const int xstep = li < M ? 128 : 0;
@@ -291,9 +294,14 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     pA = mfma16(a[1], xf[1], pA);
     f32x4 pB = mfma16(a[2], xf[2], zero);
     pB = mfma16(a[3], xf[3], pB);
+    // (the second block of a chunk past K, when K % 128 == 64, is dropped
+    // rather than scaled by zero: its products may hold anything)
+    const bool second = 2 * c + 1 < KB;   // wave-uniform
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[j] = __builtin_fmaf(cB[j], pB[j], __builtin_fmaf(cA[j], pA[j], acc[j]));
+    for (int j = 0; j < 4; ++j) {
+      acc[j] = __builtin_fmaf(cA[j], pA[j], acc[j]);
+      if (second) acc[j] = __builtin_fmaf(cB[j], pB[j], acc[j]);
+    }
   };
   __syncthreads();
   for (int t0 = 0; t0 < nmine; t0 += D) {
@@ -318,23 +326,21 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   }
 
   // T's partial sums are added after the main loop, off its critical path:
-  // a butterfly over each half-wave, in a fixed order (deterministic).
+  // the lane's two partials, then a butterfly over its 16-lane row with DPP
+  // moves (xor 1, xor 2, rotate 4, rotate 8), in a fixed order
+  // (deterministic).
   if (nz > 0) {
+    f32x4 v = tq[0] + tq[1];
 #pragma unroll
-    for (int i = 0; i < kDecTQuads; ++i) {
-      f32x4 v = tq[i];
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) {
-        v.x += __shfl_xor(v.x, o, 32);
-        v.y += __shfl_xor(v.y, o, 32);
-        v.z += __shfl_xor(v.z, o, 32);
-        v.w += __shfl_xor(v.w, o, 32);
-      }
-      const int q = hw + (kDecThreads / 32) * i;
-      if (hl == 0 && q < nq) {
-        tfin[q] = v;
-        if (blockIdx.x == 0) *reinterpret_cast<f32x4*>(Tout + 4 * q) = v;   // [M][r]
-      }
+    for (int c = 0; c < 4; ++c) {
+      v[c] += dpp_f32<0xB1>(v[c]);    // quad_perm [1, 0, 3, 2]
+      v[c] += dpp_f32<0x4E>(v[c]);    // quad_perm [2, 3, 0, 1]
+      v[c] += dpp_f32<0x124>(v[c]);   // row_ror 4
+      v[c] += dpp_f32<0x128>(v[c]);   // row_ror 8
+    }
+    if (hl == 0 && hr < nq) {
+      tfin[hr] = v;
+      if (blockIdx.x == 0) *reinterpret_cast<f32x4*>(Tout + 4 * hr) = v;   // [M][r]
     }
   }
   __syncthreads();

@@ -194,6 +194,13 @@ __device__ __forceinline__ uint32_t rep_bf16_lookup(uint32_t ta, uint32_t w) {
   return *reinterpret_cast<LdsU32*>(static_cast<uintptr_t>(a));
 }
 
+// v moved across lanes by a DPP control word (all rows and banks enabled).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 // Raw buffer access: a descriptor over [p, p + nbytes) in scalar registers
 // and 32-bit byte offsets; reads outside the range return zero.
 typedef __amdgpu_buffer_rsrc_t BufRes;
