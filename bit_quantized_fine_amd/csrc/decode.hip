@@ -73,20 +73,20 @@ int round16(int64_t v) { return static_cast<int>((v + 15) / 16 * 16); }
 // partial sums [kDecThreads] f32x4 reuse the bytes from the block scales on.
 struct DecLds {
   int boff, toff, coff, xoff, total;
-  DecLds(int64_t M, int64_t K, int r, bool xlds) {
+  DecLds(int64_t M, int64_t K, int r, bool xlds, int fr = 1) {
     const int64_t kb = K / kBlock;
     boff = kRepTabBytes;
     toff = boff + round16(int64_t(64) * r);
     coff = toff + kDecTSumMaxMR * 4;
     xoff = coff + round16(kDecRows * (kb + 1) * 4);
     const int end = xoff + (xlds ? round16(M * (K + kDecXPad) * 2) + kDecXZero : 0);
-    total = end > coff + kDecThreads * 16 ? end : coff + kDecThreads * 16;
+    total = end > coff + kDecThreads * 16 * fr ? end : coff + kDecThreads * 16 * fr;
   }
 };
 
 }  // namespace
 
-template <int D, int XP>
+template <int D, int XP, int FR>
 __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
@@ -95,6 +95,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     Nf4Tables tb, int boff, int toff, int coff, int xoff, float inv_kb) {
   constexpr int ROWS = kDecRows;
   constexpr bool XLDS = XP > 0;   // X staged in LDS, XP 16-byte pieces per thread
+  // FR = 1: eight waves per fragment; FR = 2: every wave works on both
+  // fragments, and 16 waves split K (each X piece then serves 32 rows).
+  constexpr int KS = kDecKSlots * FR;   // waves splitting K
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   char* tab = reinterpret_cast<char*>(dyn);                          // bf16 level pairs
   uint16_t* bst = reinterpret_cast<uint16_t*>(dyn + boff);           // B columns [r][ROWS]
@@ -105,13 +108,14 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   const Levels lv = load_levels(tb);
   const int tid = threadIdx.x;
   const int wave = wave_id(), lane = tid & 63;
-  const int p = wave / kDecKSlots, kw = wave % kDecKSlots;           // fragment, K slot
+  const int p = FR == 1 ? wave / kDecKSlots : 0, kw = wave % KS;      // fragment, K slot
   const int li = lane & 15, g = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * ROWS;
   const int K32 = static_cast<int>(K);
   const int KB = K32 / kBlock;
   const int nchunks = (K32 + 127) / 128;
-  const int nmine = nchunks > kw ? (nchunks - kw + kDecKSlots - 1) / kDecKSlots : 0;
+  const int nmine = nchunks > kw ? (nchunks - kw + KS - 1) / KS : 0;
+  auto frag = [&](int f) { return FR == 1 ? p : f; };   // fragment of the wave's slot f
 
   // Buffer descriptors: rows n >= N fall outside the code / constant buffers
   // and read as zero, and so do token rows li >= M of X.  The second block of
@@ -192,22 +196,27 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // wave's last one get an offset beyond every buffer and read zeros without
   // memory traffic.  Without X in LDS, each lane also loads the X pieces its
   // four MFMAs take.
-  const uint32_t cb = static_cast<uint32_t>((n0 + 16 * p + li) * (K / 2)) + 64u * kw + 16u * g;
+  uint32_t cb[FR];
+#pragma unroll
+  for (int f = 0; f < FR; ++f)
+    cb[f] = static_cast<uint32_t>((n0 + 16 * frag(f) + li) * (K / 2)) + 64u * kw + 16u * g;
   // k offset (inside a block) of the 8 codes that lane group g supplies to
   // step 0 of a block after the swap (dword 4 (g % 2) + 2 (g / 2); step 1
   // takes the next dword).
   const int xo0 = 8 * (4 * (g & 1) + 2 * (g >> 1));
   const uint32_t xb = (static_cast<uint32_t>(li) * K32 + 128u * kw + xo0) * 2u;
-  u32x4 cw[D];
+  u32x4 cw[D][FR];
   u32x4 xv[XLDS ? 1 : D][4];
   auto load = [&](int t, int st) {
     const bool live = t < nmine;
-    cw[st] = buf_load16(rc, live ? cb + 64u * kDecKSlots * t : kDecOffNone);
+#pragma unroll
+    for (int f = 0; f < FR; ++f)
+      cw[st][f] = buf_load16(rc, live ? cb[f] + 64u * KS * t : kDecOffNone);
     if constexpr (!XLDS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)   // block i / 2, step i % 2
         xv[st][i] = buf_load16(
-            rx, live ? xb + 256u * kDecKSlots * t + 128u * (i >> 1) + 16u * (i & 1) : kDecOffNone);
+            rx, live ? xb + 256u * KS * t + 128u * (i >> 1) + 16u * (i & 1) : kDecOffNone);
     }
   };
 #pragma unroll
@@ -253,54 +262,66 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   const int xrow = K32 + kDecXPad;
   const uint16_t* xlane = li < M ? xs + li * xrow + xo0 : xs + M * xrow + xo0;
   const int xstep = li < M ? 128 : 0;
-  const float* clane = csc + 16 * p + 4 * g;   // scales of the lane's output rows
+  const float* clane = csc + 4 * g;   // + 16 fragment: scales of the lane's output rows
   // Table addresses: the lane's copy offset in byte 0, entry in byte 1.  The
   // kernel declares no static LDS, so the dynamic block, and the table at its
   // start, begins at LDS address 0 and the address needs no base added.
   const uint32_t ta = static_cast<uint32_t>(lane) << 2;
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[FR];
+#pragma unroll
+  for (int f = 0; f < FR; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
   // All LDS reads of a chunk (scales, table lookups, X) are issued before any
   // of their products, so one LDS round trip serves the chunk's MFMAs.
   auto compute = [&](int t, int st) {
-    const int c = kw + kDecKSlots * t;
-    // Regroup: dwords 0, 1 of lanes 0-31 and 2, 3 of lanes 32-63 stay; the
-    // others trade places across the two halves.  After it, dwords 0, 1 hold
-    // codes of the first block and 2, 3 of the second, in every lane.
-    uint32_t d[4] = {cw[st].x, cw[st].y, cw[st].z, cw[st].w};
+    const int c = kw + KS * t;
+    u32x4 a[FR][4], xf[4];
+    f32x4 cA[FR], cB[FR];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(d[u], d[2 + u], false, false);
-      d[u] = sw[0];
-      d[2 + u] = sw[1];
+    for (int f = 0; f < FR; ++f) {
+      // Regroup: dwords 0, 1 of lanes 0-31 and 2, 3 of lanes 32-63 stay; the
+      // others trade places across the two halves.  After it, dwords 0, 1
+      // hold codes of the first block and 2, 3 of the second, in every lane.
+      uint32_t d[4] = {cw[st][f].x, cw[st][f].y, cw[st][f].z, cw[st][f].w};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(d[u], d[2 + u], false, false);
+        d[u] = sw[0];
+        d[2 + u] = sw[1];
+      }
+      cA[f] = *reinterpret_cast<const f32x4*>(clane + 16 * frag(f) + (2 * c) * ROWS);
+      cB[f] = *reinterpret_cast<const f32x4*>(clane + 16 * frag(f) + (2 * c + 1) * ROWS);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[f][i][0] = rep_bf16_lookup<0>(ta, d[i]);
+        a[f][i][1] = rep_bf16_lookup<1>(ta, d[i]);
+        a[f][i][2] = rep_bf16_lookup<2>(ta, d[i]);
+        a[f][i][3] = rep_bf16_lookup<3>(ta, d[i]);
+      }
     }
-    const f32x4 cA = *reinterpret_cast<const f32x4*>(clane + (2 * c) * ROWS);
-    const f32x4 cB = *reinterpret_cast<const f32x4*>(clane + (2 * c + 1) * ROWS);
-    u32x4 a[4], xf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      a[i][0] = rep_bf16_lookup<0>(ta, d[i]);
-      a[i][1] = rep_bf16_lookup<1>(ta, d[i]);
-      a[i][2] = rep_bf16_lookup<2>(ta, d[i]);
-      a[i][3] = rep_bf16_lookup<3>(ta, d[i]);
       if constexpr (XLDS)
         xf[i] = *reinterpret_cast<const u32x4*>(xlane + c * xstep + 64 * (i >> 1) + 8 * (i & 1));
       else
         xf[i] = xv[st][i];
     }
     __builtin_amdgcn_sched_barrier(0);
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 pA = mfma16(a[0], xf[0], zero);
-    pA = mfma16(a[1], xf[1], pA);
-    f32x4 pB = mfma16(a[2], xf[2], zero);
-    pB = mfma16(a[3], xf[3], pB);
     // (the second block of a chunk past K, when K % 128 == 64, is dropped
     // rather than scaled by zero: its products may hold anything)
     const bool second = 2 * c + 1 < KB;   // wave-uniform
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[j] = __builtin_fmaf(cA[j], pA[j], acc[j]);
-      if (second) acc[j] = __builtin_fmaf(cB[j], pB[j], acc[j]);
+    for (int f = 0; f < FR; ++f) {
+      f32x4 pA = mfma16(a[f][0], xf[0], zero);
+      pA = mfma16(a[f][1], xf[1], pA);
+      f32x4 pB = mfma16(a[f][2], xf[2], zero);
+      pB = mfma16(a[f][3], xf[3], pB);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[f][j] = __builtin_fmaf(cA[f][j], pA[j], acc[f][j]);
+        if (second) acc[f][j] = __builtin_fmaf(cB[f][j], pB[j], acc[f][j]);
+      }
     }
   };
   __syncthreads();
@@ -314,14 +335,18 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   }
 
   // The LoRA step's B operand, B[j .. j+7, n] for the lane's row n.
-  u32x4 bw = {0, 0, 0, 0};
-  if (kw < nsteps) {
-    const int j = 32 * kw + 8 * g;
+  u32x4 bw[FR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = j + 2 * i < r ? bst[(j + 2 * i) * ROWS + 16 * p + li] : 0u;
-      const uint32_t hi = j + 2 * i + 1 < r ? bst[(j + 2 * i + 1) * ROWS + 16 * p + li] : 0u;
-      bw[i] = lo | (hi << 16);
+  for (int f = 0; f < FR; ++f) {
+    bw[f] = u32x4{0, 0, 0, 0};
+    if (kw < nsteps) {
+      const int j = 32 * kw + 8 * g, row = 16 * frag(f) + li;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = j + 2 * i < r ? bst[(j + 2 * i) * ROWS + row] : 0u;
+        const uint32_t hi = j + 2 * i + 1 < r ? bst[(j + 2 * i + 1) * ROWS + row] : 0u;
+        bw[f][i] = lo | (hi << 16);
+      }
     }
   }
 
@@ -361,17 +386,28 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     uint32_t h[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) split_bf16x2(v[2 * i], v[2 * i + 1], h[i], l[i]);
-    acc = mfma16(bw, u32x4{h[0], h[1], h[2], h[3]}, acc);
-    acc = mfma16(bw, u32x4{l[0], l[1], l[2], l[3]}, acc);
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
+      acc[f] = mfma16(bw[f], u32x4{h[0], h[1], h[2], h[3]}, acc[f]);
+      acc[f] = mfma16(bw[f], u32x4{l[0], l[1], l[2], l[3]}, acc[f]);
+    }
   }
 
-  red[wave * 64 + lane] = acc;   // the block scales and X are no longer read
-  __syncthreads();
-  if (kw == 0) {
-    f32x4 t = red[(p * kDecKSlots) * 64 + lane];
+  // the block scales and X are no longer read: red [wave][FR][64]
 #pragma unroll
-    for (int w = 1; w < kDecKSlots; ++w) t += red[(p * kDecKSlots + w) * 64 + lane];
-    const int64_t nout = n0 + 16 * p + 4 * g;   // 4 consecutive outputs of token li
+  for (int f = 0; f < FR; ++f) red[(wave * FR + f) * 64 + lane] = acc[f];
+  __syncthreads();
+  // fragment po is summed over its KS slots by one wave: the first wave of
+  // the fragment (FR = 1), or wave po (FR = 2)
+  const int po = FR == 1 ? p : wave;
+  if (FR == 1 ? kw == 0 : wave < kDecR) {
+    auto part = [&](int w) {   // slot w of fragment po
+      return FR == 1 ? red[(po * kDecKSlots + w) * 64 + lane] : red[(w * FR + po) * 64 + lane];
+    };
+    f32x4 t = part(0);
+#pragma unroll
+    for (int w = 1; w < KS; ++w) t += part(w);
+    const int64_t nout = n0 + 16 * po + 4 * g;   // 4 consecutive outputs of token li
     if (li < M && nout < N) {
       *reinterpret_cast<u32x2*>(Y + (int64_t)li * N + nout) =
           u32x2{pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w)};
@@ -381,20 +417,20 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 
 namespace {
 
-template <int D, int XP>
+template <int D, int XP, int FR>
 hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w, const float* T,
                                  int nz, float* Tout, const uint16_t* B, int r, float s,
                                  uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
   // allow the largest dynamic LDS (once per variant)
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_fwd_decode<D, XP>),
+      reinterpret_cast<const void*>(&k_fwd_decode<D, XP, FR>),
       hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
   if (attr != hipSuccess) return attr;
-  const DecLds L(M, w.K, r, XP > 0);
+  const DecLds L(M, w.K, r, XP > 0, FR);
   if (L.total > kDecLdsMax) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>((w.N + kDecRows - 1) / kDecRows);
   const float inv_kb = 1.0f / static_cast<float>(w.K / kBlock);
-  hipLaunchKernelGGL((k_fwd_decode<D, XP>), dim3(grid), dim3(kDecThreads), L.total, stream,
+  hipLaunchKernelGGL((k_fwd_decode<D, XP, FR>), dim3(grid), dim3(kDecThreads), L.total, stream,
                      X, (int)M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, nz, Tout, B,
                      r, s, Y, tb, L.boff, L.toff, L.coff, L.xoff, inv_kb);
   return hipGetLastError();
@@ -422,13 +458,15 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
   if (xbytes <= kDecXLdsBytes && DecLds(M, w.K, r, true).total <= kDecLdsMax) {
     const int64_t per_piece = 16 * kDecThreads;
     if (xbytes <= per_piece)
-      e = launch_decode_variant<2, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+      e = launch_decode_variant<2, 1, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
     else if (xbytes <= 2 * per_piece)
-      e = launch_decode_variant<2, 2>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+      e = launch_decode_variant<2, 2, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
     else
-      e = launch_decode_variant<2, kDecXPieces>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+      e = launch_decode_variant<2, kDecXPieces, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
   } else {
-    e = launch_decode_variant<2, 0>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+    // X from global memory: each wave works on both fragments, so each X
+    // piece it loads serves 32 rows.
+    e = launch_decode_variant<2, 0, 2>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
   }
   prof_end(2, stream);
   return e;
