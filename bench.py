@@ -109,6 +109,7 @@ def run_training(q, torch, steps, warmup, dev, cfg_idx=1):
 
     for _ in range(warmup):
         step()
+    step()   # the eager reference for the graph check (also when warmup is 0)
     torch.cuda.synchronize()
     outs = ("Y", "T", "dX", "dA", "dB")
     eager = [[L[k].clone() for k in outs] for L in layers]
@@ -356,10 +357,10 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
     return out
 
 
-def run_cpu_baseline(train):
+def run_cpu_baseline(train, repeats=3):
     """The oracle (dequantize + forward + backward, float64 products) on a
-    bounded sample of the same workload: all seven linears once at full M
-    (one training step), on this host's cores."""
+    bounded sample of the same workload: all seven linears at full M (one
+    training step), `repeats` times, on this host's cores."""
     import numpy as np
 
     import oracle
@@ -376,12 +377,13 @@ def run_cpu_baseline(train):
         for idx in range(len(cfg.linears)):
             (lin, inp), = list(workloads.config_inputs(1, linears=[idx]))
             codes, e, d, _ = oracle.quantize(inp.W)       # load-time, untimed
-            t0 = time.perf_counter()
-            What = oracle.dequantize(codes, e, d, lin.N, lin.K)
-            oracle.linear_fwd(inp.X, What, inp.A, inp.B, cfg.s)
-            oracle.linear_bwd(inp.dY, inp.X, What, inp.A, inp.B, cfg.s)
-            secs += time.perf_counter() - t0
-            flops += oracle.linear_flops(cfg.M[0], lin.N, lin.K, cfg.r)
+            for _ in range(repeats):
+                t0 = time.perf_counter()
+                What = oracle.dequantize(codes, e, d, lin.N, lin.K)
+                oracle.linear_fwd(inp.X, What, inp.A, inp.B, cfg.s)
+                oracle.linear_bwd(inp.dY, inp.X, What, inp.A, inp.B, cfg.s)
+                secs += time.perf_counter() - t0
+                flops += oracle.linear_flops(cfg.M[0], lin.N, lin.K, cfg.r)
         threads = cores
         if threadpool_info:
             nums = [p.get("num_threads", 0) for p in threadpool_info()
@@ -392,7 +394,7 @@ def run_cpu_baseline(train):
             ctx.__exit__(None, None, None)
     return dict(value=flops / secs / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
                 seconds=secs,
-                sample="one step: all seven linears, M=2048, r=64: oracle dequantize + "
+                sample=f"{repeats} steps: all seven linears, M=2048, r=64: oracle dequantize + "
                        "fwd + bwd (float64 products); load-time quantization untimed")
 
 
