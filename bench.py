@@ -70,6 +70,12 @@ def bf16_dev(bits, dev):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+def percentiles(xs):
+    """p10, median and p90 of a list of per-step times (ms)."""
+    import numpy as np
+    return [float(v) for v in np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])]
+
+
 def run_training(q, torch, steps, warmup, dev, cfg_idx=1):
     """One step = fwd + bwd of the config's seven linears.  Config 3 runs the
     backward as under gradient checkpointing: T is not kept, the backward
@@ -126,11 +132,16 @@ def run_training(q, torch, steps, warmup, dev, cfg_idx=1):
         for k, t in zip(outs, ref):
             if not torch.equal(L[k], t):
                 raise RuntimeError(f"graph replay differs from the eager step ({L['lin'].name}.{k})")
+    # an event after every replay gives the per-step spread (median, p10, p90)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(steps):
+    evs[0].record()
+    for i in range(steps):
         graph.replay()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     del graph
 
     # Kernel durations: the same steps run eagerly with the per-family event
@@ -150,6 +161,7 @@ def run_training(q, torch, steps, warmup, dev, cfg_idx=1):
     fwd_flops = sum(2 * M * L["lin"].K * L["lin"].N + 2 * M * r * L["lin"].N for L in layers)
     dx_flops = sum(2 * M * L["lin"].K * L["lin"].N + 2 * M * r * L["lin"].K for L in layers)
     return dict(layers=layers, M=M, r=r, s=s, ms_step=ms_step, ms_step_eager=ms_step_eager,
+                step_ms_pct=percentiles(per_step),
                 flops_step=flops_step,
                 fam=fam, fwd_flops=fwd_flops, dx_flops=dx_flops, cfg=cfg)
 
@@ -569,6 +581,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": tr["ms_step"],
         "ms_per_step_eager_timed_kernels": tr["ms_step_eager"],
+        "step_ms_p10_p50_p90": tr["step_ms_pct"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

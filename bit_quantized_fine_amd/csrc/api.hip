@@ -289,7 +289,8 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
     // T's partial sums are added up inside the decode kernel (no reduction
     // launch); its workgroup 0 writes T.
     int nz = 0;
-    e = launch_lora_down_partials(X, M, w->K, A, r, ws, &nz, hs);
+    e = launch_lora_down_partials(X, M, w->K, A, r, decode_max_t_partials(M, w->K, r), ws, &nz,
+                                  hs);
     if (e == hipSuccess) e = launch_fwd_decode(X, M, v, ws, nz, T, B, r, s, Y, tables(), hs);
     return hip_status(e);
   }

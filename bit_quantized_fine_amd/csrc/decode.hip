@@ -54,13 +54,16 @@ constexpr int kDecLdsMax = 160 * 1024;         // LDS of one workgroup
 constexpr int kDecXPieces = kDecXLdsBytes / 16 / kDecThreads;   // at most 4 16-byte X pieces a thread
 constexpr int kDecXZero = 256;                 // zero bytes after X (lanes past M read there)
 constexpr int kDecXPad = 8;                    // X rows in LDS are K + 8 elements apart
-// T partial sums (at most kMaxDownPartials of them) are added up by rows of
-// 16 lanes: row h takes the quad (4 ranks of one token) h, its lane z the
-// partials z and z + 16.  M r <= kDecTSumMaxMR keeps that within one quad
-// per row.
-constexpr int kDecTQuads = 2;   // loads per lane (two partials, or 8 values of a final T)
+// T partial sums are added up by rows of 16 lanes: row h takes the quad (4
+// ranks of one token) h, its lane z the partials z + 16 i, i < TQ.  M r <=
+// kDecTSumMaxMR keeps that within one quad per row.  A kernel with X in LDS
+// takes up to 64 partials (TQ = 4); the one reading X from global memory, 32
+// (TQ = 2, registers are short there).  With a final T, the lanes of the
+// LoRA waves use the first two loads for their 8 values.
+constexpr int dec_tq(int fr) { return fr == 1 ? 4 : 2; }
 constexpr int kDecTSumMaxMR = 4 * (kDecThreads / 16);
-static_assert(kMaxDownPartials <= 2 * 16, "two partials per lane of a 16-lane row");
+static_assert(kMaxDownPartials <= dec_tq(1) * 16, "partials per lane of a 16-lane row");
+static_assert(kMaxDownPartials / 2 <= dec_tq(2) * 16, "partials per lane of a 16-lane row");
 // Block constants of the workgroup's rows, read as 8-byte pieces.
 constexpr int kDecEPieces = (kDecRows * kDecMaxK / kBlock / 8 + kDecThreads - 1) / kDecThreads;
 
@@ -160,12 +163,13 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   }
   // T for the LoRA update, used only after the main loop.  With nz > 0, the
   // 16-lane row h sums quad h (4 ranks of one token) over the partials, lane
-  // z loading partials z and z + 16; with nz == 0 T is final and the lanes of
-  // the LoRA waves load their own 8 values of it.
+  // z loading partials z + 16 i; with nz == 0 T is final and the lanes of the
+  // LoRA waves load their own 8 values of it (the first two loads).
   const int nsteps = (r + 31) / 32;
   const int nq = M * r / 4;
   const int hr = tid >> 4, hl = tid & 15;
-  f32x4 tq[kDecTQuads];
+  constexpr int TQ = dec_tq(FR);
+  f32x4 tq[TQ];
   {
     // (one load sequence for both cases: a branch here would make the
     // compiler wait for the loads of one side before those of the other)
@@ -173,9 +177,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const int j = 32 * kw + 8 * g;
     const bool lora_lane = kw < nsteps && li < M && j < r;
 #pragma unroll
-    for (int i = 0; i < kDecTQuads; ++i) {
+    for (int i = 0; i < TQ; ++i) {
       const int z = hl + 16 * i;
-      const bool ok = nz > 0 ? (hr < nq && z < nz) : lora_lane;
+      const bool ok = nz > 0 ? (hr < nq && z < nz) : (lora_lane && i < 2);
       const int idx = nz > 0 ? z * M * r + 4 * hr : li * r + j + 4 * i;
       tq[i] = __builtin_bit_cast(
           f32x4, buf_load16(rt, ok ? static_cast<uint32_t>(idx * 4) : kDecOffNone));
@@ -351,11 +355,12 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   }
 
   // T's partial sums are added after the main loop, off its critical path:
-  // the lane's two partials, then a butterfly over its 16-lane row with DPP
+  // the lane's four partials, then a butterfly over its 16-lane row with DPP
   // moves (xor 1, xor 2, rotate 4, rotate 8), in a fixed order
   // (deterministic).
   if (nz > 0) {
     f32x4 v = tq[0] + tq[1];
+    if constexpr (TQ == 4) v = (tq[0] + tq[1]) + (tq[2] + tq[3]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       v[c] += dpp_f32<0xB1>(v[c]);    // quad_perm [1, 0, 3, 2]
@@ -427,7 +432,7 @@ hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w,
       hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
   if (attr != hipSuccess) return attr;
   const DecLds L(M, w.K, r, XP > 0, FR);
-  if (L.total > kDecLdsMax) return hipErrorInvalidValue;
+  if (L.total > kDecLdsMax || nz > 16 * dec_tq(FR)) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>((w.N + kDecRows - 1) / kDecRows);
   const float inv_kb = 1.0f / static_cast<float>(w.K / kBlock);
   hipLaunchKernelGGL((k_fwd_decode<D, XP, FR>), dim3(grid), dim3(kDecThreads), L.total, stream,
@@ -436,9 +441,19 @@ hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w,
   return hipGetLastError();
 }
 
+bool decode_x_in_lds(int64_t M, int64_t K, int r) {
+  return M * K * 2 <= kDecXLdsBytes && DecLds(M, K, r, true).total <= kDecLdsMax;
+}
+
 }  // namespace
 
 bool decode_fits(int64_t M, int64_t K) { return M <= 16 && K <= kDecMaxK; }
+
+// Up to 64 partials when one token's T is at most 64 values and X sits in LDS
+// (each workgroup reads all nz M r of them), else 32.
+int decode_max_t_partials(int64_t M, int64_t K, int r) {
+  return M * r <= 64 && decode_x_in_lds(M, K, r) ? kMaxDownPartials : kMaxDownPartials / 2;
+}
 
 bool decode_folds_t(int64_t M, int r) {
   return r > 0 && M <= 4 && M * r <= kDecTSumMaxMR;
@@ -454,8 +469,8 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
   // X goes to LDS when it fits next to the rest (M = 1 up to K = 22016 with
   // r <= 64; M = 4 up to K = 8192), in as few 16-byte pieces per thread as it
   // needs; otherwise each wave reads its X pieces from global memory.
-  const int64_t xbytes = M * w.K * 2;
-  if (xbytes <= kDecXLdsBytes && DecLds(M, w.K, r, true).total <= kDecLdsMax) {
+  if (decode_x_in_lds(M, w.K, r)) {
+    const int64_t xbytes = M * w.K * 2;
     const int64_t per_piece = 16 * kDecThreads;
     if (xbytes <= per_piece)
       e = launch_decode_variant<2, 1, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);

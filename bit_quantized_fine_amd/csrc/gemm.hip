@@ -593,7 +593,8 @@ constexpr int RB_X = 128;    // tile of the long dimension
 size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r) {
   if (r <= 0) return 0;
   if (M <= 16)
-    return (size_t)lora_down_partial_count(K) * M * r + rank_ws_floats(17, N, K, r);
+    return (size_t)lora_down_partial_count(K, kMaxDownPartials) * M * r +
+           rank_ws_floats(17, N, K, r);
   const int64_t rt = (r + RB_R - 1) / RB_R;
   const Split t = choose_split(K, rt, (M + RB_X - 1) / RB_X);
   const Split g = choose_split(N, rt, (M + RB_X - 1) / RB_X);
@@ -606,17 +607,18 @@ size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r) {
   return m;
 }
 
-int lora_down_partial_count(int64_t K) {
+int lora_down_partial_count(int64_t K, int maxp) {
   const int64_t slices = (K + LDS_K - 1) / LDS_K;
-  const int64_t spw = (slices + kMaxDownPartials - 1) / kMaxDownPartials;
+  const int64_t spw = (slices + maxp - 1) / maxp;
   return static_cast<int>((slices + spw - 1) / spw);
 }
 
 hipError_t launch_lora_down_partials(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A,
-                                     int r, float* ws, int* nz, hipStream_t stream) {
+                                     int r, int maxp, float* ws, int* nz, hipStream_t stream) {
+  if (maxp < 1 || maxp > kMaxDownPartials) return hipErrorInvalidValue;
   const int64_t slices = (K + LDS_K - 1) / LDS_K;
-  const int spw = static_cast<int>((slices + kMaxDownPartials - 1) / kMaxDownPartials);
-  *nz = lora_down_partial_count(K);
+  const int spw = static_cast<int>((slices + maxp - 1) / maxp);
+  *nz = lora_down_partial_count(K, maxp);
   prof_begin(4, stream);
   hipLaunchKernelGGL(k_lora_down_small, dim3(*nz), dim3(256), 0, stream, X, (int)M, K, A, r, spw,
                      ws);
@@ -628,7 +630,7 @@ hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint1
                             int r, float* T, float* ws, hipStream_t stream) {
   if (M <= 16) {
     int nz = 0;
-    hipError_t e = launch_lora_down_partials(X, M, K, A, r, ws, &nz, stream);
+    hipError_t e = launch_lora_down_partials(X, M, K, A, r, kMaxDownPartials / 2, ws, &nz, stream);
     if (e == hipSuccess) {
       prof_begin(4, stream);
       e = reduce<false>(ws, nz, M * r, 1.f, T, stream);

@@ -57,12 +57,14 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
 // Rank-r products with a split reduction; partials go to `ws`.
 size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r);
 
-// Few-token LoRA down-projection: at most kMaxDownPartials fp32 partial sums
-// [nz][M][r] of T = X . A go to ws (nz returned); M <= 16.
-constexpr int kMaxDownPartials = 32;
-int lora_down_partial_count(int64_t K);
+// Few-token LoRA down-projection: nz <= maxp fp32 partial sums [nz][M][r]
+// of T = X . A go to ws (nz returned); M <= 16, maxp <= kMaxDownPartials.
+constexpr int kMaxDownPartials = 64;
+int lora_down_partial_count(int64_t K, int maxp);
 hipError_t launch_lora_down_partials(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A,
-                                     int r, float* ws, int* nz, hipStream_t stream);
+                                     int r, int maxp, float* ws, int* nz, hipStream_t stream);
+// The most T partial sums the decode kernel chosen for (M, K, r) adds up.
+int decode_max_t_partials(int64_t M, int64_t K, int r);
 
 // T[M,r] = X . A (fp32 out).
 hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K,

@@ -57,7 +57,9 @@ FWD_CASES = [
     (16, 1000, 64 * 33, 64, 0.25),   # K with a half chunk; X read from global memory
     (1, 232, 64 * 33, 32, 0.5),      # K with a half chunk; X staged in LDS
     (4, 96, 16384, 64, 0.25),        # T folded, X too large for LDS
-    (2, 64, 16384, 8, 0.5),          # X of exactly the LDS staging limit (64 KB)
+    (2, 64, 16384, 8, 0.5),          # X of exactly the LDS staging limit (64 KB); 64 T partials
+    (1, 96, 16384 + 64 * 5, 64, 0.25),   # 33 T partial sums, ragged last 256-k slice
+    (1, 64, 32768, 64, 0.5),         # one token, X from global memory: at most 32 partials
     (4, 96, 1024, 256, 0.25),        # M * r too large to fold T into the decode kernel
     (2, 64, 32768 + 64, 8, 0.5),     # K beyond the decode kernel: GEMM path at M = 2
     (17, 1024, 1024, 16, 1.0),       # first GEMM size
