@@ -76,19 +76,19 @@ def percentiles(xs):
     return [float(v) for v in np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])]
 
 
-def run_training(q, torch, steps, warmup, dev, cfg_idx=1):
-    """One step = fwd + bwd of the config's seven linears.  Config 3 runs the
-    backward as under gradient checkpointing: T is not kept, the backward
-    recomputes it (and dequantizes W again, as every backward does)."""
+def run_training(q, torch, steps, warmup, dev, key="llama7b"):
+    """One step = fwd + bwd of the workload's seven linears.  The 33B workload
+    runs the backward as under gradient checkpointing: T is not kept, the
+    backward recomputes it (and dequantizes W again, as every backward does)."""
     import numpy as np
 
     import workloads
-    cfg = workloads.CONFIGS[cfg_idx]
+    cfg = workloads.WORKLOADS[key]
     M, r, s = cfg.M[0], cfg.r, cfg.s
-    recompute = cfg_idx == 3
+    recompute = key == "llama33b_recompute"
     layers = []
     t0 = time.time()
-    for lin, inp in workloads.config_inputs(cfg_idx):
+    for lin, inp in workloads.workload_inputs(key):
         w = q.qlora_nf4_quantize(torch.from_numpy(inp.W).to(dev))
         L = dict(lin=lin, w=w, X=bf16_dev(inp.X, dev), A=bf16_dev(inp.A, dev),
                  B=bf16_dev(inp.B, dev), dY=bf16_dev(inp.dY, dev))
@@ -176,7 +176,7 @@ def run_stack(q, torch, dev, steps=2, warmup=1):
     chain in reverse.  Also one decode token (M = 1, forward only) through
     the whole chain, so the 33 GB of codes stream from HBM once per token."""
     import workloads
-    cfg = workloads.CONFIGS[4]
+    cfg = workloads.WORKLOADS["stack_65b"]
     M, r, s = cfg.M[0], cfg.r, cfg.s
     t0 = time.time()
     lins = []
@@ -281,7 +281,7 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
     a graph (the calls allocate nothing and record no memsets) and replayed;
     the eager per-call time, host launch path included, is reported too."""
     import workloads
-    cfg = workloads.CONFIGS[2]
+    cfg = workloads.WORKLOADS["decode_65b"]
     r, s = cfg.r, cfg.s
     g = torch.Generator(device=dev)
     g.manual_seed(2000)
@@ -382,12 +382,12 @@ def run_cpu_baseline(train, repeats=3):
     except Exception:  # pragma: no cover
         threadpool_info = threadpool_limits = None
     cores = len(os.sched_getaffinity(0))
-    cfg = workloads.CONFIGS[1]
+    cfg = workloads.WORKLOADS["llama7b"]
     flops, secs = 0, 0.0
     ctx = threadpool_limits(cores) if threadpool_limits else None
     try:
         for idx in range(len(cfg.linears)):
-            (lin, inp), = list(workloads.config_inputs(1, linears=[idx]))
+            (lin, inp), = list(workloads.workload_inputs("llama7b", linears=[idx]))
             codes, e, d, _ = oracle.quantize(inp.W)       # load-time, untimed
             for _ in range(repeats):
                 t0 = time.perf_counter()
@@ -473,10 +473,12 @@ def main():
                          "numbers (for profiling it on its own)")
     ap.add_argument("--decode-reps", type=int, default=20,
                     help="graph replays per shape in the decode leg")
-    ap.add_argument("--config", type=int, default=1, choices=(1, 3, 4),
-                    help="1: the headline (LLaMA-7B linears, M=2048); 3: the 33B layer at "
-                         "M=4096 with recompute backward; 4: the 65B stack of 560 linears "
-                         "resident on the GPU (training step and one decode token)")
+    ap.add_argument("--workload", default="llama7b",
+                    choices=("llama7b", "llama33b_recompute", "stack_65b"),
+                    help="llama7b: the headline (LLaMA-7B linears, M=2048); "
+                         "llama33b_recompute: the 33B layer at M=4096 with recompute backward; "
+                         "stack_65b: the 65B stack of 560 linears resident on the GPU (training "
+                         "step and one decode token)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg) of this many MiB before "
                          "the step, as the yardstick for rocprofv3 FETCH_SIZE/WRITE_SIZE")
@@ -518,7 +520,7 @@ def main():
                           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
                           "decode": dec}), flush=True)
         return
-    if args.config == 4:
+    if args.workload == "stack_65b":
         st = run_stack(q, torch, dev)
         log(f"65B stack step: {st['ms_step']:.1f} ms, {st['tflops']:.1f} TFLOP/s; one decode token "
             f"through all 560 linears: {st['ms_token']:.2f} ms, {st['token_gbs']:.0f} GB/s")
@@ -536,7 +538,7 @@ def main():
         }), flush=True)
         return
 
-    tr = run_training(q, torch, args.steps, args.warmup, dev, cfg_idx=args.config)
+    tr = run_training(q, torch, args.steps, args.warmup, dev, key=args.workload)
     value = tr["flops_step"] / (tr["ms_step"] * 1e-3) / 1e12
     log(f"train step: {tr['ms_step']:.3f} ms ({tr['ms_step_eager']:.3f} ms eager with the kernel "
         f"timer on), {value:.1f} TFLOP/s; kernels: {tr['fam']}")
@@ -590,11 +592,11 @@ def main():
         "config": {
             "workload": ("LLaMA-7B-shaped QLoRA linears q,k,v,o [4096x4096], gate,up "
                          "[11008x4096], down [4096x11008]; NF4 base (block 64, DQ 256); "
-                         "fwd + bwd (dX, dA, dB)") if args.config == 1 else
+                         "fwd + bwd (dX, dA, dB)") if args.workload == "llama7b" else
                         ("33B-shaped QLoRA linears q,k,v,o [6656x6656], gate,up "
                          "[17920x6656], down [6656x17920]; NF4 base; fwd + recompute bwd"),
-            "global_batch": cfg.M[0], "seq_len": 512 if args.config == 1 else 2048,
-            "batch": 4 if args.config == 1 else 2, "tokens": cfg.M[0],
+            "global_batch": cfg.M[0], "seq_len": 512 if args.workload == "llama7b" else 2048,
+            "batch": 4 if args.workload == "llama7b" else 2, "tokens": cfg.M[0],
             "rank": cfg.r, "lora_scale": cfg.s, "parallelism": "single GPU",
         },
         "roofline": roofline,

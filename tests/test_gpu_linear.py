@@ -183,14 +183,14 @@ def test_bwd_without_dx():
 
 
 # ---------------------------------------------------------------------------
-# Full-size configurations
+# Full-size workloads
 # ---------------------------------------------------------------------------
 
-def _full_linear_check(cfg_idx, lin_idx, M=None, rows=None):
-    cfg = workloads.CONFIGS[cfg_idx]
-    (lin, inp), = list(workloads.config_inputs(cfg_idx, M=M, linears=[lin_idx]))
+def _full_linear_check(key, lin_idx, M=None, rows=None):
+    cfg = workloads.WORKLOADS[key]
+    (lin, inp), = list(workloads.workload_inputs(key, M=M, linears=[lin_idx]))
     m = inp.X.shape[0]
-    say(f"config {cfg_idx} linear {lin.name} N={lin.N} K={lin.K} M={m}")
+    say(f"{key} linear {lin.name} N={lin.N} K={lin.K} M={m}")
     w = q.qlora_nf4_quantize(f32(inp.W))
     X, A, B, dY = bf16(inp.X), bf16(inp.A), bf16(inp.B), bf16(inp.dY)
     Y, T = q.qlora_linear_fwd(X, w, A, B, cfg.s)
@@ -210,19 +210,20 @@ def _full_linear_check(cfg_idx, lin_idx, M=None, rows=None):
 
 
 @pytest.mark.parametrize("lin_idx", [0, 4, 6])
-def test_config1_full_size(lin_idx):
+def test_llama7b_full_size(lin_idx):
     """LLaMA-7B linears at M=2048 (q, gate, down shapes), compared in full."""
     need_gpu()
-    _full_linear_check(1, lin_idx)
+    _full_linear_check("llama7b", lin_idx)
 
 
 @pytest.mark.parametrize("lin_idx,M", [(0, 1), (1, 4), (2, 16), (2, 1)])
-def test_config2_decode_full_size(lin_idx, M):
+def test_decode_65b_full_size(lin_idx, M):
     """65B-shaped decode linears at M in {1, 4, 16}, compared in full."""
     need_gpu()
-    cfg = workloads.CONFIGS[2]
-    (lin, inp), = list(workloads.config_inputs(2, M=M, linears=[lin_idx], with_grad=False))
-    say(f"config 2 {lin.name} N={lin.N} K={lin.K} M={M}")
+    cfg = workloads.WORKLOADS["decode_65b"]
+    (lin, inp), = list(workloads.workload_inputs("decode_65b", M=M, linears=[lin_idx],
+                                                 with_grad=False))
+    say(f"decode_65b {lin.name} N={lin.N} K={lin.K} M={M}")
     w = q.qlora_nf4_quantize(f32(inp.W))
     Y, T = q.qlora_linear_fwd(bf16(inp.X), w, bf16(inp.A), bf16(inp.B), cfg.s)
     torch.cuda.synchronize()
@@ -234,13 +235,13 @@ def test_config2_decode_full_size(lin_idx, M):
 
 
 @pytest.mark.parametrize("lin_idx", [0, 6])
-def test_config3_full_size_recompute(lin_idx):
+def test_llama33b_full_size_recompute(lin_idx):
     """33B-shaped linears at M=4096 with the recompute (checkpointing) bwd:
     sampled rows of Y and dX, full dA and dB."""
     need_gpu()
-    cfg = workloads.CONFIGS[3]
-    (lin, inp), = list(workloads.config_inputs(3, linears=[lin_idx]))
-    say(f"config 3 {lin.name} N={lin.N} K={lin.K} M={inp.X.shape[0]}")
+    cfg = workloads.WORKLOADS["llama33b_recompute"]
+    (lin, inp), = list(workloads.workload_inputs("llama33b_recompute", linears=[lin_idx]))
+    say(f"llama33b_recompute {lin.name} N={lin.N} K={lin.K} M={inp.X.shape[0]}")
     w = q.qlora_nf4_quantize(f32(inp.W))
     X, A, B, dY = bf16(inp.X), bf16(inp.A), bf16(inp.B), bf16(inp.dY)
     Y, _ = q.qlora_linear_fwd(X, w, A, B, cfg.s)
@@ -281,12 +282,12 @@ def test_workspace_contents_do_not_matter(fill):
     assert_close("T", T1, Tr)
 
 
-def _device_config4_linear(idx, M):
+def _device_stack_65b_linear(idx, M):
     """Linear idx of the 65B stack, drawn on the device as the stack is
     (seeds 4000 + idx for W, 5000 + idx for A and B), with X and dY drawn on
     the device too; returns device tensors and their host copies (the same
     bytes on both sides)."""
-    cfg = workloads.CONFIGS[4]
+    cfg = workloads.WORKLOADS["stack_65b"]
     lin = cfg.linears[idx]
     W = workloads.device_weight(torch, dev(), lin.N, lin.K, seed=4000 + idx)
     A, B = workloads.device_adapters(torch, dev(), lin.N, lin.K, cfg.r, seed=5000 + idx)
@@ -296,13 +297,13 @@ def _device_config4_linear(idx, M):
     return cfg, lin, W, A, B, X, dY, host
 
 
-def test_config4_first_linear():
+def test_stack_65b_first_linear():
     """65B stack, layer 0's q projection (8192 x 8192, M = 2048) drawn on the
     device: codes and constants in full, sampled rows of Y and dX, full dA
     and dB."""
     need_gpu()
-    say("config 4 linear 0 (q, 8192x8192), M=2048")
-    cfg, lin, W, A, B, X, dY, h = _device_config4_linear(0, 2048)
+    say("stack_65b linear 0 (q, 8192x8192), M=2048")
+    cfg, lin, W, A, B, X, dY, h = _device_stack_65b_linear(0, 2048)
     w = q.qlora_nf4_quantize(W)
     Y, T = q.qlora_linear_fwd(X, w, A, B, cfg.s)
     dX, dA, dB = q.qlora_linear_bwd(dY, X, w, A, B, cfg.s, T=T)
@@ -322,15 +323,15 @@ def test_config4_first_linear():
     assert_close("dB", dB.float().cpu().numpy(), dBr)
 
 
-def test_config4_last_linear_row_groups():
+def test_stack_65b_last_linear_row_groups():
     """65B stack, layer 79's down projection (8192 x 22016, M = 2048): the
     first and last 32 rows (43 whole groups of 256 block constants each,
     so the oracle can quantize them alone) bit-exact, Y on those rows for
     sampled tokens, full dA, and dB on those rows' columns."""
     need_gpu()
     idx = 559
-    say("config 4 linear 559 (down, 8192x22016), M=2048")
-    cfg, lin, W, A, B, X, dY, h = _device_config4_linear(idx, 2048)
+    say("stack_65b linear 559 (down, 8192x22016), M=2048")
+    cfg, lin, W, A, B, X, dY, h = _device_stack_65b_linear(idx, 2048)
     assert lin.name == "down" and (32 * lin.K // 64) % 256 == 0
     w = q.qlora_nf4_quantize(W)
     Y, T = q.qlora_linear_fwd(X, w, A, B, cfg.s)

@@ -45,10 +45,10 @@ def test_quantize_dequantize_bit_exact(N, K):
     np.testing.assert_array_equal(bits(deq), oracle.dequantize(*ref, N, K))
 
 
-def test_parity_config_weight_bit_exact():
+def test_parity_1k_weight_bit_exact():
     need_gpu()
-    say("config 0 weight, seeded recipe")
-    (lin, inp), = list(workloads.config_inputs(0))
+    say("parity_1k weight, seeded recipe")
+    (lin, inp), = list(workloads.workload_inputs("parity_1k"))
     w, ref = _quantize_both(inp.W)
     _assert_quant_equal(w, ref)
     np.testing.assert_array_equal(bits(q.qlora_nf4_dequantize(w)),

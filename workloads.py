@@ -5,9 +5,11 @@ arithmetic.  Both the oracle-side tests and the GPU-side tests and benchmark
 take their inputs from here, so both sides see the same bytes.
 
 Recipe (stated once, used everywhere):
-  * linear j of config i draws from numpy.random.default_rng([seed, j]) with
-    seed = i unless a test picks another seed (linears are numbered in the
-    order q, k, v, o, gate, up, down);
+  * linear j of a workload draws from numpy.random.default_rng([seed, j]),
+    with the workload's own seed (0 for the 1024x1024 parity linear, 1 for
+    the LLaMA-7B linears, 2 for the 65B decode shapes, 3 for the 33B
+    linears) unless a test picks another seed; linears are numbered in the
+    order q, k, v, o, gate, up, down;
   * per linear the draws are, in this order:
       W   float32 [N, K], standard normal x 0.02
       an outlier mask, uniform(0,1) < 0.001, and W *= 10 on the mask
@@ -35,8 +37,9 @@ class Linear:
 
 
 @dataclass(frozen=True)
-class Config:
-    idx: int
+class Workload:
+    key: str
+    seed: int
     name: str
     linears: Tuple[Linear, ...]
     M: Tuple[int, ...]
@@ -56,19 +59,20 @@ def _llama_layer(hidden: int, ffn: int) -> Tuple[Linear, ...]:
             Linear("down", hidden, ffn))
 
 
-CONFIGS = {
-    0: Config(0, "single linear 1024x1024, M=16, r=16 (parity case)",
-              (Linear("w", 1024, 1024),), (16,), 16, 16.0),
-    1: Config(1, "LLaMA-7B layer linears, M=2048 tokens, r=64",
-              _llama_layer(4096, 11008), (2048,), 64, 16.0),
-    2: Config(2, "65B-shaped decode sweep, M in {1,4,16}, r=64",
-              (Linear("qkvo", 8192, 8192), Linear("up", 22016, 8192),
-               Linear("down", 8192, 22016)), (1, 4, 16), 64, 16.0,
-              "alpha not given for this sweep; alpha=16 assumed (s=0.25)"),
-    3: Config(3, "33B-shaped layer linears, M=4096 tokens, r=64, recompute bwd",
-              _llama_layer(6656, 17920), (4096,), 64, 16.0),
-    4: Config(4, "65B-shaped stack, 80 layers x 7 linears, M=2048, r=64",
-              _llama_layer(8192, 22016) * 80, (2048,), 64, 16.0),
+WORKLOADS = {
+    "parity_1k": Workload("parity_1k", 0, "single linear 1024x1024, M=16, r=16 (parity case)",
+                          (Linear("w", 1024, 1024),), (16,), 16, 16.0),
+    "llama7b": Workload("llama7b", 1, "LLaMA-7B layer linears, M=2048 tokens, r=64",
+                        _llama_layer(4096, 11008), (2048,), 64, 16.0),
+    "decode_65b": Workload("decode_65b", 2, "65B-shaped decode sweep, M in {1,4,16}, r=64",
+                           (Linear("qkvo", 8192, 8192), Linear("up", 22016, 8192),
+                            Linear("down", 8192, 22016)), (1, 4, 16), 64, 16.0,
+                           "alpha not given for this sweep; alpha=16 assumed (s=0.25)"),
+    "llama33b_recompute": Workload("llama33b_recompute", 3,
+                                   "33B-shaped layer linears, M=4096 tokens, r=64, "
+                                   "recompute bwd", _llama_layer(6656, 17920), (4096,), 64, 16.0),
+    "stack_65b": Workload("stack_65b", 4, "65B-shaped stack, 80 layers x 7 linears, M=2048, r=64",
+                          _llama_layer(8192, 22016) * 80, (2048,), 64, 16.0),
 }
 
 
@@ -108,28 +112,28 @@ def draw_linear(rng, N: int, K: int, M: int, r: int, b_std: float = 0.01,
     return LinearInputs(W, X, A, B, dY)
 
 
-def linear_rng(cfg_idx: int, lin_idx: int, seed: int = None):
-    return np.random.default_rng([cfg_idx if seed is None else seed, lin_idx])
+def linear_rng(wl_seed: int, lin_idx: int, seed: int = None):
+    return np.random.default_rng([wl_seed if seed is None else seed, lin_idx])
 
 
-def config_inputs(cfg_idx: int, M: int = None, seed: int = None,
-                  linears: List[int] = None, with_grad: bool = True):
-    """Yield (Linear, LinearInputs) for the linears of a config, in order.
+def workload_inputs(key: str, M: int = None, seed: int = None,
+                    linears: List[int] = None, with_grad: bool = True):
+    """Yield (Linear, LinearInputs) for the linears of a workload, in order.
 
     Each linear has its own generator, so a subset yields the same bytes as
-    the full config for those linears.
+    the full workload for those linears.
     """
-    cfg = CONFIGS[cfg_idx]
-    m = cfg.M[0] if M is None else M
-    idxs = range(len(cfg.linears)) if linears is None else linears
+    wl = WORKLOADS[key]
+    m = wl.M[0] if M is None else M
+    idxs = range(len(wl.linears)) if linears is None else linears
     for i in idxs:
-        lin = cfg.linears[i]
-        yield lin, draw_linear(linear_rng(cfg_idx, i, seed), lin.N, lin.K, m, cfg.r,
+        lin = wl.linears[i]
+        yield lin, draw_linear(linear_rng(wl.seed, i, seed), lin.N, lin.K, m, wl.r,
                                with_grad=with_grad)
 
 
 def device_weight(torch, dev, N: int, K: int, seed: int):
-    """Config 4's weights, drawn on the device (the 65B stack is too large
+    """The 65B stack's weights, drawn on the device (the 65B stack is too large
     to draw on the host): torch.Generator(device).manual_seed(seed), W =
     standard normal x 0.02, outliers (uniform < 0.001) x 10, float32 [N, K]."""
     g = torch.Generator(device=dev)
