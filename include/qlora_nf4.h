@@ -39,6 +39,9 @@
  *     is enqueued and a nonzero qlora_status is returned.  A failed kernel
  *     launch returns QLORA_ERR_HIP.  Faults inside kernels surface at the
  *     caller's next synchronisation.
+ *   - A workspace is scratch for the duration of one call: calls that may
+ *     run concurrently (on different streams) need separate workspaces, and
+ *     outputs must not overlap inputs or the workspace.
  *   - The NF4 weight buffers are read-only for fwd/bwd: the base is frozen
  *     ("The Quantization Layer" of "QLoRA: Quantized Low Rank Adaptation at
  *     Extreme Scale").
