@@ -67,6 +67,10 @@ FWD_CASES = [
     (256, 384, 1024, 256, 0.0625),   # maximum rank
     (129, 136, 64, 8, 2.0),          # single reduction tile
     (520, 264, 192, 40, 0.5),        # rank not a multiple of 32, three token tiles
+    (1, 8, 64, 8, 1.0),              # smallest decode: 8 rows, one block (half a 128-k chunk)
+    (3, 8, 64, 256, 0.5),            # rank above K, decode with a separate T reduction
+    (2048, 8, 64, 8, 1.0),           # GEMM with one 8-row tile and eight token tiles
+    (40, 4104, 128, 16, 0.25),       # N a multiple of 8 only (513 x 8)
 ]
 
 
@@ -90,6 +94,8 @@ def test_fwd_parity(M, N, K, r, s):
     (33, 1000, 64 * 33, 64, 0.25),
     (520, 264, 192, 40, 0.5),        # rank not a multiple of 32, three token tiles
     (64, 8, 64, 8, 1.0),             # one 8-row reduction chunk, a half column tile
+    (1, 8, 64, 8, 1.0),              # one token
+    (3, 4104, 128, 256, 0.5),        # maximum rank, N a multiple of 8 only
 ])
 def test_bwd_parity(M, N, K, r, s):
     need_gpu()
