@@ -363,3 +363,40 @@ def test_stack_65b_last_linear_row_groups():
         assert_close(f"dB[:, {r0}:+32]", dB.float().cpu().numpy()[:, rs], dBr)
     _, dAr, _ = oracle.linear_bwd(h["dY"], h["X"], None, h["A"], h["B"], cfg.s, need_dx=False)
     assert_close("dA", dA.float().cpu().numpy(), dAr)
+
+
+def test_largest_weight_sampled_rows():
+    """The largest weight the API accepts, N x K = 2^32 (131072 x 32768, 2 GB
+    of codes, the largest buffer offsets): codes, constants and Y of the
+    decode path (M = 1) and of the GEMM path (M = 256) on the first, last and
+    32 random rows, against the oracle on those rows alone (a row holds two
+    whole double-quantization groups, so rows quantize independently)."""
+    need_gpu()
+    N, K, r, s = 131072, 32768, 64, 0.25
+    say(f"largest weight {N}x{K}")
+    W = workloads.device_weight(torch, dev(), N, K, seed=8000)
+    w = q.qlora_nf4_quantize(W)
+    rng = np.random.default_rng(8)
+    rows = np.concatenate([np.arange(16), np.sort(rng.choice(np.arange(16, N - 16), 32,
+                                                             replace=False)),
+                           np.arange(N - 16, N)])
+    ridx = torch.from_numpy(rows).to(dev())
+    Wr = W.index_select(0, ridx).cpu().numpy()
+    del W
+    torch.cuda.empty_cache()
+    A, B = workloads.device_adapters(torch, dev(), N, K, r, seed=8001)
+    Ah, Bh = bits(A), bits(B)
+    codes, e, d, _ = oracle.quantize(Wr)
+    np.testing.assert_array_equal(
+        w.codes.view(N, K // 2).index_select(0, ridx).cpu().numpy().reshape(-1), codes)
+    np.testing.assert_array_equal(
+        w.absmax_q.view(N, K // 64).index_select(0, ridx).cpu().numpy().reshape(-1), e)
+    np.testing.assert_array_equal(
+        w.absmax_scale.view(N, 2).index_select(0, ridx).cpu().numpy().reshape(-1), d)
+    What = oracle.dequantize(codes, e, d, len(rows), K)
+    for M in (1, 256):
+        X = workloads.device_activations(torch, dev(), M, K, seed=8002 + M)
+        Y, _ = q.qlora_linear_fwd(X, w, A, B, s)
+        torch.cuda.synchronize()
+        Yr, _ = oracle.linear_fwd(bits(X), What, Ah, Bh[:, rows], s)
+        assert_close(f"Y[M={M}, rows]", Y.float().cpu().numpy()[:, rows], Yr)

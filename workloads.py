@@ -140,8 +140,8 @@ def device_weight(torch, dev, N: int, K: int, seed: int):
     g.manual_seed(seed)
     W = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02
     mask = torch.rand((N, K), generator=g, device=dev) < 0.001
-    W[mask] *= 10.0
-    return W
+    # (where(), not masked indexing: the latter fails beyond 2^31 elements)
+    return torch.where(mask, W * 10.0, W)
 
 
 def device_adapters(torch, dev, N: int, K: int, r: int, seed: int, b_std: float = 0.01):
