@@ -370,7 +370,8 @@ def test_largest_weight_sampled_rows():
     of codes, the largest buffer offsets): codes, constants and Y of the
     decode path (M = 1) and of the GEMM path (M = 256) on the first, last and
     32 random rows, against the oracle on those rows alone (a row holds two
-    whole double-quantization groups, so rows quantize independently)."""
+    whole double-quantization groups, so rows quantize independently); then
+    the backward at M = 256 with dY nonzero only in those rows' columns."""
     need_gpu()
     N, K, r, s = 131072, 32768, 64, 0.25
     say(f"largest weight {N}x{K}")
@@ -396,7 +397,20 @@ def test_largest_weight_sampled_rows():
     What = oracle.dequantize(codes, e, d, len(rows), K)
     for M in (1, 256):
         X = workloads.device_activations(torch, dev(), M, K, seed=8002 + M)
-        Y, _ = q.qlora_linear_fwd(X, w, A, B, s)
+        Y, T = q.qlora_linear_fwd(X, w, A, B, s)
         torch.cuda.synchronize()
         Yr, _ = oracle.linear_fwd(bits(X), What, Ah, Bh[:, rows], s)
         assert_close(f"Y[M={M}, rows]", Y.float().cpu().numpy()[:, rows], Yr)
+    # Backward with dY nonzero only in the sampled rows' columns, so that dX,
+    # dA and those columns of dB depend on the sampled rows alone.
+    dYh = np.zeros((M, N), np.uint16)
+    dYh[:, rows] = workloads.to_bf16_bits(rng.standard_normal((M, len(rows)), dtype=np.float32))
+    dX, dA, dB = q.qlora_linear_bwd(bf16(dYh), X, w, A, B, s, T=T)
+    torch.cuda.synchronize()
+    dXr, dAr, dBr = oracle.linear_bwd(dYh[:, rows], bits(X), What, Ah, Bh[:, rows], s)
+    assert_close("dX", dX.float().cpu().numpy(), dXr)
+    assert_close("dA", dA.float().cpu().numpy(), dAr)
+    dBg = dB.float().cpu().numpy()
+    assert_close("dB[:, rows]", dBg[:, rows], dBr)
+    others = np.setdiff1d(np.arange(N), rows)
+    assert not np.any(dBg[:, others]), "dB nonzero where dY is zero"
