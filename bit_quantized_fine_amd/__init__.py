@@ -102,6 +102,59 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name, shape, dtype):
+    """The C entry points trust their pointers to hold the documented
+    [rows, cols] layout, so tensors are checked here before a call: first
+    dtype, shape and contiguity of every argument, then (_on_gpu) that all
+    of them sit on the same GPU."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(named):
+    """named: (name, tensor or None) pairs; the first tensor's GPU is the one."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _check_weight(w):
+    import torch
+    n_codes, n_blocks = w.N * w.K // 2, w.N * w.K // 64
+    _need(w.codes, "w.codes", (n_codes,), torch.uint8)
+    _need(w.absmax_q, "w.absmax_q", (n_blocks,), torch.uint8)
+    _need(w.absmax_scale, "w.absmax_scale", ((n_blocks + 255) // 256,), torch.float32)
+    return [("w.codes", w.codes), ("w.absmax_q", w.absmax_q),
+            ("w.absmax_scale", w.absmax_scale)]
+
+
+def _check_adapters(A, B, w):
+    import torch
+    if A is None or B is None:
+        if A is not None or B is not None:
+            raise ValueError("A and B go together (both None selects r = 0)")
+        return 0
+    if A.dim() != 2:
+        raise ValueError("A must be [K, r]")
+    r = A.shape[1]
+    _need(A, "A", (w.K, r), torch.bfloat16)
+    _need(B, "B", (r, w.N), torch.bfloat16)
+    return r
+
+
 class NF4Weight(NamedTuple):
     codes: "torch.Tensor"          # uint8 [N*K/2]
     absmax_q: "torch.Tensor"       # uint8 [N*K/64]
@@ -134,7 +187,11 @@ def qlora_nf4_thresholds():
 def qlora_nf4_quantize(W, out: Optional[NF4Weight] = None) -> NF4Weight:
     """Quantize a float32 [N, K] CUDA tensor to NF4 + double-quantized constants."""
     import torch
+    if W.dim() != 2:
+        raise ValueError("W must be [N, K]")
     N, K = W.shape
+    _need(W, "W", (N, K), torch.float32)
+    _on_gpu([("W", W)] + (_check_weight(out) if out is not None else []))
     L = lib()
     if out is None:
         out = NF4Weight(
@@ -151,6 +208,7 @@ def qlora_nf4_quantize(W, out: Optional[NF4Weight] = None) -> NF4Weight:
 def qlora_nf4_dequantize(w: NF4Weight):
     """bf16 [N, K] dequantized copy of an NF4 weight."""
     import torch
+    _on_gpu(_check_weight(w))
     out = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=w.codes.device)
     cw = w._c()
     _check("qlora_nf4_dequantize",
@@ -169,12 +227,25 @@ def qlora_linear_fwd(X, w: NF4Weight, A=None, B=None, s: float = 1.0,
                      Y=None, T=None, workspace=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Y = X . deq(W)^T + s . (X . A) . B.  Returns (Y bf16 [M,N], T fp32 [M,r])."""
     import torch
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
     M = X.shape[0]
-    r = 0 if A is None else A.shape[1]
+    _need(X, "X", (M, w.K), torch.bfloat16)
+    wt = _check_weight(w)
+    r = _check_adapters(A, B, w)
+    if Y is not None:
+        _need(Y, "Y", (M, w.N), torch.bfloat16)
+    if T is not None and r > 0:
+        _need(T, "T", (M, r), torch.float32)
+    if workspace is not None:
+        _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
+    _on_gpu([("X", X)] + wt + [("A", A), ("B", B), ("Y", Y), ("T", T if r > 0 else None),
+                               ("workspace", workspace)])
+    dev = X.device
     if Y is None:
-        Y = torch.empty((M, w.N), dtype=torch.bfloat16, device=X.device)
+        Y = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev)
     if T is None and r > 0:
-        T = torch.empty((M, r), dtype=torch.float32, device=X.device)
+        T = torch.empty((M, r), dtype=torch.float32, device=dev)
     need = lib().qlora_linear_fwd_workspace_bytes(M, w.N, w.K, r)
     if workspace is None or workspace.numel() < need:
         workspace = _ws(need, X.device)
@@ -193,8 +264,27 @@ def qlora_linear_bwd(dY, X, w: NF4Weight, A=None, B=None, s: float = 1.0, T=None
     T is the forward's T = X . A; None recomputes it (gradient checkpointing).
     """
     import torch
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
     M = X.shape[0]
-    r = 0 if A is None else A.shape[1]
+    _need(X, "X", (M, w.K), torch.bfloat16)
+    _need(dY, "dY", (M, w.N), torch.bfloat16)
+    wt = _check_weight(w)
+    r = _check_adapters(A, B, w)
+    if T is not None and r > 0:
+        _need(T, "T", (M, r), torch.float32)
+    if need_dx and dX is not None:
+        _need(dX, "dX", (M, w.K), torch.bfloat16)
+    if r > 0 and dA is not None:
+        _need(dA, "dA", (w.K, r), torch.bfloat16)
+    if r > 0 and dB is not None:
+        _need(dB, "dB", (r, w.N), torch.bfloat16)
+    if workspace is not None:
+        _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
+    _on_gpu([("X", X), ("dY", dY)] + wt +
+            [("A", A), ("B", B), ("T", T if r > 0 else None),
+             ("dX", dX if need_dx else None), ("dA", dA if r > 0 else None),
+             ("dB", dB if r > 0 else None), ("workspace", workspace)])
     dev = X.device
     if need_dx and dX is None:
         dX = torch.empty((M, w.K), dtype=torch.bfloat16, device=dev)

@@ -1,0 +1,70 @@
+"""Host-side checks of the Python binding: tensors that do not match the
+documented layout are refused before any call into the library (the C entry
+points cannot see tensor shapes, only pointers)."""
+import pytest
+import torch
+
+import bit_quantized_fine_amd as q
+
+
+def _weight(N=64, K=128):
+    return q.NF4Weight(torch.zeros(N * K // 2, dtype=torch.uint8),
+                       torch.zeros(N * K // 64, dtype=torch.uint8),
+                       torch.zeros((N * K // 64 + 255) // 256, dtype=torch.float32), N, K)
+
+
+def test_fwd_refuses_wrong_shapes_and_dtypes():
+    w = _weight()
+    X = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        q.qlora_linear_fwd(torch.zeros(4, 127, dtype=torch.bfloat16), w)
+    with pytest.raises(TypeError, match="bfloat16"):
+        q.qlora_linear_fwd(torch.zeros(4, 128, dtype=torch.float32), w)
+    with pytest.raises(ValueError, match="contiguous"):
+        q.qlora_linear_fwd(torch.zeros(128, 4, dtype=torch.bfloat16).t(), w)
+    A = torch.zeros(128, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="together"):
+        q.qlora_linear_fwd(X, w, A, None)
+    # everything in order except the device: refused as a host tensor
+    with pytest.raises(ValueError, match="GPU tensor"):
+        q.qlora_linear_fwd(X, w)
+
+
+def test_fwd_checks_adapters_and_outputs():
+    w = _weight()
+    X = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        q.qlora_linear_fwd(X, w, torch.zeros(128, 8, dtype=torch.bfloat16),
+                           torch.zeros(8, 63, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="shape"):
+        q.qlora_linear_fwd(X, w, torch.zeros(120, 8, dtype=torch.bfloat16),
+                           torch.zeros(8, 64, dtype=torch.bfloat16))
+
+
+def test_weight_buffers_are_checked():
+    w = _weight()
+    bad = w._replace(codes=torch.zeros(10, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="w.codes"):
+        q.qlora_linear_fwd(torch.zeros(4, 128, dtype=torch.bfloat16), bad)
+    bad = w._replace(absmax_scale=torch.zeros(1, dtype=torch.float64))
+    with pytest.raises(TypeError, match="w.absmax_scale"):
+        q.qlora_nf4_dequantize(bad)
+
+
+def test_bwd_refuses_wrong_shapes():
+    w = _weight()
+    X = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dY"):
+        q.qlora_linear_bwd(torch.zeros(4, 63, dtype=torch.bfloat16), X, w)
+    with pytest.raises(ValueError, match="shape"):
+        q.qlora_linear_bwd(torch.zeros(4, 64, dtype=torch.bfloat16), X, w,
+                           torch.zeros(128, 8, dtype=torch.bfloat16),
+                           torch.zeros(8, 64, dtype=torch.bfloat16),
+                           T=torch.zeros(4, 7, dtype=torch.float32))
+
+
+def test_quantize_refuses_wrong_input():
+    with pytest.raises(TypeError, match="float32"):
+        q.qlora_nf4_quantize(torch.zeros(8, 64, dtype=torch.float16))
+    with pytest.raises(ValueError, match=r"\[N, K\]"):
+        q.qlora_nf4_quantize(torch.zeros(8 * 64, dtype=torch.float32))
