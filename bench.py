@@ -76,7 +76,7 @@ def percentiles(xs):
     return [float(v) for v in np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])]
 
 
-def run_training(q, torch, steps, warmup, dev, key="llama7b"):
+def run_training(q, torch, steps, warmup, dev, key="llama7b", M=None):
     """One step = fwd + bwd of the workload's seven linears.  The 33B workload
     runs the backward as under gradient checkpointing: T is not kept, the
     backward recomputes it (and dequantizes W again, as every backward does)."""
@@ -84,11 +84,11 @@ def run_training(q, torch, steps, warmup, dev, key="llama7b"):
 
     import workloads
     cfg = workloads.WORKLOADS[key]
-    M, r, s = cfg.M[0], cfg.r, cfg.s
+    M, r, s = (cfg.M[0] if M is None else M), cfg.r, cfg.s
     recompute = key == "llama33b_recompute"
     layers = []
     t0 = time.time()
-    for lin, inp in workloads.workload_inputs(key):
+    for lin, inp in workloads.workload_inputs(key, M=M):
         w = q.qlora_nf4_quantize(torch.from_numpy(inp.W).to(dev))
         L = dict(lin=lin, w=w, X=bf16_dev(inp.X, dev), A=bf16_dev(inp.A, dev),
                  B=bf16_dev(inp.B, dev), dY=bf16_dev(inp.dY, dev))
@@ -483,6 +483,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the extra step at one GPU's share of 8-way data parallelism "
+                         "(256 of the 2048 tokens)")
     ap.add_argument("--decode-only", action="store_true",
                     help="run only the decode leg (65B shapes, M in {1, 4, 16}) and print its "
                          "numbers (for profiling it on its own)")
@@ -585,6 +588,18 @@ def main():
     if not args.no_decode:
         decode = run_decode(q, torch, dev, reps=args.decode_reps)
 
+    shard = None
+    if args.workload == "llama7b" and not args.no_shard:
+        # extra data point: the same step at the per-GPU share of 8-way data
+        # parallelism over the 2048-token batch (not the headline value)
+        sh = run_training(q, torch, args.steps, args.warmup, dev, key="llama7b", M=256)
+        shard = dict(tokens=256, data_parallel=8, ms_per_step=sh["ms_step"],
+                     tflops=sh["flops_step"] / (sh["ms_step"] * 1e-3) / 1e12,
+                     note="one GPU's share of 8-way data parallelism over the 2048-token "
+                          "batch; the dA/dB all-reduce is not part of it")
+        log(f"dp8 shard (M=256): {sh['ms_step']:.3f} ms per step, {shard['tflops']:.1f} TFLOP/s")
+        del sh
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(tr)
@@ -619,6 +634,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "decode_m1_gbs": None if decode is None else decode["M=1"]["gbs_call"],
+        "dp8_shard": shard,
         "decode": decode,
         "kernels": kernels,
     }

@@ -99,15 +99,25 @@ Nf4View view(const qlora_nf4_weight* w) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
 
+// Forward workspace: the split-reduction partials of T, then (reusing the
+// same bytes once T is final) those of the GEMM when it splits its reduction.
 size_t fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
-  if (r <= 0) return 0;
-  return round_up(rank_ws_floats(M, N, K, r) * sizeof(float), 256);
+  size_t f = r > 0 ? rank_ws_floats(M, N, K, r) : 0;
+  if (!decode_fits(M, K)) {
+    const GemmSplit sp = fwd_gemm_split(M, N, K);
+    if (sp.splits > 1) f = std::max<size_t>(f, (size_t)sp.splits * M * N);
+  }
+  return round_up(f * sizeof(float), 256);
 }
 
+// Backward workspace: G [M][r] and the recomputed T [M][r] (r > 0), then the
+// partials of the rank products, whose bytes the dX GEMM's partials reuse.
 size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
-  if (r <= 0) return 0;
-  const size_t mr = round_up((size_t)M * r * sizeof(float), 256);
-  return 2 * mr + round_up(rank_ws_floats(M, N, K, r) * sizeof(float), 256);
+  const size_t mr = r > 0 ? round_up((size_t)M * r * sizeof(float), 256) : 0;
+  size_t f = r > 0 ? rank_ws_floats(M, N, K, r) : 0;
+  const GemmSplit sp = dx_gemm_split(M, N, K);
+  if (sp.splits > 1) f = std::max<size_t>(f, (size_t)sp.splits * M * K);
+  return 2 * mr + round_up(f * sizeof(float), 256);
 }
 
 // ---------------------------------------------------------------------------
@@ -299,7 +309,7 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
   if (decode)
     e = launch_fwd_decode(X, M, v, T, 0, nullptr, B, r, s, Y, tables(), hs);
   else
-    e = launch_fwd_gemm(X, M, v, T, B, r, s, Y, tables(), hs);
+    e = launch_fwd_gemm(X, M, v, T, B, r, s, Y, ws, tables(), hs);
   return hip_status(e);
 }
 
@@ -325,12 +335,12 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
   const Nf4View v = view(w);
   hipError_t e = hipSuccess;
   float* G = nullptr;
+  char* base = static_cast<char*>(workspace);
+  const size_t mr = r > 0 ? round_up((size_t)M * r * sizeof(float), 256) : 0;
+  float* part = base ? reinterpret_cast<float*>(base + 2 * mr) : nullptr;
   if (r > 0) {
-    char* base = static_cast<char*>(workspace);
-    const size_t mr = round_up((size_t)M * r * sizeof(float), 256);
     G = reinterpret_cast<float*>(base);
     float* Tr = reinterpret_cast<float*>(base + mr);
-    float* part = reinterpret_cast<float*>(base + 2 * mr);
     const float* T = T_saved;
     if (!T) {
       e = launch_lora_down(X, M, w->K, A, r, Tr, part, hs);
@@ -340,7 +350,7 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
     if (e == hipSuccess) e = launch_grad_a(X, M, w->K, G, r, s, dA, part, hs);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
-  if (dX) e = launch_dx_gemm(dY, M, v, G, A, r, s, dX, tables(), hs);
+  if (dX) e = launch_dx_gemm(dY, M, v, G, A, r, s, dX, part, tables(), hs);
   return hip_status(e);
 }
 

@@ -590,6 +590,25 @@ constexpr int RB_X = 128;    // tile of the long dimension
 
 }  // namespace
 
+GemmSplit gemm_split(int64_t tiles, int64_t nchunks) {
+  GemmSplit g{1, static_cast<int>(nchunks)};
+  // Only when the tiles would fill under three quarters of the 256 CUs, and
+  // with at least 8 chunks per split (the partials cost a pass of their own).
+  if (tiles >= 192 || nchunks < 16) return g;
+  const int64_t want = std::min<int64_t>(256 / tiles, nchunks / 8);
+  if (want < 2) return g;
+  int64_t cps = (nchunks + want - 1) / want;
+  cps += cps & 1;   // whole pairs of chunks
+  g.splits = static_cast<int>((nchunks + cps - 1) / cps);
+  g.cps = static_cast<int>(cps);
+  return g;
+}
+
+hipError_t launch_split_reduce_bf16(const float* part, int splits, int64_t count, uint16_t* out,
+                                    hipStream_t stream) {
+  return reduce<true>(part, splits, count, 1.f, out, stream);
+}
+
 size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r) {
   if (r <= 0) return 0;
   if (M <= 16)

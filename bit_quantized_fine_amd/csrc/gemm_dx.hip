@@ -69,7 +69,8 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
     const uint16_t* __restrict__ dY, int64_t M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
     int64_t N, int64_t K, const float* __restrict__ G, const uint16_t* __restrict__ Al,
-    int r, float s, uint16_t* __restrict__ dX, int ptiles, int qtiles, Nf4Tables tb) {
+    int r, float s, uint16_t* __restrict__ dX, int ptiles, int qtiles, int cps,
+    float* __restrict__ part, Nf4Tables tb) {
   // Dynamic LDS only (the level table sits at address 0): the replicated
   // table, two weight tiles, two dY tiles; the table's bytes hold the
   // accumulator exchange after the main loop.
@@ -84,10 +85,16 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
   const int wt = wave % XWT, ks = wave / XWT;
   build_rep_pair_table<XT>(tab, load_levels(tb), tid);
 
-  const int tile = xcd_remap_dx(blockIdx.x, ptiles * qtiles);
+  // With a split reduction (few tiles), workgroup b takes row chunks
+  // [z cps, (z + 1) cps) of its tile and writes fp32 partial sums.
+  const int ntiles = ptiles * qtiles;
+  const int lin = xcd_remap_dx(blockIdx.x, static_cast<int>(gridDim.x));
+  const int z = lin / ntiles, tile = lin - z * ntiles;
   const int qt = tile / ptiles, pt = tile - qt * ptiles;
   const int64_t k0 = (int64_t)pt * XP, q0 = (int64_t)qt * XQ;
-  const int nchunks = static_cast<int>((N + XN - 1) / XN);
+  const int c0 = z * cps;
+  // end of this split's row chunks
+  const int nchunks = min(static_cast<int>((N + XN - 1) / XN), c0 + cps);
   const int KB = static_cast<int>(K / kBlock);
 
   // Buffer descriptors: rows n >= N and tokens m >= M read as zero.
@@ -212,15 +219,15 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
       for (int b = 0; b < XTB; ++b) acc[a][b] = mfma16(af[a], bf[b], acc[a][b]);
   };
 
-  load_codes(0, 0);
-  load_codes(1, 1);
-  load_y(0, 0);
-  load_y(1, 1);
+  load_codes(c0, 0);
+  load_codes(c0 + 1, 1);
+  load_y(c0, 0);
+  load_y(c0 + 1, 1);
   __syncthreads();   // level table
   dequant(0, 0);
   store_y(0, 0);
-  load_codes(2, 0);
-  load_y(2, 0);
+  load_codes(c0 + 2, 0);
+  load_y(c0 + 2, 0);
   __syncthreads();
   // iteration c: read the operands of chunk c from buffers c&1; stage chunk
   // c+1 into buffers (c+1)&1 -- dequantize its codes and store its dY, both
@@ -240,14 +247,15 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
   // load counting sees one path and waits only for the stage it consumes.
   // An odd chunk count adds one pass over a chunk past the end, whose codes,
   // constants and activations all read as zero: it adds zeros.
-  for (int c = 0; c < nchunks; c += 2) {
+  for (int c = c0; c < nchunks; c += 2) {
     iter(c, std::integral_constant<int, 0>{});
     iter(c + 1, std::integral_constant<int, 1>{});
   }
 
-  // LoRA term: extra steps over the rank, 32 at a time, alternating
-  // between the two halves before their accumulators are added.
-  for (int j0 = 32 * ks; j0 < r; j0 += 64) {
+  // LoRA term (the first split only): extra steps over the rank, 32 at a
+  // time, alternating between the two halves before their accumulators are
+  // added.
+  for (int j0 = 32 * ks; z == 0 && j0 < r; j0 += 64) {
     const int j = j0 + 8 * g;
     u32x4 gh[XTB], gl[XTB];
 #pragma unroll
@@ -303,6 +311,7 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
   if (ks != 0) return;
 
   // dX[m, k..k+3] for the lane's 4 consecutive columns k of each subtile
+  // (bf16), or this split's fp32 partial sums part[z][m][k..k+3]
 #pragma unroll
   for (int a = 0; a < XTA; ++a) {
     const int64_t k = k0 + 16 * a + 4 * g;
@@ -311,28 +320,41 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
       const int64_t m = q0 + 64 * wt + 16 * b + li;
       if (m < M && k < K) {
         const f32x4 v = acc[a][b];
-        *reinterpret_cast<u32x2*>(dX + m * K + k) =
-            u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+        if (part) {
+          *reinterpret_cast<f32x4*>(part + ((int64_t)z * M + m) * K + k) = v;
+        } else {
+          *reinterpret_cast<u32x2*>(dX + m * K + k) =
+              u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+        }
       }
     }
   }
 }
 
+GemmSplit dx_gemm_split(int64_t M, int64_t N, int64_t K) {
+  return gemm_split((K + XP - 1) / XP * ((M + XQ - 1) / XQ), (N + XN - 1) / XN);
+}
+
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
                           const float* G, const uint16_t* A, int r, float s,
-                          uint16_t* dX, const Nf4Tables& tb, hipStream_t stream) {
+                          uint16_t* dX, float* part, const Nf4Tables& tb, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_dx_gemm), hipFuncAttributeMaxDynamicSharedMemorySize,
       kDxLds);
   if (attr != hipSuccess) return attr;
   const int ptiles = static_cast<int>((w.K + XP - 1) / XP);
   const int qtiles = static_cast<int>((M + XQ - 1) / XQ);
+  const GemmSplit sp = dx_gemm_split(M, w.N, w.K);
+  if (sp.splits > 1 && !part) return hipErrorInvalidValue;
   prof_begin(1, stream);
-  hipLaunchKernelGGL(k_dx_gemm, dim3(ptiles * qtiles), dim3(XT), kDxLds, stream, dY, M,
-                     w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, G, A, r, s, dX, ptiles,
-                     qtiles, tb);
+  hipLaunchKernelGGL(k_dx_gemm, dim3(ptiles * qtiles * sp.splits), dim3(XT), kDxLds, stream, dY,
+                     M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, G, A, r, s, dX, ptiles,
+                     qtiles, sp.cps, sp.splits > 1 ? part : nullptr, tb);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && sp.splits > 1)
+    e = launch_split_reduce_bf16(part, sp.splits, M * w.K, dX, stream);
   prof_end(1, stream);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace qnf4

@@ -60,7 +60,8 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
     const uint16_t* __restrict__ X, int64_t M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
     int64_t N, int64_t K, const float* __restrict__ T, const uint16_t* __restrict__ Bl,
-    int r, float s, uint16_t* __restrict__ Y, int ptiles, int qtiles, Nf4Tables tb) {
+    int r, float s, uint16_t* __restrict__ Y, int ptiles, int qtiles, int cps,
+    float* __restrict__ part, Nf4Tables tb) {
   // Dynamic LDS only (so the table sits at address 0): the replicated level
   // table, then two A tile buffers; after the main loop the same bytes hold
   // the accumulator exchange and the B^T tile of the LoRA update.
@@ -75,10 +76,15 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   const int wt = wave % GWT, ks = wave / GWT;
   build_rep_pair_table<GT>(tab, load_levels(tb), tid);
 
-  const int tile = xcd_remap(blockIdx.x, ptiles * qtiles);
+  // With a split reduction (few tiles), workgroup b takes chunks
+  // [z cps, (z + 1) cps) of its tile and writes fp32 partial sums.
+  const int ntiles = ptiles * qtiles;
+  const int lin = xcd_remap(blockIdx.x, static_cast<int>(gridDim.x));
+  const int z = lin / ntiles, tile = lin - z * ntiles;
   const int qt = tile / ptiles, pt = tile - qt * ptiles;
   const int64_t p0 = (int64_t)pt * GP, q0 = (int64_t)qt * GQ;
-  const int nchunks = static_cast<int>(K / GK);
+  const int c0 = z * cps;
+  const int nchunks = min(static_cast<int>(K / GK), c0 + cps);   // end of this split's chunks
   const int KB = static_cast<int>(K / kBlock);
 
   // Buffer descriptors: rows n >= N and tokens m >= M read as zero.
@@ -183,15 +189,15 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
       for (int b = 0; b < GTB; ++b) acc[a][b] = mfma16(af[a], bf[b], acc[a][b]);
   };
 
-  load_codes(0, 0);
-  load_codes(1, 1);
-  load_x(0, 0);
-  load_x(1, 1);
+  load_codes(c0, 0);
+  load_codes(c0 + 1, 1);
+  load_x(c0, 0);
+  load_x(c0 + 1, 1);
   __syncthreads();   // level table
   dequant(0, 0);
   store_x(0, 0);
-  load_codes(2, 0);
-  load_x(2, 0);
+  load_codes(c0 + 2, 0);
+  load_x(c0 + 2, 0);
   __syncthreads();
   // iteration c: read the operands of chunk c from buffers c&1; stage chunk
   // c+1 into buffers (c+1)&1 -- dequantize its codes and store its X, both
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   // load counting sees one path and waits only for the stage it consumes.
   // An odd chunk count adds one pass over a chunk past the end, whose codes,
   // constants and activations all read as zero: it adds zeros.
-  for (int c = 0; c < nchunks; c += 2) {
+  for (int c = c0; c < nchunks; c += 2) {
     iter(c, std::integral_constant<int, 0>{});
     iter(c + 1, std::integral_constant<int, 1>{});
   }
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   // LoRA update: 64 ranks at a time, B^T tile [128 rows][64 ranks] in LDS,
   // s.T hi / lo halves per lane from global memory.  Each k half takes one
   // of the chunk's two 32-rank steps, before the halves are added.
-  if (r > 0) {
+  if (r > 0 && z == 0) {   // the first split adds the LoRA update
     uint16_t* bt = As;
     for (int j0 = 0; j0 < r; j0 += 64) {
       if (tid < GP) {   // patch tid: rows 8 (tid % 16) .., ranks j0 + 8 (tid / 16) ..
@@ -297,7 +303,8 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
     __syncthreads();
   }
 
-  // Y[m, n..n+3] for the lane's 4 consecutive rows n of each subtile
+  // Y[m, n..n+3] for the lane's 4 consecutive rows n of each subtile (bf16),
+  // or this split's fp32 partial sums part[z][m][n..n+3]
   if (ks == 0) {
 #pragma unroll
     for (int a = 0; a < GTA; ++a) {
@@ -307,29 +314,42 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
         const int64_t m = q0 + 64 * wt + 16 * b + li;
         if (m < M && n < N) {
           const f32x4 v = acc[a][b];
-          *reinterpret_cast<u32x2*>(Y + m * N + n) =
-              u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+          if (part) {
+            *reinterpret_cast<f32x4*>(part + ((int64_t)z * M + m) * N + n) = v;
+          } else {
+            *reinterpret_cast<u32x2*>(Y + m * N + n) =
+                u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+          }
         }
       }
     }
   }
 }
 
+GemmSplit fwd_gemm_split(int64_t M, int64_t N, int64_t K) {
+  return gemm_split((N + GP - 1) / GP * ((M + GQ - 1) / GQ), K / GK);
+}
+
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
                             const float* T, const uint16_t* B, int r, float s,
-                            uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
+                            uint16_t* Y, float* part, const Nf4Tables& tb, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_fwd_gemm), hipFuncAttributeMaxDynamicSharedMemorySize,
       kFwdLds);
   if (attr != hipSuccess) return attr;
   const int ptiles = static_cast<int>((w.N + GP - 1) / GP);
   const int qtiles = static_cast<int>((M + GQ - 1) / GQ);
+  const GemmSplit sp = fwd_gemm_split(M, w.N, w.K);
+  if (sp.splits > 1 && !part) return hipErrorInvalidValue;
   prof_begin(0, stream);
-  hipLaunchKernelGGL(k_fwd_gemm, dim3(ptiles * qtiles), dim3(GT), kFwdLds, stream, X, M,
-                     w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, B, r, s, Y, ptiles,
-                     qtiles, tb);
+  hipLaunchKernelGGL(k_fwd_gemm, dim3(ptiles * qtiles * sp.splits), dim3(GT), kFwdLds, stream, X,
+                     M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, B, r, s, Y, ptiles,
+                     qtiles, sp.cps, sp.splits > 1 ? part : nullptr, tb);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && sp.splits > 1)
+    e = launch_split_reduce_bf16(part, sp.splits, M * w.N, Y, stream);
   prof_end(0, stream);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace qnf4

@@ -30,12 +30,25 @@ struct Nf4View {
 void prof_begin(int family, hipStream_t stream);
 void prof_end(int family, hipStream_t stream);
 
+// Split reduction of a dequantizing GEMM whose tiles would leave most of
+// the CUs idle: `splits` workgroups per tile, each over `cps` consecutive
+// chunks of the reduction, write fp32 partials that a second kernel adds up
+// in split order (deterministic) and rounds to bf16.
+struct GemmSplit {
+  int splits, cps;
+};
+GemmSplit gemm_split(int64_t tiles, int64_t nchunks);
+hipError_t launch_split_reduce_bf16(const float* part, int splits, int64_t count, uint16_t* out,
+                                    hipStream_t stream);
+
 // Y[M,N] = bf16( X . deq(W)^T + s . T . B ), large-M MFMA path with the
 // dequantized weight tiles staged in LDS.  T [M, r] fp32 (may be null when
-// r == 0).
+// r == 0).  part: fwd_gemm_split(M, N, K).splits * M * N floats when that is
+// above 1 (else unused).
+GemmSplit fwd_gemm_split(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
                            const float* T, const uint16_t* B, int r, float s,
-                           uint16_t* Y, const Nf4Tables& tb, hipStream_t stream);
+                           uint16_t* Y, float* part, const Nf4Tables& tb, hipStream_t stream);
 
 // Same result, small-M streaming path, for shapes with decode_fits(M, K).
 // decode_folds_t(M, r): the kernel can add up T's partial sums itself.
@@ -50,9 +63,10 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
 
 // dX[M,K] = bf16( dY . deq(W) + s . G . A^T ), MFMA path with the
 // dequantized weight tiles staged in LDS and read back transposed.
+GemmSplit dx_gemm_split(int64_t M, int64_t N, int64_t K);
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
                           const float* G, const uint16_t* A, int r, float s,
-                          uint16_t* dX, const Nf4Tables& tb, hipStream_t stream);
+                          uint16_t* dX, float* part, const Nf4Tables& tb, hipStream_t stream);
 
 // Rank-r products with a split reduction; partials go to `ws`.
 size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r);

@@ -222,6 +222,15 @@ def test_llama7b_full_size(lin_idx):
     _full_linear_check("llama7b", lin_idx)
 
 
+@pytest.mark.parametrize("lin_idx", [0, 6])
+def test_llama7b_dp8_shard(lin_idx):
+    """One GPU's share of 8-way data parallelism (M = 256): the GEMMs have
+    too few tiles for the CUs and split their reductions (fp32 partials,
+    added up in split order); compared in full."""
+    need_gpu()
+    _full_linear_check("llama7b", lin_idx, M=256)
+
+
 @pytest.mark.parametrize("lin_idx,M", [(0, 1), (1, 4), (2, 16), (2, 1)])
 def test_decode_65b_full_size(lin_idx, M):
     """65B-shaped decode linears at M in {1, 4, 16}, compared in full."""
