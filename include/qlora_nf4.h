@@ -138,8 +138,10 @@ int qlora_nf4_dequantize(const qlora_nf4_weight* w, uint16_t* W_bf16,
                          qlora_stream_t stream);
 
 /*
- * Workspace bytes qlora_linear_fwd needs for these sizes (split-reduction
- * partials of the LoRA down-projection).  Contents need no initialisation.
+ * Workspace bytes qlora_linear_fwd needs for these sizes: split-reduction
+ * partials of the LoRA down-projection, and those of the dequantizing GEMM
+ * when its tiles are too few for the GPU (small M; then also for r = 0).
+ * Contents need no initialisation.
  */
 size_t qlora_linear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
 
@@ -162,8 +164,8 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
 
 /*
  * Workspace bytes qlora_linear_bwd needs (G = dY . B^T, the recomputed T
- * when none is passed, and split-reduction partials).  No initialisation
- * needed.
+ * when none is passed, and split-reduction partials of the rank-r products
+ * and, for small M, of the dX GEMM).  No initialisation needed.
  */
 size_t qlora_linear_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
 
