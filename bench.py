@@ -597,7 +597,9 @@ def main():
                      tflops=sh["flops_step"] / (sh["ms_step"] * 1e-3) / 1e12,
                      note="one GPU's share of 8-way data parallelism over the 2048-token "
                           "batch; the dA/dB all-reduce is not part of it")
-        log(f"dp8 shard (M=256): {sh['ms_step']:.3f} ms per step, {shard['tflops']:.1f} TFLOP/s")
+        shard["kernels_ms_per_step"] = {k: ms / args.steps for k, (ms, n) in sh["fam"].items() if n}
+        log(f"dp8 shard (M=256): {sh['ms_step']:.3f} ms per step, {shard['tflops']:.1f} TFLOP/s; "
+            f"kernels (ms per step, eager): {shard['kernels_ms_per_step']}")
         del sh
 
     cpu = None
