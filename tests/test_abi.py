@@ -150,3 +150,20 @@ def test_profile_api_host_only():
     assert L.qlora_profile_read(0, ctypes.byref(ms), ctypes.byref(n)) == 0
     assert n.value == 0 and ms.value == 0.0
     assert L.qlora_profile_read(9, None, None) == 2
+
+
+def test_gemm_split_workspace_sizes():
+    """The GEMMs split their reduction only when their tiles would leave most
+    CUs idle; the workspace then holds one fp32 partial [M, N] (forward) or
+    [M, K] (dX) per split, also for r = 0."""
+    L = q.lib()
+    # 2048 tokens, 4096 x 4096: 256 tiles of 128 x 256, no split
+    assert L.qlora_linear_fwd_workspace_bytes(2048, 4096, 4096, 0) == 0
+    assert L.qlora_linear_bwd_workspace_bytes(2048, 4096, 4096, 0) == 0
+    # 256 tokens: 32 tiles, 8 splits of 8 chunks (64 chunks of 64)
+    assert L.qlora_linear_fwd_workspace_bytes(256, 4096, 4096, 0) == 8 * 256 * 4096 * 4
+    assert L.qlora_linear_bwd_workspace_bytes(256, 4096, 4096, 0) == 8 * 256 * 4096 * 4
+    # with LoRA the partials of the rank products share those bytes
+    assert L.qlora_linear_fwd_workspace_bytes(256, 4096, 4096, 64) >= 8 * 256 * 4096 * 4
+    # few tokens take the decode path: no GEMM partials
+    assert L.qlora_linear_fwd_workspace_bytes(16, 4096, 4096, 0) == 0
