@@ -410,7 +410,7 @@ def run_cpu_baseline(train, repeats=3):
                 oracle.linear_fwd(inp.X, What, inp.A, inp.B, cfg.s)
                 oracle.linear_bwd(inp.dY, inp.X, What, inp.A, inp.B, cfg.s)
                 secs += time.perf_counter() - t0
-                flops += oracle.linear_flops(cfg.M[0], lin.N, lin.K, cfg.r)
+                flops += linear_flops(cfg.M[0], lin.N, lin.K, cfg.r)
         threads = cores
         if threadpool_info:
             nums = [p.get("num_threads", 0) for p in threadpool_info()

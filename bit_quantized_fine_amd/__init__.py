@@ -191,6 +191,8 @@ def qlora_nf4_quantize(W, out: Optional[NF4Weight] = None) -> NF4Weight:
         raise ValueError("W must be [N, K]")
     N, K = W.shape
     _need(W, "W", (N, K), torch.float32)
+    if out is not None and (out.N, out.K) != (N, K):
+        raise ValueError(f"out is a {out.N} x {out.K} weight, W is {N} x {K}")
     _on_gpu([("W", W)] + (_check_weight(out) if out is not None else []))
     L = lib()
     if out is None:

@@ -202,7 +202,9 @@ const char* qlora_status_string(int status) {
   switch (status) {
     case QLORA_OK: return "ok";
     case QLORA_ERR_NULL: return "a required pointer is NULL";
-    case QLORA_ERR_SHAPE: return "invalid shape (need M>=1, N>=1, N%8==0, K>=64, K%64==0)";
+    case QLORA_ERR_SHAPE:
+      return "invalid shape (need M>=1, N>=1, N%8==0, K>=64, K%64==0, N<=2^22, K<=2^22, "
+             "N*K<=2^32)";
     case QLORA_ERR_RANK: return "invalid rank (need 0<=r<=256, r%8==0)";
     case QLORA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case QLORA_ERR_HIP: return "HIP runtime error or kernel launch failure";

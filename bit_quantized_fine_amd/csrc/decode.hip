@@ -3,35 +3,31 @@
 // Y = X . deq(W)^T + s . T . B with T = X . A computed beforehand.  At small
 // M the layer is a stream over the NF4 weight (0.516 bytes per weight), so
 // the kernel is organised around the code stream: every lane issues 16-byte
-// loads of 32 consecutive codes, turns them into bf16 levels in registers
-// and feeds them straight to v_mfma_f32_16x16x32_bf16 with the token
-// dimension padded to 16.
+// loads of 32 consecutive codes, dequantizes them in registers and feeds them
+// straight to v_mfma_f32_16x16x32_bf16 with the token dimension padded to 16.
 //
-// The weight of a code is c_b . q (Mathematical Formulation of "DL0087
-// QLoRA": the block constant dequantized from the 8-bit constant and its
-// group scale, times the NF4 level).  Since c_b is shared by the 64 weights
-// of a block, this kernel multiplies the levels by X first and the block's
-// partial sum by c_b after: every MFMA covers the codes of one block only,
-// and four FMAs per block apply its scale to the lane's four outputs.  The
-// per-weight work is then one table lookup, with no multiply and no
-// conversion (the levels are rounded to bf16 once, in the table).
+// Every weight entering the MFMA is the defined dequantized value
+// bf16_rne(fl32(q[code] . c_b)) with c_b = fl32(e_b . d_g) (Mathematical
+// Formulation of "DL0087 QLoRA": the bf16 tile is rebuilt just before the
+// matmul).  A code byte selects an fp32 level pair from a table in LDS; the
+// pair is multiplied by the block constant and rounded to a bf16 pair.
 //
 // Workgroup = 16 waves on two fragments of 16 weight rows; eight waves share
 // a fragment and split its reduction dimension in chunks of 128 k (wave kw
 // takes chunks kw, kw+8, ...).  A chunk is two blocks.  Lane l loads the 16
-// bytes at 16 (l / 16) of row (l % 16)'s 64-byte chunk segment: lanes 0-31
-// hold the first block, lanes 32-63 the second.  One cross-half swap of two
-// of the four dwords (v_permlane32_swap) leaves every lane with two dwords of
-// each block; MFMA s of a block takes dword s of each lane, and X is read at
-// the matching k.  The code loads are the only vector-memory traffic of the
-// main loop; they run D chunks ahead in a register ring.
+// bytes at 16 (l / 16) of row (l % 16)'s 64-byte chunk segment, i.e. the 32 k
+// starting at 32 (l / 16): lanes 0-31 hold the first block, lanes 32-63 the
+// second, so each lane needs one block constant per chunk.  MFMA i of a chunk
+// takes dword i of every lane (k = 32 (l / 16) + 8 i .. +7), and X is read at
+// the same k.  The code loads are the only vector-memory traffic of the main
+// loop; they run D chunks ahead in a register ring.
 //
-// Staged in LDS once: the bf16 level-pair table (64 copies, one per lane, so
-// lookups never meet a bank conflict), the block scales c_b of the
-// workgroup's rows as fp32 [K/64 + 1][32] (the extra column is zero), the
-// workgroup's columns of B, and X itself when it fits.  The waves' partial
-// sums meet in LDS; the LoRA update is added as extra MFMA steps over the
-// rank before that reduction.
+// Staged in LDS once: the fp32 level-pair table (32 copies, lane l reading
+// copy l % 32, so a half-wave's lookups never meet a bank conflict), the
+// block constants c_b of the workgroup's rows as fp32 [K/64 + 1][32] (the
+// extra column is zero), the workgroup's columns of B, and X itself when it
+// fits.  The waves' partial sums meet in LDS; the LoRA update is added as
+// extra MFMA steps over the rank before that reduction.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -102,7 +98,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // fragments, and 16 waves split K (each X piece then serves 32 rows).
   constexpr int KS = kDecKSlots * FR;   // waves splitting K
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
-  char* tab = reinterpret_cast<char*>(dyn);                          // bf16 level pairs
+  char* tab = reinterpret_cast<char*>(dyn);                          // fp32 level pairs
   uint16_t* bst = reinterpret_cast<uint16_t*>(dyn + boff);           // B columns [r][ROWS]
   f32x4* tfin = reinterpret_cast<f32x4*>(dyn + toff);                // [kDecTSumMaxMR / 4]
   float* csc = reinterpret_cast<float*>(dyn + coff);                 // [KB + 1][ROWS]
@@ -122,8 +118,8 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 
   // Buffer descriptors: rows n >= N fall outside the code / constant buffers
   // and read as zero, and so do token rows li >= M of X.  The second block of
-  // a chunk past K (K % 128 == 64) reads the next row's codes; its products
-  // are dropped.
+  // a chunk past K (K % 128 == 64) reads the next row's codes; its weights
+  // are zero (block constant from the zero column KB).
   const uint32_t nb = static_cast<uint32_t>(N * K / kBlock);
   const BufRes rc = make_bufres(codes, static_cast<uint32_t>(N * K / 2));
   const BufRes re = make_bufres(absmax_q, nb);
@@ -204,10 +200,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 #pragma unroll
   for (int f = 0; f < FR; ++f)
     cb[f] = static_cast<uint32_t>((n0 + 16 * frag(f) + li) * (K / 2)) + 64u * kw + 16u * g;
-  // k offset (inside a block) of the 8 codes that lane group g supplies to
-  // step 0 of a block after the swap (dword 4 (g % 2) + 2 (g / 2); step 1
-  // takes the next dword).
-  const int xo0 = 8 * (4 * (g & 1) + 2 * (g >> 1));
+  // k offset (inside a chunk) of the 8 codes lane group g supplies to MFMA 0
+  // of a chunk (MFMA i takes the 8 after 8 i more).
+  const int xo0 = 32 * g;
   const uint32_t xb = (static_cast<uint32_t>(li) * K32 + 128u * kw + xo0) * 2u;
   u32x4 cw[D][FR];
   u32x4 xv[XLDS ? 1 : D][4];
@@ -219,15 +214,14 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     if constexpr (!XLDS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)   // block i / 2, step i % 2
-        xv[st][i] = buf_load16(
-            rx, live ? xb + 256u * KS * t + 128u * (i >> 1) + 16u * (i & 1) : kDecOffNone);
+        xv[st][i] = buf_load16(rx, live ? xb + 256u * KS * t + 16u * i : kDecOffNone);
     }
   };
 #pragma unroll
   for (int u = 0; u < D; ++u) load(u, u);
 
   // Stage into LDS: level table, X, block scales, B.
-  build_rep_bf16_pair_table<kDecThreads>(tab, lv, tid);
+  build_rep_pair_table<kDecThreads>(tab, lv, tid);
   if constexpr (XLDS) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
@@ -259,72 +253,56 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   if (tid < ROWS) csc[KB * ROWS + tid] = 0.f;
   if ((tid >> 2) < r) reinterpret_cast<u32x4*>(bst)[tid] = bpiece;
 
-  // Lanes past M read X from the zero bytes with stride 0; past K (the second
-  // block of a chunk when K % 128 == 64) their X reads stay inside the row
-  // padding, the next token row or the zero bytes, and the products are
-  // dropped.
+  // Lanes past M read X from the zero bytes with stride 0.  Past K (the
+  // second block of a chunk when K % 128 == 64) the X reads of lanes 32-63
+  // stay inside the next token row or the zero bytes, and their weights are
+  // zero: their block constant is the zero column KB.
   const int xrow = K32 + kDecXPad;
   const uint16_t* xlane = li < M ? xs + li * xrow + xo0 : xs + M * xrow + xo0;
   const int xstep = li < M ? 128 : 0;
-  const float* clane = csc + 4 * g;   // + 16 fragment: scales of the lane's output rows
+  // block constant of the lane's row li and block 2 c + g / 2: + 16 fragment
+  const float* clane = csc + (g >> 1) * ROWS + li;
   // Table addresses: the lane's copy offset in byte 0, entry in byte 1.  The
   // kernel declares no static LDS, so the dynamic block, and the table at its
   // start, begins at LDS address 0 and the address needs no base added.
-  const uint32_t ta = static_cast<uint32_t>(lane) << 2;
+  const uint32_t ta = rep_lane_base(lane);
 
   f32x4 acc[FR];
 #pragma unroll
   for (int f = 0; f < FR; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // All LDS reads of a chunk (scales, table lookups, X) are issued before any
-  // of their products, so one LDS round trip serves the chunk's MFMAs.
+  // All LDS reads of a fragment's chunk (block constant, table lookups, X)
+  // are issued before any of their products, so one LDS round trip serves
+  // its MFMAs; with two fragments a wave (X from global memory) takes them
+  // one after the other, which keeps the lookups of one in registers.
   auto compute = [&](int t, int st) {
     const int c = kw + KS * t;
-    u32x4 a[FR][4], xf[4];
-    f32x4 cA[FR], cB[FR];
-#pragma unroll
-    for (int f = 0; f < FR; ++f) {
-      // Regroup: dwords 0, 1 of lanes 0-31 and 2, 3 of lanes 32-63 stay; the
-      // others trade places across the two halves.  After it, dwords 0, 1
-      // hold codes of the first block and 2, 3 of the second, in every lane.
-      uint32_t d[4] = {cw[st][f].x, cw[st][f].y, cw[st][f].z, cw[st][f].w};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(d[u], d[2 + u], false, false);
-        d[u] = sw[0];
-        d[2 + u] = sw[1];
-      }
-      cA[f] = *reinterpret_cast<const f32x4*>(clane + 16 * frag(f) + (2 * c) * ROWS);
-      cB[f] = *reinterpret_cast<const f32x4*>(clane + 16 * frag(f) + (2 * c + 1) * ROWS);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[f][i][0] = rep_bf16_lookup<0>(ta, d[i]);
-        a[f][i][1] = rep_bf16_lookup<1>(ta, d[i]);
-        a[f][i][2] = rep_bf16_lookup<2>(ta, d[i]);
-        a[f][i][3] = rep_bf16_lookup<3>(ta, d[i]);
-      }
-    }
+    u32x4 xf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (XLDS)
-        xf[i] = *reinterpret_cast<const u32x4*>(xlane + c * xstep + 64 * (i >> 1) + 8 * (i & 1));
+        xf[i] = *reinterpret_cast<const u32x4*>(xlane + c * xstep + 8 * i);
       else
         xf[i] = xv[st][i];
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // (the second block of a chunk past K, when K % 128 == 64, is dropped
-    // rather than scaled by zero: its products may hold anything)
-    const bool second = 2 * c + 1 < KB;   // wave-uniform
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int f = 0; f < FR; ++f) {
-      f32x4 pA = mfma16(a[f][0], xf[0], zero);
-      pA = mfma16(a[f][1], xf[1], pA);
-      f32x4 pB = mfma16(a[f][2], xf[2], zero);
-      pB = mfma16(a[f][3], xf[3], pB);
+      const float ch = clane[16 * frag(f) + 2 * c * ROWS];
+      f32x2 v[4][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[f][j] = __builtin_fmaf(cA[f][j], pA[j], acc[f][j]);
-        if (second) acc[f][j] = __builtin_fmaf(cB[f][j], pB[j], acc[f][j]);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = cw[st][f][i];
+        v[i][0] = rep_lookup<0>(ta, w);
+        v[i][1] = rep_lookup<1>(ta, w);
+        v[i][2] = rep_lookup<2>(ta, w);
+        v[i][3] = rep_lookup<3>(ta, w);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x4 a;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) a[b] = pack_bf16x2(v[i][b].x * ch, v[i][b].y * ch);
+        acc[f] = mfma16(a, xf[i], acc[f]);
       }
     }
   };

@@ -28,10 +28,6 @@ struct OpParams {
   int64_t nrows;   // extent of the tile-row index
   int64_t nred;    // extent of the reduction index
   float scale;     // fp32 sources: value = scale * src
-  // NF4 sources
-  const uint8_t* absmax_q;
-  const float* absmax_scale;
-  int64_t N, K;
 };
 
 __device__ __forceinline__ u32x4 ld16(const void* p) {
@@ -529,16 +525,6 @@ OpParams op(const void* p, int64_t ld, int64_t nrows, int64_t nred, float scale 
   o.nrows = nrows;
   o.nred = nred;
   o.scale = scale;
-  return o;
-}
-
-OpParams nf4op(const Nf4View& w) {
-  OpParams o{};
-  o.ptr = w.codes;
-  o.absmax_q = w.absmax_q;
-  o.absmax_scale = w.absmax_scale;
-  o.N = w.N;
-  o.K = w.K;
   return o;
 }
 

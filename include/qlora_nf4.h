@@ -46,6 +46,13 @@
  *     ("The Quantization Layer" of "QLoRA: Quantized Low Rank Adaptation at
  *     Extreme Scale").
  *   - r = 0 (A and B may then be NULL) selects the base-only layer.
+ *   - Limits: K % 64 == 0 (a block lies inside one row), r % 8 == 0 and
+ *     r <= 256, N % 8 == 0 for qlora_linear_fwd / qlora_linear_bwd (the
+ *     kernels write 8-byte groups of 4 outputs and read 16-byte pieces of
+ *     B), N <= 2^22, K <= 2^22 and N*K <= 2^32 (32-bit buffer offsets).
+ *   - Path selection (results follow the same definition on both paths):
+ *     qlora_linear_fwd streams the weight with the few-token kernel when
+ *     M <= 16 and K <= 32768, and runs the tiled MFMA GEMM otherwise.
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H
@@ -60,8 +67,9 @@ extern "C" {
 typedef enum {
   QLORA_OK = 0,
   QLORA_ERR_NULL = 1,       /* a required pointer is NULL */
-  QLORA_ERR_SHAPE = 2,      /* M, N or K out of range, or K % 64 != 0 */
-  QLORA_ERR_RANK = 3,       /* r outside [0, 256] */
+  QLORA_ERR_SHAPE = 2,      /* M < 1, N < 1, K < 64, K % 64 != 0, N % 8 != 0
+                               (fwd/bwd), N > 2^22, K > 2^22 or N*K > 2^32 */
+  QLORA_ERR_RANK = 3,       /* r outside [0, 256] or r % 8 != 0 */
   QLORA_ERR_ALIGN = 4,      /* a device pointer is not 16-byte aligned */
   QLORA_ERR_HIP = 5,        /* a HIP runtime call or kernel launch failed */
   QLORA_ERR_WORKSPACE = 6   /* workspace too small */
@@ -155,7 +163,8 @@ size_t qlora_linear_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
  *      kept for the backward pass.
  *   workspace: device, at least qlora_linear_fwd_workspace_bytes() bytes
  *      (may be NULL when that is 0).
- * Accumulation is fp32; Y is rounded to bf16 once.  M >= 1.
+ * Accumulation is fp32; Y is rounded to bf16 once.  M >= 1, N % 8 == 0,
+ * r % 8 == 0 (QLORA_ERR_SHAPE / QLORA_ERR_RANK otherwise).
  */
 int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
                      const uint16_t* A, const uint16_t* B, int r, float s,

@@ -28,13 +28,12 @@ from .nf4 import (BLOCK, GROUP, normal_quantile, nf4_levels_f64, nf4_levels,
                   bf16_rne_bits, bf16_bits_to_f64, encode, quantize,
                   unpack_codes, dequantize, dequantize_at, code_boundaries,
                   storage_bytes, bits_per_param)
-from .linear import (linear_fwd_f64, linear_bwd_f64, linear_fwd, linear_bwd,
-                     linear_flops)
+from .linear import linear_fwd_f64, linear_bwd_f64, linear_fwd, linear_bwd
 
 __all__ = [
     "BLOCK", "GROUP", "normal_quantile", "nf4_levels_f64", "nf4_levels",
     "bf16_rne_bits", "bf16_bits_to_f64", "encode", "quantize", "unpack_codes",
     "dequantize", "dequantize_at", "code_boundaries", "storage_bytes",
     "bits_per_param", "linear_fwd_f64", "linear_bwd_f64", "linear_fwd",
-    "linear_bwd", "linear_flops",
+    "linear_bwd",
 ]

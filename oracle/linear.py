@@ -64,12 +64,3 @@ def linear_bwd(dY_bits, X_bits, W_bits, A_bits, B_bits, s, need_dx=True):
     return linear_bwd_f64(bf16_bits_to_f64(dY_bits), bf16_bits_to_f64(X_bits), W,
                           bf16_bits_to_f64(A_bits), bf16_bits_to_f64(B_bits), s,
                           need_dx=need_dx)
-
-
-def linear_flops(M, N, K, r):
-    """Algorithmic flops of one forward + backward: 4MKN + 6Mr(K+N).
-
-    Forward: X.W^T (2MKN), X.A (2MKr), T.B (2MrN).  Backward: dY.W (2MKN),
-    dY.B^T (2MNr), G.A^T (2MrK), X^T.G (2MKr), T^T.dY (2MrN).
-    """
-    return 4 * M * K * N + 6 * M * r * (K + N)

@@ -68,3 +68,11 @@ def test_quantize_refuses_wrong_input():
         q.qlora_nf4_quantize(torch.zeros(8, 64, dtype=torch.float16))
     with pytest.raises(ValueError, match=r"\[N, K\]"):
         q.qlora_nf4_quantize(torch.zeros(8 * 64, dtype=torch.float32))
+
+
+def test_quantize_refuses_output_of_another_shape():
+    """An output weight of the same element count but another N x K (the
+    kernel would write W's layout into it) is refused."""
+    out = _weight(N=128, K=64)
+    with pytest.raises(ValueError, match="128 x 64"):
+        q.qlora_nf4_quantize(torch.zeros(64, 128, dtype=torch.float32), out=out)

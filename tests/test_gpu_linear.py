@@ -22,9 +22,9 @@ pytestmark = pytest.mark.gpu
 class Case:
     """One linear: seeded inputs, GPU tensors, oracle reference."""
 
-    def __init__(self, M, N, K, r, s, seed, b_std=0.01, b_zero=False):
+    def __init__(self, M, N, K, r, s, seed, b_std=0.01, b_zero=False, x_kind="normal"):
         rng = np.random.default_rng(seed)
-        inp = workloads.draw_linear(rng, N, K, M, r, b_std=b_std)
+        inp = workloads.draw_linear(rng, N, K, M, r, b_std=b_std, x_kind=x_kind)
         if b_zero:
             inp.B[:] = 0
         self.M, self.N, self.K, self.r, self.s = M, N, K, r, s
@@ -84,6 +84,37 @@ def test_fwd_parity(M, N, K, r, s):
     Yref, Tref = c.ref_fwd()
     assert_close("Y", Y.float().cpu().numpy(), Yref)
     assert_close("T", T.cpu().numpy(), Tref)
+
+
+@pytest.mark.parametrize("x_kind", ["relu", "shifted"])
+@pytest.mark.parametrize("M,N,K", [
+    (1, 256, 8192),       # decode, X in LDS (one 16-byte piece a thread)
+    (1, 256, 22016),      # decode, X in LDS (four pieces a thread), 65B FFN width
+    (4, 256, 8192),       # decode, X in LDS (four pieces a thread), T folded
+    (16, 256, 8192),      # decode, X from global memory (both fragments a wave)
+    (16, 256, 22016),     # the same at the 65B FFN width
+    (1, 200, 64 * 33),    # decode, half chunk past K (K % 128 == 64)
+    (16, 200, 64 * 33),
+    (64, 256, 8192),      # GEMM path
+])
+def test_fwd_nonzero_mean_activations(M, N, K, x_kind):
+    """Activations with a non-zero mean (the positive part of N(0,1), as a
+    ReLU-family layer feeds its down projection, and N(1,1)): rounding errors
+    of the dequantized weights would add up coherently over K here instead of
+    cancelling, so every weight must be the defined bf16_rne(fl32(q . c))."""
+    need_gpu()
+    say(f"fwd {x_kind} X, M={M} N={N} K={K}")
+    c = Case(M, N, K, 64, 0.25, seed=M * 3 + N + K + len(x_kind), x_kind=x_kind)
+    Y, T = c.gpu_fwd()
+    torch.cuda.synchronize()
+    Yref, Tref = c.ref_fwd()
+    assert_close("Y", Y.float().cpu().numpy(), Yref)
+    assert_close("T", T.cpu().numpy(), Tref)
+    # the base product alone (r = 0), where no adapter term can mask an error
+    Y0, _ = c.gpu_fwd(r=0)
+    torch.cuda.synchronize()
+    base = oracle.bf16_bits_to_f64(c.inp.X) @ oracle.bf16_bits_to_f64(c.What).T
+    assert_close("Y(r=0)", Y0.float().cpu().numpy(), base)
 
 
 @pytest.mark.parametrize("M,N,K,r,s", [
@@ -231,22 +262,30 @@ def test_llama7b_dp8_shard(lin_idx):
     _full_linear_check("llama7b", lin_idx, M=256)
 
 
-@pytest.mark.parametrize("lin_idx,M", [(0, 1), (1, 4), (2, 16), (2, 1)])
-def test_decode_65b_full_size(lin_idx, M):
-    """65B-shaped decode linears at M in {1, 4, 16}, compared in full."""
+@pytest.mark.parametrize("lin_idx", [0, 1, 2])
+def test_decode_65b_full_size(lin_idx):
+    """65B-shaped decode linears (8192 x 8192, 22016 x 8192, 8192 x 22016),
+    each at M = 1, 4 and 16 with the workload's X, and at M = 4 with
+    non-negative X too, compared in full (the oracle quantizes the weight
+    once per shape)."""
     need_gpu()
     cfg = workloads.WORKLOADS["decode_65b"]
-    (lin, inp), = list(workloads.workload_inputs("decode_65b", M=M, linears=[lin_idx],
+    (lin, inp), = list(workloads.workload_inputs("decode_65b", M=16, linears=[lin_idx],
                                                  with_grad=False))
-    say(f"decode_65b {lin.name} N={lin.N} K={lin.K} M={M}")
+    say(f"decode_65b {lin.name} N={lin.N} K={lin.K}")
     w = q.qlora_nf4_quantize(f32(inp.W))
-    Y, T = q.qlora_linear_fwd(bf16(inp.X), w, bf16(inp.A), bf16(inp.B), cfg.s)
-    torch.cuda.synchronize()
+    A, B = bf16(inp.A), bf16(inp.B)
     codes, e, d, _ = oracle.quantize(inp.W)
     np.testing.assert_array_equal(w.codes.cpu().numpy(), codes)
     What = oracle.dequantize(codes, e, d, lin.N, lin.K)
-    Yr, _ = oracle.linear_fwd(inp.X, What, inp.A, inp.B, cfg.s)
-    assert_close("Y", Y.float().cpu().numpy(), Yr)
+    xr = workloads.to_bf16_bits(workloads.draw_activations(np.random.default_rng(lin_idx), 4,
+                                                           lin.K, "relu"))
+    for M, Xh in ((1, inp.X[:1]), (4, inp.X[:4]), (16, inp.X), (4, xr)):
+        say(f"  M={M}")
+        Y, T = q.qlora_linear_fwd(bf16(Xh), w, A, B, cfg.s)
+        torch.cuda.synchronize()
+        Yr, _ = oracle.linear_fwd(Xh, What, inp.A, inp.B, cfg.s)
+        assert_close("Y", Y.float().cpu().numpy(), Yr)
 
 
 @pytest.mark.parametrize("lin_idx", [0, 6])

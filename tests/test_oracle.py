@@ -425,8 +425,3 @@ def test_b_zero_gives_zero_dA():
     dX, dA, dB = oracle.linear_bwd_f64(dY, X, W, A, np.zeros((2, 8)), 1.0)
     assert np.all(dA == 0)
     assert np.any(dB != 0)
-
-
-def test_flops_count():
-    assert oracle.linear_flops(2048, 4096, 4096, 64) == 4 * 2048 * 4096 * 4096 + \
-        6 * 2048 * 64 * 8192

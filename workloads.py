@@ -13,7 +13,10 @@ Recipe (stated once, used everywhere):
   * per linear the draws are, in this order:
       W   float32 [N, K], standard normal x 0.02
       an outlier mask, uniform(0,1) < 0.001, and W *= 10 on the mask
-      X   [M, K] standard normal, rounded to bf16
+      X   [M, K] standard normal, rounded to bf16 (x_kind "relu" keeps
+          max(x, 0) of the same draw, "shifted" adds 1: non-zero-mean
+          activations such as a ReLU-family layer feeds its down
+          projection)
       A   [K, r] normal with standard deviation 1/r, rounded to bf16
       B   [r, N] normal with standard deviation b_std (0.01), rounded to bf16
       dY  [M, N] standard normal, rounded to bf16
@@ -100,10 +103,26 @@ class LinearInputs:
     extra: dict = field(default_factory=dict)
 
 
+X_KINDS = ("normal", "relu", "shifted")
+
+
+def draw_activations(rng, M: int, K: int, x_kind: str = "normal") -> np.ndarray:
+    """[M, K] float32 activations: standard normal, its positive part
+    ("relu") or the standard normal plus 1 ("shifted"); one draw either way."""
+    if x_kind not in X_KINDS:
+        raise ValueError(f"x_kind must be one of {X_KINDS}")
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    if x_kind == "relu":
+        x = np.maximum(x, np.float32(0.0))
+    elif x_kind == "shifted":
+        x = x + np.float32(1.0)
+    return x
+
+
 def draw_linear(rng, N: int, K: int, M: int, r: int, b_std: float = 0.01,
-                with_grad: bool = True) -> LinearInputs:
+                with_grad: bool = True, x_kind: str = "normal") -> LinearInputs:
     W = draw_weight(rng, N, K)
-    X = to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    X = to_bf16_bits(draw_activations(rng, M, K, x_kind))
     a_std = np.float32(1.0 / r) if r else np.float32(0.0)
     A = to_bf16_bits(rng.standard_normal((K, r), dtype=np.float32) * a_std)
     B = to_bf16_bits(rng.standard_normal((r, N), dtype=np.float32) * np.float32(b_std))
