@@ -16,6 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 
 QLORA_OK = 0
+QLORA_ERR_SCRATCH = 7
+NOALLOC_SCRATCH_BYTES = 32 << 20   # QLORA_NOALLOC_SCRATCH_BYTES of the header
 _lib = None
 
 
@@ -45,6 +47,11 @@ _SIGS = {
                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]),
+    "qlora_linear_fwd_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64,
+                                                ctypes.POINTER(_Nf4Weight), ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                                                ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p]),
     "qlora_linear_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64,
                                                            ctypes.c_int64, ctypes.c_int]),
     "qlora_linear_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -256,6 +263,35 @@ def qlora_linear_fwd(X, w: NF4Weight, A=None, B=None, s: float = 1.0,
            lib().qlora_linear_fwd(_ptr(X), M, ctypes.byref(cw), _ptr(A), _ptr(B), r,
                                   float(s), _ptr(Y), _ptr(T), _ptr(workspace), need,
                                   _stream(X)))
+    return Y, T
+
+
+def qlora_linear_fwd_noalloc(X, w: NF4Weight, A=None, B=None, s: float = 1.0,
+                             Y=None, T=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """qlora_linear_fwd on the library's fixed per-GPU scratch instead of a
+    workspace (for callers that cannot allocate device memory; pass Y and T
+    to keep this call allocation-free on the Python side too).  Calls that
+    overlap on one GPU race on that scratch."""
+    import torch
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    M = X.shape[0]
+    _need(X, "X", (M, w.K), torch.bfloat16)
+    wt = _check_weight(w)
+    r = _check_adapters(A, B, w)
+    if Y is not None:
+        _need(Y, "Y", (M, w.N), torch.bfloat16)
+    if T is not None and r > 0:
+        _need(T, "T", (M, r), torch.float32)
+    _on_gpu([("X", X)] + wt + [("A", A), ("B", B), ("Y", Y), ("T", T if r > 0 else None)])
+    if Y is None:
+        Y = torch.empty((M, w.N), dtype=torch.bfloat16, device=X.device)
+    if T is None and r > 0:
+        T = torch.empty((M, r), dtype=torch.float32, device=X.device)
+    cw = w._c()
+    _check("qlora_linear_fwd_noalloc",
+           lib().qlora_linear_fwd_noalloc(_ptr(X), M, ctypes.byref(cw), _ptr(A), _ptr(B), r,
+                                          float(s), _ptr(Y), _ptr(T), _stream(X)))
     return Y, T
 
 

@@ -102,7 +102,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP
 // Forward workspace: the split-reduction partials of T, then (reusing the
 // same bytes once T is final) those of the GEMM when it splits its reduction.
 size_t fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
-  size_t f = r > 0 ? rank_ws_floats(M, N, K, r) : 0;
+  size_t f = lora_down_ws_floats(M, K, r);
   if (!decode_fits(M, K)) {
     const GemmSplit sp = fwd_gemm_split(M, N, K);
     if (sp.splits > 1) f = std::max<size_t>(f, (size_t)sp.splits * M * N);
@@ -118,6 +118,75 @@ size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
   const GemmSplit sp = dx_gemm_split(M, N, K);
   if (sp.splits > 1) f = std::max<size_t>(f, (size_t)sp.splits * M * K);
   return 2 * mr + round_up(f * sizeof(float), 256);
+}
+
+int check_fwd_args(const uint16_t* X, int64_t M, const qlora_nf4_weight* w, const uint16_t* A,
+                   const uint16_t* B, int r, const uint16_t* Y, const float* T) {
+  int st = check_weight(w);
+  if (st) return st;
+  if ((st = check_rank(r))) return st;
+  if (!X || !Y) return QLORA_ERR_NULL;
+  if (r > 0 && (!A || !B || !T)) return QLORA_ERR_NULL;
+  if (M < 1 || w->N % 8 != 0) return QLORA_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(Y) || (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(T))))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch of the allocation-free forward.  A file-scope device array:
+// each GPU the library runs on holds its own copy, at its own address, until
+// the process ends.  Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in for the symbol); the device address is
+// looked up once per device with hipGetSymbolAddress, with that device
+// current, and kept.
+// ---------------------------------------------------------------------------
+
+constexpr size_t kScratchBytes = QLORA_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QLORA_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QLORA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return QLORA_OK;
+}
+
+// The forward once its arguments are checked; ws holds at least
+// fwd_ws_bytes(M, N, K, r) bytes.
+int fwd_impl(const uint16_t* X, int64_t M, const qlora_nf4_weight* w, const uint16_t* A,
+             const uint16_t* B, int r, float s, uint16_t* Y, float* T, float* ws,
+             hipStream_t hs) {
+  const Nf4View v = view(w);
+  hipError_t e = hipSuccess;
+  const bool decode = decode_fits(M, w->K);
+  if (decode && decode_folds_t(M, r)) {
+    // T's partial sums are added up inside the decode kernel (no reduction
+    // launch); its workgroup 0 writes T.
+    int nz = 0;
+    e = launch_lora_down_partials(X, M, w->K, A, r, decode_max_t_partials(M, w->K, r), ws, &nz,
+                                  hs);
+    if (e == hipSuccess) e = launch_fwd_decode(X, M, v, ws, nz, T, B, r, s, Y, tables(), hs);
+    return hip_status(e);
+  }
+  if (r > 0) e = launch_lora_down(X, M, w->K, A, r, T, ws, hs);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  if (decode)
+    e = launch_fwd_decode(X, M, v, T, 0, nullptr, B, r, s, Y, tables(), hs);
+  else
+    e = launch_fwd_gemm(X, M, v, T, B, r, s, Y, ws, tables(), hs);
+  return hip_status(e);
 }
 
 // ---------------------------------------------------------------------------
@@ -209,6 +278,9 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case QLORA_ERR_HIP: return "HIP runtime error or kernel launch failure";
     case QLORA_ERR_WORKSPACE: return "workspace too small";
+    case QLORA_ERR_SCRATCH:
+      return "the call needs more workspace than the fixed scratch of qlora_linear_fwd_noalloc "
+             "(QLORA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -280,39 +352,24 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
                      const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
                      float* T, void* workspace, size_t workspace_bytes,
                      qlora_stream_t stream) {
-  int st = check_weight(w);
+  int st = check_fwd_args(X, M, w, A, B, r, Y, T);
   if (st) return st;
-  if ((st = check_rank(r))) return st;
-  if (!X || !Y) return QLORA_ERR_NULL;
-  if (r > 0 && (!A || !B || !T)) return QLORA_ERR_NULL;
-  if (M < 1 || w->N % 8 != 0) return QLORA_ERR_SHAPE;
-  if (!aligned16(X) || !aligned16(Y) || (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(T))))
-    return QLORA_ERR_ALIGN;
   const size_t need = fwd_ws_bytes(M, w->N, w->K, r);
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return QLORA_ERR_ALIGN;
+  return fwd_impl(X, M, w, A, B, r, s, Y, T, static_cast<float*>(workspace),
+                  static_cast<hipStream_t>(stream));
+}
 
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
-  const Nf4View v = view(w);
-  hipError_t e = hipSuccess;
-  float* ws = static_cast<float*>(workspace);
-  const bool decode = decode_fits(M, w->K);
-  if (decode && decode_folds_t(M, r)) {
-    // T's partial sums are added up inside the decode kernel (no reduction
-    // launch); its workgroup 0 writes T.
-    int nz = 0;
-    e = launch_lora_down_partials(X, M, w->K, A, r, decode_max_t_partials(M, w->K, r), ws, &nz,
-                                  hs);
-    if (e == hipSuccess) e = launch_fwd_decode(X, M, v, ws, nz, T, B, r, s, Y, tables(), hs);
-    return hip_status(e);
-  }
-  if (r > 0) e = launch_lora_down(X, M, w->K, A, r, T, ws, hs);
-  if (e != hipSuccess) return QLORA_ERR_HIP;
-  if (decode)
-    e = launch_fwd_decode(X, M, v, T, 0, nullptr, B, r, s, Y, tables(), hs);
-  else
-    e = launch_fwd_gemm(X, M, v, T, B, r, s, Y, ws, tables(), hs);
-  return hip_status(e);
+int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
+                             const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
+                             float* T, qlora_stream_t stream) {
+  int st = check_fwd_args(X, M, w, A, B, r, Y, T);
+  if (st) return st;
+  if (fwd_ws_bytes(M, w->N, w->K, r) > kScratchBytes) return QLORA_ERR_SCRATCH;
+  float* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws))) return st;
+  return fwd_impl(X, M, w, A, B, r, s, Y, T, ws, static_cast<hipStream_t>(stream));
 }
 
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,

@@ -612,6 +612,13 @@ size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r) {
   return m;
 }
 
+size_t lora_down_ws_floats(int64_t M, int64_t K, int r) {
+  if (r <= 0) return 0;
+  if (M <= 16) return (size_t)lora_down_partial_count(K, kMaxDownPartials) * M * r;
+  const Split t = choose_split(K, (r + RB_R - 1) / RB_R, (M + RB_X - 1) / RB_X);
+  return (size_t)t.splits * M * r;
+}
+
 int lora_down_partial_count(int64_t K, int maxp) {
   const int64_t slices = (K + LDS_K - 1) / LDS_K;
   const int64_t spw = (slices + maxp - 1) / maxp;

@@ -70,6 +70,8 @@ hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
 
 // Rank-r products with a split reduction; partials go to `ws`.
 size_t rank_ws_floats(int64_t M, int64_t N, int64_t K, int r);
+// The partials of T = X . A alone (the forward's rank product).
+size_t lora_down_ws_floats(int64_t M, int64_t K, int r);
 
 // Few-token LoRA down-projection: nz <= maxp fp32 partial sums [nz][M][r]
 // of T = X . A go to ws (nz returned); M <= 16, maxp <= kMaxDownPartials.

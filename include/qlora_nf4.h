@@ -72,7 +72,9 @@ typedef enum {
   QLORA_ERR_RANK = 3,       /* r outside [0, 256] or r % 8 != 0 */
   QLORA_ERR_ALIGN = 4,      /* a device pointer is not 16-byte aligned */
   QLORA_ERR_HIP = 5,        /* a HIP runtime call or kernel launch failed */
-  QLORA_ERR_WORKSPACE = 6   /* workspace too small */
+  QLORA_ERR_WORKSPACE = 6,  /* workspace too small */
+  QLORA_ERR_SCRATCH = 7     /* qlora_linear_fwd_noalloc: the call needs more than
+                               QLORA_NOALLOC_SCRATCH_BYTES of workspace */
 } qlora_status;
 
 /* A hipStream_t, passed as an opaque pointer so this header needs no HIP. */
@@ -170,6 +172,32 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
                      const uint16_t* A, const uint16_t* B, int r, float s,
                      uint16_t* Y, float* T, void* workspace,
                      size_t workspace_bytes, qlora_stream_t stream);
+
+/*
+ * The forward of qlora_linear_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments and results, bit for bit, without the
+ * workspace arguments.  The workspace is instead a fixed device array of
+ * QLORA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends; no call allocates or frees anything.
+ *   - A call whose workspace (qlora_linear_fwd_workspace_bytes) exceeds that
+ *     size returns QLORA_ERR_SCRATCH before enqueueing anything.  The GEMM's
+ *     split-reduction partials never exceed 32 MiB, and T's partial sums
+ *     exceed it only when M . r > 2^23, so every call with M . r <= 2^23
+ *     (M <= 32768 at r = 256, M <= 131072 at r = 64) fits.
+ *   - The first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress, with that device current); make it outside
+ *     graph capture.
+ *   - Every call on one GPU uses that GPU's array: calls that overlap on
+ *     one GPU (on different streams, or from several threads) race, and
+ *     must be serialised by the caller.  The array's contents need no
+ *     initialisation and keep whatever the last call left.
+ */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t M,
+                             const qlora_nf4_weight* w, const uint16_t* A,
+                             const uint16_t* B, int r, float s, uint16_t* Y,
+                             float* T, qlora_stream_t stream);
 
 /*
  * Workspace bytes qlora_linear_bwd needs (G = dY . B^T, the recomputed T

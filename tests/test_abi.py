@@ -66,8 +66,8 @@ def test_size_helpers():
 
 def test_status_strings_and_version():
     L = q.lib()
-    for s in range(7):
-        assert L.qlora_status_string(s)
+    for s in range(8):
+        assert L.qlora_status_string(s) != b"unknown status"
     assert L.qlora_status_string(99) == b"unknown status"
     assert L.qlora_version().decode().count(".") == 2
 
@@ -167,3 +167,22 @@ def test_gemm_split_workspace_sizes():
     assert L.qlora_linear_fwd_workspace_bytes(256, 4096, 4096, 64) >= 8 * 256 * 4096 * 4
     # few tokens take the decode path: no GEMM partials
     assert L.qlora_linear_fwd_workspace_bytes(16, 4096, 4096, 0) == 0
+
+
+def test_noalloc_forward_refuses_calls_beyond_its_scratch():
+    """qlora_linear_fwd_noalloc checks its fixed scratch before touching the
+    device: a call whose workspace exceeds QLORA_NOALLOC_SCRATCH_BYTES gets
+    QLORA_ERR_SCRATCH (the pointers are never read)."""
+    L = q.lib()
+    M, N, K, r = 1 << 18, 8, 64, 64          # T alone: M r fp32 = 64 MiB
+    assert L.qlora_linear_fwd_workspace_bytes(M, N, K, r) > q.NOALLOC_SCRATCH_BYTES
+    w = _w(N=N, K=K)
+    st = L.qlora_linear_fwd_noalloc(16, M, ctypes.byref(w), 16, 16, r, 1.0, 16, 16, None)
+    assert st == q.QLORA_ERR_SCRATCH
+    assert b"scratch" in L.qlora_status_string(st)
+    # the largest split-reduction partials of the GEMM (256 tiles' worth) fit
+    assert L.qlora_linear_fwd_workspace_bytes(256, 4096, 4096, 64) <= q.NOALLOC_SCRATCH_BYTES
+    assert L.qlora_linear_fwd_workspace_bytes(32768, 4096, 4096, 256) <= q.NOALLOC_SCRATCH_BYTES
+    # argument errors come first, as in qlora_linear_fwd
+    assert L.qlora_linear_fwd_noalloc(None, 4, ctypes.byref(w), 16, 16, 8, 1.0, 16, 16,
+                                      None) == 1
