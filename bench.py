@@ -384,10 +384,61 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
     return out
 
 
-def run_cpu_baseline(train, repeats=3):
-    """The oracle (dequantize + forward + backward, float64 products) on a
-    bounded sample of the same workload: all seven linears at full M (one
-    training step), `repeats` times, on this host's cores."""
+def run_peaks(q, torch, dev):
+    """Rates this GPU reaches on a plain 4 GiB streaming read and on a loop of
+    independent bf16 32x32x16 MFMAs (the library's probe kernels), best of
+    a few launch sizes, each timed with HIP events over 5 launches."""
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best_gbs = 0.0
+    for wg in (1024, 2048, 4096, 8192):
+        q.qlora_probe_hbm_read(buf, wg, sink)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(5):
+            q.qlora_probe_hbm_read(buf, wg, sink)
+        ev1.record()
+        torch.cuda.synchronize()
+        best_gbs = max(best_gbs, 5 * nbytes / (ev0.elapsed_time(ev1) * 1e-3) / 1e9)
+    del buf
+    best_tf = 0.0
+    for wg in (1024, 2048):
+        q.qlora_probe_mfma_bf16(100, wg, sink)
+        torch.cuda.synchronize()
+        ev0.record()
+        flops = sum(q.qlora_probe_mfma_bf16(4000, wg, sink) for _ in range(3))
+        ev1.record()
+        torch.cuda.synchronize()
+        best_tf = max(best_tf, flops / (ev0.elapsed_time(ev1) * 1e-3) / 1e12)
+    torch.cuda.empty_cache()
+    return dict(hbm_read_gbs=best_gbs, mfma_bf16_tflops=best_tf,
+                note="4 GiB non-temporal 16-byte streaming read; independent "
+                     "v_mfma_f32_32x32x16_bf16 on register operands; best of several grid sizes")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_cpu_baseline(train, repeats=2):
+    """The oracle (plain NumPy: dequantize, then float64 products) timed on a
+    bounded sample of each workload on this host's cores.  The value is the
+    headline workload's: all seven LLaMA-7B linears at M = 2048 (one
+    training step, `repeats` times; load-time quantization untimed).  Also
+    timed: the 1024 x 1024 parity linear in full (quantize, dequantize, fwd,
+    bwd), one M = 1 forward of the 8192 x 8192 decode shape and one linear
+    (q, 6656 x 6656, M = 4096) of the 33B layer with the recompute backward;
+    for the last two the codes are drawn at random (the time does not depend
+    on their values) instead of quantized."""
     import numpy as np
 
     import oracle
@@ -397,10 +448,11 @@ def run_cpu_baseline(train, repeats=3):
     except Exception:  # pragma: no cover
         threadpool_info = threadpool_limits = None
     cores = len(os.sched_getaffinity(0))
-    cfg = workloads.WORKLOADS["llama7b"]
-    flops, secs = 0, 0.0
     ctx = threadpool_limits(cores) if threadpool_limits else None
+    extra = {}
     try:
+        cfg = workloads.WORKLOADS["llama7b"]
+        flops, secs = 0, 0.0
         for idx in range(len(cfg.linears)):
             (lin, inp), = list(workloads.workload_inputs("llama7b", linears=[idx]))
             codes, e, d, _ = oracle.quantize(inp.W)       # load-time, untimed
@@ -411,6 +463,58 @@ def run_cpu_baseline(train, repeats=3):
                 oracle.linear_bwd(inp.dY, inp.X, What, inp.A, inp.B, cfg.s)
                 secs += time.perf_counter() - t0
                 flops += linear_flops(cfg.M[0], lin.N, lin.K, cfg.r)
+        # the parity linear, everything timed
+        c0 = workloads.WORKLOADS["parity_1k"]
+        (lin, inp), = list(workloads.workload_inputs("parity_1k"))
+        t0 = time.perf_counter()
+        codes, e, d, _ = oracle.quantize(inp.W)
+        What = oracle.dequantize(codes, e, d, lin.N, lin.K)
+        oracle.linear_fwd(inp.X, What, inp.A, inp.B, c0.s)
+        oracle.linear_bwd(inp.dY, inp.X, What, inp.A, inp.B, c0.s)
+        dt = time.perf_counter() - t0
+        extra["parity_1k"] = dict(seconds=dt, sample="quantize + dequantize + fwd + bwd, "
+                                  "1024x1024, M=16, r=16")
+        rng = np.random.default_rng(99)
+
+        def random_weight(N, K):
+            codes = rng.integers(0, 256, N * K // 2, dtype=np.uint8)
+            e = rng.integers(0, 256, N * K // 64, dtype=np.uint8)
+            d = (rng.random((N * K // 64 + 255) // 256, dtype=np.float32) * 1e-3).astype(np.float32)
+            return codes, e, d
+
+        # one decode call (M = 1) on the 8192 x 8192 shape: bytes per second
+        N = K = 8192
+        r = 64
+        codes, e, d = random_weight(N, K)
+        X = workloads.to_bf16_bits(rng.standard_normal((1, K), dtype=np.float32))
+        A = workloads.to_bf16_bits(rng.standard_normal((K, r), dtype=np.float32) / r)
+        B = workloads.to_bf16_bits(rng.standard_normal((r, N), dtype=np.float32) * 0.01)
+        t0 = time.perf_counter()
+        What = oracle.dequantize(codes, e, d, N, K)
+        oracle.linear_fwd(X, What, A, B, 0.25)
+        dt = time.perf_counter() - t0
+        alg = N * K // 2 + N * K // 64 + 4 * (N * K // 64 // 256) + 2 * (K + N + K * r + r * N)
+        extra["decode_65b_m1"] = dict(seconds=dt, value=alg / dt / 1e9, unit="GB/s",
+                                      sample="one M=1 forward of 8192x8192, r=64: oracle "
+                                             "dequantize + fwd")
+        # one linear of the 33B layer, recompute backward
+        cfg3 = workloads.WORKLOADS["llama33b_recompute"]
+        N = K = 6656
+        M = cfg3.M[0]
+        codes, e, d = random_weight(N, K)
+        X = workloads.to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+        dY = workloads.to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32))
+        A = workloads.to_bf16_bits(rng.standard_normal((K, r), dtype=np.float32) / r)
+        B = workloads.to_bf16_bits(rng.standard_normal((r, N), dtype=np.float32) * 0.01)
+        t0 = time.perf_counter()
+        What = oracle.dequantize(codes, e, d, N, K)
+        oracle.linear_fwd(X, What, A, B, cfg3.s)
+        What = oracle.dequantize(codes, e, d, N, K)   # the backward dequantizes again
+        oracle.linear_bwd(dY, X, What, A, B, cfg3.s)
+        dt = time.perf_counter() - t0
+        extra["llama33b_recompute_q"] = dict(
+            seconds=dt, value=linear_flops(M, N, K, r) / dt / 1e12, unit="TFLOP/s",
+            sample="one linear (6656x6656, M=4096, r=64): dequantize + fwd + dequantize + bwd")
         threads = cores
         if threadpool_info:
             nums = [p.get("num_threads", 0) for p in threadpool_info()
@@ -420,9 +524,10 @@ def run_cpu_baseline(train, repeats=3):
         if ctx is not None:
             ctx.__exit__(None, None, None)
     return dict(value=flops / secs / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
-                seconds=secs,
-                sample=f"{repeats} steps: all seven linears, M=2048, r=64: oracle dequantize + "
-                       "fwd + bwd (float64 products); load-time quantization untimed")
+                seconds=secs, cpu_model=cpu_model(),
+                sample=f"{repeats} steps: all seven LLaMA-7B linears, M=2048, r=64: oracle "
+                       "dequantize + fwd + bwd (float64 products); load-time quantization untimed",
+                other_workloads=extra)
 
 
 def _rocprof_csvs(root, suffix):
@@ -450,6 +555,22 @@ def summarize_rocprof(root, copy_mib, top=16, by_grid=False):
             lines.append(f"{r['Name'][:70]:70s} {int(r['Calls']):6d} "
                          f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
                          f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):7.2f}")
+    if by_grid:
+        # durations per kernel and grid size (tells the shapes of one kernel apart)
+        for path in _rocprof_csvs(root, "kernel_trace.csv"):
+            agg = {}
+            for r in csv.DictReader(open(path)):
+                grid = r.get("Grid_Size") or "x".join(
+                    r.get(f"Grid_Size_{a}", "?") for a in ("X", "Y", "Z"))
+                key = f"{r['Kernel_Name'].split('(')[0][:52]} grid={grid}"
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                agg.setdefault(key, []).append(dur)
+            lines.append(f"{'kernel (per grid size)':70s} {'calls':>6s} {'avg_us':>9s} "
+                         f"{'median_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+            for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1]))[:3 * top]:
+                v = sorted(v)
+                lines.append(f"{k[:70]:70s} {len(v):6d} {sum(v) / len(v):9.2f} "
+                             f"{v[len(v) // 2]:9.2f} {v[0]:9.2f} {v[-1]:9.2f}")
     traffic = {}
     for path in _rocprof_csvs(root, "counter_collection.csv"):
         agg = {}
@@ -457,7 +578,9 @@ def summarize_rocprof(root, copy_mib, top=16, by_grid=False):
             name = r["Kernel_Name"]
             if by_grid:   # (the calibration copy keeps its name's "neg" in front)
                 tag = "neg_kernel " if "neg_kernel" in name else ""
-                name = f"{(tag + name.split('(')[0])[:52]} grid={r['Grid_Size']}"
+                grid = r.get("Grid_Size") or "x".join(
+                    r.get(f"Grid_Size_{a}", "?") for a in ("X", "Y", "Z"))
+                name = f"{(tag + name.split('(')[0])[:52]} grid={grid}"
             key = (name, r["Counter_Name"])
             agg.setdefault(key, []).append(float(r["Counter_Value"]))
         lines.append(f"{'kernel':70s} {'counter':>12s} {'dispatches':>10s} {'mean_per_dispatch':>18s}")
@@ -483,6 +606,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured-peak probes (4 GiB streaming read, bf16 MFMA loop)")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the extra step at one GPU's share of 8-way data parallelism "
                          "(256 of the 2048 tokens)")
@@ -602,6 +727,18 @@ def main():
             f"kernels (ms per step, eager): {shard['kernels_ms_per_step']}")
         del sh
 
+    peaks = None
+    if not args.no_peaks:
+        peaks = run_peaks(q, torch, dev)
+        log(f"measured peaks: {peaks['hbm_read_gbs']:.0f} GB/s streaming read, "
+            f"{peaks['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA")
+        roofline["measured_peak"] = peaks["mfma_bf16_tflops"]
+        roofline["frac_of_measured_peak"] = roofline["achieved"] / peaks["mfma_bf16_tflops"]
+        if decode is not None:
+            for mk, dv in decode.items():
+                dv["frac_hbm_vendor"] = dv["gbs_call"] / PEAK_HBM_GBS
+                dv["frac_hbm_measured"] = dv["gbs_call"] / peaks["hbm_read_gbs"]
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(tr)
@@ -635,6 +772,7 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "measured_peaks": peaks,
         "decode_m1_gbs": None if decode is None else decode["M=1"]["gbs_call"],
         "dp8_shard": shard,
         "decode": decode,

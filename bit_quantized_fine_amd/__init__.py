@@ -60,6 +60,10 @@ _SIGS = {
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]),
+    "qlora_probe_hbm_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_void_p]),
+    "qlora_probe_mfma_bf16": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_void_p]),
     "qlora_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "qlora_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64)]),
@@ -356,6 +360,20 @@ def qlora_profile_read(family: int):
     _check("qlora_profile_read", lib().qlora_profile_read(family, ctypes.byref(ms),
                                                            ctypes.byref(n)))
     return ms.value, n.value
+
+
+def qlora_probe_hbm_read(buf, workgroups: int, sink):
+    """Enqueue one streaming read of the uint8 device tensor buf."""
+    _check("qlora_probe_hbm_read",
+           lib().qlora_probe_hbm_read(_ptr(buf), buf.numel(), _ptr(sink), workgroups,
+                                      _stream(buf)))
+
+
+def qlora_probe_mfma_bf16(iters: int, workgroups: int, sink):
+    """Enqueue the bf16 MFMA loop; returns its flop count."""
+    _check("qlora_probe_mfma_bf16",
+           lib().qlora_probe_mfma_bf16(iters, workgroups, _ptr(sink), _stream(sink)))
+    return workgroups * 4 * iters * 8 * 32768
 
 
 PROFILE_FAMILIES = {0: "fwd_gemm", 1: "dx_gemm", 2: "fwd_decode", 3: "quantize", 4: "rank"}

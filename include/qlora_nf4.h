@@ -244,6 +244,26 @@ int qlora_profile_enable(int enable);
 int qlora_profile_read(int family, double* total_ms, int64_t* launches);
 int qlora_profile_reset(void);
 
+/*
+ * Peak probes (measurement only; not part of the layer).  They give the
+ * rates this GPU reaches, against which kernel rates are also reported.
+ *   qlora_probe_hbm_read: `workgroups` workgroups of 256 threads read the
+ *     `bytes` (a multiple of 16, buf 16-byte aligned) of device buffer buf
+ *     once with 16-byte non-temporal loads.  The caller times the launch;
+ *     use a buffer far larger than the last-level cache (e.g. 4 GiB).
+ *   qlora_probe_mfma_bf16: `workgroups` workgroups of 4 waves; every wave
+ *     issues iters x 8 independent v_mfma_f32_32x32x16_bf16 on register
+ *     operands: workgroups x 4 x iters x 8 x 32768 flops.
+ * sink: device memory of at least `workgroups` uint32, written only in a
+ * case that does not occur (it keeps the work from being removed).
+ * Errors: QLORA_ERR_NULL, QLORA_ERR_ALIGN, QLORA_ERR_SHAPE (workgroups or
+ * iters < 1), QLORA_ERR_HIP on a failed launch.
+ */
+int qlora_probe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups,
+                         qlora_stream_t stream);
+int qlora_probe_mfma_bf16(int64_t iters, int workgroups, uint32_t* sink,
+                          qlora_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
