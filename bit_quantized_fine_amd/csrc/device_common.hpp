@@ -1,6 +1,6 @@
 // Device-side building blocks shared by the gfx950 kernels of the QLoRA NF4
-// linear layer: vector types, bf16 packing, the NF4 byte-pair lookup table
-// and the 16x16x32 bf16 MFMA wrapper.
+// linear layer: vector types, bf16 packing, the NF4 level-pair lookup tables,
+// dequantization in registers, and the 16x16x32 bf16 MFMA wrapper.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -56,51 +56,6 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi,
   lo = pack_bf16x2(a - bf16_lo_to_f32(hi), b - bf16_hi_to_f32(hi));
 }
 
-// Byte-pair lookup table of NF4 levels in LDS: entry b holds
-// (level[b & 15], level[b >> 4]), i.e. the two weights a packed code byte
-// encodes, even element first.  256 entries x 8 bytes = 2 KB.
-__device__ __forceinline__ void build_pair_table(float2* tab, const Nf4Tables& tb,
-                                                 int tid, int nthreads) {
-  for (int b = tid; b < 256; b += nthreads) {
-    float lo = 0.f, hi = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      lo = ((b & 15) == j) ? tb.q[j] : lo;
-      hi = ((b >> 4) == j) ? tb.q[j] : hi;
-    }
-    tab[b] = make_float2(lo, hi);
-  }
-}
-
-// Dequantize the 8 codes of one 32-bit word (4 bytes, elements in order) with
-// block constant c_hat: bf16_rne(fl32(level[code] * c_hat)), packed as 8
-// consecutive bf16 (4 dwords).
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, float c_hat,
-                                          const float2* tab) {
-  const float2 p0 = tab[w & 0xFFu];
-  const float2 p1 = tab[(w >> 8) & 0xFFu];
-  const float2 p2 = tab[(w >> 16) & 0xFFu];
-  const float2 p3 = tab[w >> 24];
-  u32x4 o;
-  o.x = pack_bf16x2(p0.x * c_hat, p0.y * c_hat);
-  o.y = pack_bf16x2(p1.x * c_hat, p1.y * c_hat);
-  o.z = pack_bf16x2(p2.x * c_hat, p2.y * c_hat);
-  o.w = pack_bf16x2(p3.x * c_hat, p3.y * c_hat);
-  return o;
-}
-
-// Same, but keeps the fp32 products (used by the transposing loader, which
-// packs pairs across rows instead of along the row).
-__device__ __forceinline__ void dequant8_f32(uint32_t w, float c_hat,
-                                             const float2* tab, float* v) {
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const float2 p = tab[(w >> (8 * b)) & 0xFFu];
-    v[2 * b] = p.x * c_hat;
-    v[2 * b + 1] = p.y * c_hat;
-  }
-}
-
 // Byte-pair table replicated for conflict-free lookups: 32 copies of the 256
 // entries, entry b of copy c at byte 256 b + 8 c, so lane l reads copy
 // (l % 32) and the 32 lanes of a half-wave always hit distinct bank pairs
@@ -144,6 +99,57 @@ __device__ __forceinline__ void build_rep_pair_table(char* tab, const Levels& lv
 #pragma unroll
   for (int c = 0; c < kCopies; ++c)
     reinterpret_cast<float2*>(tab)[32 * e + ((c0 + c + e) & 31)] = make_float2(lo, hi);
+}
+
+// Dequantization in registers, without a lookup table in memory.  For one
+// block with constant c_hat, the 16 possible weights bf16_rne(fl32(q_j c_hat))
+// are formed once (16 multiplies, 8 conversions) and split into byte planes:
+// lo[a] holds the low bytes of weights 4a .. 4a+3, hi[a] their high bytes.
+// A code then selects its bytes with v_perm_b32: one permute picks from 8
+// entries by the code's low 3 bits, a second one chooses between the two
+// halves of the table by bit 3.
+struct Bf16Planes {
+  uint32_t lo[4], hi[4];
+};
+__device__ __forceinline__ Bf16Planes block_planes(const Levels& lv, float chat) {
+  uint32_t P[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) P[m] = pack_bf16x2(lv.v[2 * m] * chat, lv.v[2 * m + 1] * chat);
+  Bf16Planes t;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    t.lo[a] = __builtin_amdgcn_perm(P[2 * a + 1], P[2 * a], 0x06040200u);
+    t.hi[a] = __builtin_amdgcn_perm(P[2 * a + 1], P[2 * a], 0x07050301u);
+  }
+  return t;
+}
+
+// The four bytes of plane pl (lo or hi) for the four codes whose low 3 bits
+// are the bytes of sel, bit 3 given as 4 in the bytes of half (+ 0x03020100).
+__device__ __forceinline__ uint32_t plane_pick(const uint32_t* pl, uint32_t sel, uint32_t half) {
+  return __builtin_amdgcn_perm(__builtin_amdgcn_perm(pl[3], pl[2], sel),
+                               __builtin_amdgcn_perm(pl[1], pl[0], sel), half);
+}
+
+// The 8 codes of w (4 bytes, elements in order, even element in the low
+// nibble) -> 8 consecutive bf16 weights (4 dwords).
+__device__ __forceinline__ u32x4 dequant8_planes(uint32_t w, const Bf16Planes& t) {
+  const uint32_t se = w & 0x07070707u;                            // even elements
+  const uint32_t so = (w >> 4) & 0x07070707u;                     // odd elements
+  const uint32_t me = ((w >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t mo = ((w >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t le = plane_pick(t.lo, se, me), he = plane_pick(t.hi, se, me);
+  const uint32_t lo = plane_pick(t.lo, so, mo), ho = plane_pick(t.hi, so, mo);
+  // bf16 pairs (elements 0, 2), (4, 6) and (1, 3), (5, 7) ...
+  const uint32_t e01 = __builtin_amdgcn_perm(he, le, 0x05010400u);
+  const uint32_t e23 = __builtin_amdgcn_perm(he, le, 0x07030602u);
+  const uint32_t o01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u);
+  const uint32_t o23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);
+  // ... interleaved into element order
+  return u32x4{__builtin_amdgcn_perm(o01, e01, 0x05040100u),
+               __builtin_amdgcn_perm(o01, e01, 0x07060302u),
+               __builtin_amdgcn_perm(o23, e23, 0x05040100u),
+               __builtin_amdgcn_perm(o23, e23, 0x07060302u)};
 }
 
 typedef __attribute__((address_space(3))) const f32x2 LdsF32x2;

@@ -75,21 +75,21 @@ __global__ __launch_bounds__(256) void k_quantize(
 }
 
 // Standalone dequantization: each thread expands 16 code bytes (32 weights,
-// half a block) into 32 bf16 values.
+// half a block) into 32 bf16 values, with the block's 16 dequantized values
+// formed in registers and selected by byte permutes (the same routine the
+// tiled forward GEMM uses).
 __global__ __launch_bounds__(256) void k_dequantize(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
     const float* __restrict__ absmax_scale, int64_t nchunks,
     uint16_t* __restrict__ out, Nf4Tables tb) {
-  __shared__ float2 tab[256];
-  build_pair_table(tab, tb, threadIdx.x, blockDim.x);
-  __syncthreads();
+  const Levels lv = load_levels(tb);
   for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks;
        c += (int64_t)gridDim.x * blockDim.x) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(codes + c * 16);
-    const float chat = block_scale(absmax_q, absmax_scale, c >> 1);
+    const Bf16Planes t = block_planes(lv, block_scale(absmax_q, absmax_scale, c >> 1));
     u32x4* dst = reinterpret_cast<u32x4*>(out + c * 32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = dequant8(w[i], chat, tab);
+    for (int i = 0; i < 4; ++i) dst[i] = dequant8_planes(w[i], t);
   }
 }
 
