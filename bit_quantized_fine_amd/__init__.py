@@ -60,6 +60,23 @@ _SIGS = {
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                         ctypes.c_void_p]),
+    "qlora_block_fwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int,
+                                                          ctypes.c_int64, ctypes.c_int64,
+                                                          ctypes.c_int]),
+    "qlora_block_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(_Nf4Weight),
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]),
+    "qlora_block_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int,
+                                                          ctypes.c_int64, ctypes.c_int64,
+                                                          ctypes.c_int]),
+    "qlora_block_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.POINTER(_Nf4Weight), ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]),
     "qlora_probe_hbm_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_void_p]),
     "qlora_probe_mfma_bf16": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
@@ -360,6 +377,87 @@ def qlora_profile_read(family: int):
     _check("qlora_profile_read", lib().qlora_profile_read(family, ctypes.byref(ms),
                                                            ctypes.byref(n)))
     return ms.value, n.value
+
+
+def _check_block_adapters(A, B, w, S):
+    import torch
+    if A is None or B is None or A.dim() != 2:
+        raise ValueError("A [K, S*r] and B [r, S*nseg] are required")
+    if A.shape[1] % S:
+        raise ValueError(f"A has {A.shape[1]} columns, not a multiple of S = {S}")
+    r = A.shape[1] // S
+    _need(A, "A", (w.K, S * r), torch.bfloat16)
+    _need(B, "B", (r, w.N), torch.bfloat16)
+    return r
+
+
+def qlora_block_fwd(X, w: NF4Weight, S: int, A, B, s: float = 1.0, Y=None, T=None,
+                    workspace=None):
+    """S projections sharing X, stacked along N in w: returns Y [M, S*nseg]
+    (projection j in columns j*nseg ..) and T [M, S*r]."""
+    import torch
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    M = X.shape[0]
+    _need(X, "X", (M, w.K), torch.bfloat16)
+    wt = _check_weight(w)
+    if S < 1 or w.N % S:
+        raise ValueError(f"w.N = {w.N} is not a multiple of S = {S}")
+    r = _check_block_adapters(A, B, w, S)
+    nseg = w.N // S
+    if Y is not None:
+        _need(Y, "Y", (M, w.N), torch.bfloat16)
+    if T is not None:
+        _need(T, "T", (M, S * r), torch.float32)
+    _on_gpu([("X", X)] + wt + [("A", A), ("B", B), ("Y", Y), ("T", T), ("workspace", workspace)])
+    if Y is None:
+        Y = torch.empty((M, w.N), dtype=torch.bfloat16, device=X.device)
+    if T is None:
+        T = torch.empty((M, S * r), dtype=torch.float32, device=X.device)
+    need = lib().qlora_block_fwd_workspace_bytes(M, S, nseg, w.K, r)
+    if workspace is None or workspace.numel() < need:
+        workspace = _ws(need, X.device)
+    cw = w._c()
+    _check("qlora_block_fwd",
+           lib().qlora_block_fwd(_ptr(X), M, ctypes.byref(cw), S, _ptr(A), _ptr(B), r, float(s),
+                                 _ptr(Y), _ptr(T), _ptr(workspace), need, _stream(X)))
+    return Y, T
+
+
+def qlora_block_bwd(dY, X, w: NF4Weight, S: int, A, B, s: float = 1.0, T=None,
+                    need_dx: bool = True, dX=None, dA=None, dB=None, workspace=None):
+    """Backward of the fused block: (dX [M, K] summed over the projections or
+    None, dA [K, S*r], dB [r, S*nseg])."""
+    import torch
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    M = X.shape[0]
+    _need(X, "X", (M, w.K), torch.bfloat16)
+    _need(dY, "dY", (M, w.N), torch.bfloat16)
+    wt = _check_weight(w)
+    if S < 1 or w.N % S:
+        raise ValueError(f"w.N = {w.N} is not a multiple of S = {S}")
+    r = _check_block_adapters(A, B, w, S)
+    nseg = w.N // S
+    if T is not None:
+        _need(T, "T", (M, S * r), torch.float32)
+    _on_gpu([("X", X), ("dY", dY)] + wt + [("A", A), ("B", B), ("T", T)])
+    dev = X.device
+    if need_dx and dX is None:
+        dX = torch.empty((M, w.K), dtype=torch.bfloat16, device=dev)
+    if dA is None:
+        dA = torch.empty((w.K, S * r), dtype=torch.bfloat16, device=dev)
+    if dB is None:
+        dB = torch.empty((r, w.N), dtype=torch.bfloat16, device=dev)
+    need = lib().qlora_block_bwd_workspace_bytes(M, S, nseg, w.K, r)
+    if workspace is None or workspace.numel() < need:
+        workspace = _ws(need, dev)
+    cw = w._c()
+    _check("qlora_block_bwd",
+           lib().qlora_block_bwd(_ptr(dY), _ptr(X), M, ctypes.byref(cw), S, _ptr(A), _ptr(B), r,
+                                 float(s), _ptr(T), _ptr(dX if need_dx else None), _ptr(dA),
+                                 _ptr(dB), _ptr(workspace), need, _stream(X)))
+    return (dX if need_dx else None), dA, dB
 
 
 def qlora_probe_hbm_read(buf, workgroups: int, sink):

@@ -190,6 +190,39 @@ int fwd_impl(const uint16_t* X, int64_t M, const qlora_nf4_weight* w, const uint
 }
 
 // ---------------------------------------------------------------------------
+// Fused multi-projection block: S projections that share their input, stored
+// as one NF4 weight of S * nseg rows with their adapters side by side.
+// ---------------------------------------------------------------------------
+
+// Limits of the block layout: segments aligned to the GEMM's 128-row tiles and
+// to whole groups of 256 block constants (so a segment is a weight of its
+// own), and a combined rank S r the rank products and the dX term take.
+int check_block(const qlora_nf4_weight* w, int S, int r) {
+  if (S < 1 || w->N % S != 0) return QLORA_ERR_SHAPE;
+  const int64_t nseg = w->N / S;
+  if (nseg % 128 != 0 || (nseg * w->K / kBlock) % kGroup != 0) return QLORA_ERR_SHAPE;
+  if (r < 1 || int64_t(S) * r > 256) return QLORA_ERR_RANK;
+  return QLORA_OK;
+}
+
+size_t block_fwd_ws_bytes(int64_t M, int S, int64_t nseg, int64_t K, int r) {
+  size_t f = lora_down_ws_floats(M, K, S * r);
+  if (!decode_fits(M, K)) {
+    const GemmSplit sp = fwd_gemm_split(M, S * nseg, K);
+    if (sp.splits > 1) f = std::max<size_t>(f, (size_t)sp.splits * M * S * nseg);
+  }
+  return round_up(f * sizeof(float), 256);
+}
+
+size_t block_bwd_ws_bytes(int64_t M, int S, int64_t nseg, int64_t K, int r) {
+  const size_t mr = round_up((size_t)M * S * r * sizeof(float), 256);
+  size_t f = std::max(rank_ws_floats(M, nseg, K, r), rank_ws_floats(M, S * nseg, K, S * r));
+  const GemmSplit sp = dx_gemm_split(M, S * nseg, K);
+  if (sp.splits > 1) f = std::max<size_t>(f, (size_t)sp.splits * M * K);
+  return 2 * mr + round_up(f * sizeof(float), 256);
+}
+
+// ---------------------------------------------------------------------------
 // Kernel timing: event pairs around launches, accumulated per family.
 // ---------------------------------------------------------------------------
 
@@ -410,6 +443,97 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
   if (dX) e = launch_dx_gemm(dY, M, v, G, A, r, s, dX, part, tables(), hs);
+  return hip_status(e);
+}
+
+size_t qlora_block_fwd_workspace_bytes(int64_t M, int S, int64_t nseg, int64_t K, int r) {
+  if (M < 1 || S < 1 || nseg < 1 || K < 1 || r < 1) return 0;
+  return block_fwd_ws_bytes(M, S, nseg, K, r);
+}
+
+size_t qlora_block_bwd_workspace_bytes(int64_t M, int S, int64_t nseg, int64_t K, int r) {
+  if (M < 1 || S < 1 || nseg < 1 || K < 1 || r < 1) return 0;
+  return block_bwd_ws_bytes(M, S, nseg, K, r);
+}
+
+int qlora_block_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w, int S,
+                    const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y, float* T,
+                    void* workspace, size_t workspace_bytes, qlora_stream_t stream) {
+  int st = check_fwd_args(X, M, w, A, B, r, Y, T);
+  if (st) return st;
+  if (r == 0) return QLORA_ERR_RANK;
+  if ((st = check_block(w, S, r))) return st;
+  const int64_t nseg = w->N / S;
+  const int rt = S * r;
+  const size_t need = block_fwd_ws_bytes(M, S, nseg, w->K, r);
+  if (!workspace || workspace_bytes < need) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
+
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(workspace);
+  // T = X . [A_0 .. A_{S-1}] for all projections in one product
+  hipError_t e = launch_lora_down(X, M, w->K, A, rt, T, ws, hs);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  if (!decode_fits(M, w->K)) {
+    // one GEMM over all S nseg rows; each row tile adds its own adapter
+    e = launch_fwd_gemm(X, M, view(w), T, B, r, s, Y, ws, tables(), hs, rt, nseg);
+    return hip_status(e);
+  }
+  // few tokens: the streaming kernel per projection (a segment is a whole
+  // weight: its codes, constants and group scales start at group boundaries)
+  const int64_t seg_codes = nseg * w->K / 2, seg_blocks = nseg * w->K / kBlock;
+  for (int j = 0; j < S && e == hipSuccess; ++j) {
+    const Nf4View v{w->codes + j * seg_codes, w->absmax_q + j * seg_blocks,
+                    w->absmax_scale + j * seg_blocks / kGroup, nseg, w->K};
+    // (each projection writes its own columns of Y, row stride S nseg)
+    e = launch_fwd_decode(X, M, v, T + j * r, 0, nullptr, B + j * nseg, r, s, Y + j * nseg,
+                          tables(), hs, rt, w->N, w->N);
+  }
+  return hip_status(e);
+}
+
+int qlora_block_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
+                    int S, const uint16_t* A, const uint16_t* B, int r, float s,
+                    const float* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                    void* workspace, size_t workspace_bytes, qlora_stream_t stream) {
+  int st = check_weight(w);
+  if (st) return st;
+  if ((st = check_rank(r))) return st;
+  if (r == 0) return QLORA_ERR_RANK;
+  if ((st = check_block(w, S, r))) return st;
+  if (!dY || !X || !A || !B || !dA || !dB) return QLORA_ERR_NULL;
+  if (M < 1) return QLORA_ERR_SHAPE;
+  if (!aligned16(dY) || !aligned16(X) || (dX && !aligned16(dX)) || !aligned16(A) ||
+      !aligned16(B) || !aligned16(dA) || !aligned16(dB) || (T_saved && !aligned16(T_saved)))
+    return QLORA_ERR_ALIGN;
+  const int64_t nseg = w->N / S;
+  const int rt = S * r;
+  const size_t need = block_bwd_ws_bytes(M, S, nseg, w->K, r);
+  if (!workspace || workspace_bytes < need) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QLORA_ERR_ALIGN;
+
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  const size_t mr = round_up((size_t)M * rt * sizeof(float), 256);
+  float* G = reinterpret_cast<float*>(base);            // [M][S r]
+  float* Tr = reinterpret_cast<float*>(base + mr);      // [M][S r]
+  float* part = reinterpret_cast<float*>(base + 2 * mr);
+  hipError_t e = hipSuccess;
+  const float* T = T_saved;
+  if (!T) {
+    e = launch_lora_down(X, M, w->K, A, rt, Tr, part, hs);
+    T = Tr;
+  }
+  // per projection: G_j = dY_j . B_j^T and dB_j = s . T_j^T . dY_j, on the
+  // segments' columns of dY, B, dB and the segments' ranks of T and G
+  for (int j = 0; j < S && e == hipSuccess; ++j)
+    e = launch_grad_in_and_b(dY + j * nseg, M, nseg, B + j * nseg, T + j * r, r, s, G + j * r,
+                             dB + j * nseg, part, hs, w->N, w->N, rt);
+  // dA = s . X^T . G for all projections in one product
+  if (e == hipSuccess) e = launch_grad_a(X, M, w->K, G, rt, s, dA, part, hs);
+  // dX = sum_j dY_j . deq(W_j) + s . G_j . A_j^T: one GEMM over all S nseg rows
+  if (e == hipSuccess && dX)
+    e = launch_dx_gemm(dY, M, view(w), G, A, rt, s, dX, part, tables(), hs);
   return hip_status(e);
 }
 

@@ -91,7 +91,8 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
     int64_t N, int64_t K, const float* __restrict__ T, int nz, float* __restrict__ Tout,
     const uint16_t* __restrict__ Bl, int r, float s, uint16_t* __restrict__ Y,
-    Nf4Tables tb, int boff, int toff, int coff, int xoff, float inv_kb) {
+    Nf4Tables tb, int boff, int toff, int coff, int xoff, float inv_kb, int ldt, int ldb,
+    int ldy) {
   constexpr int ROWS = kDecRows;
   constexpr bool XLDS = XP > 0;   // X staged in LDS, XP 16-byte pieces per thread
   // FR = 1: eight waves per fragment; FR = 2: every wave works on both
@@ -169,14 +170,15 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   {
     // (one load sequence for both cases: a branch here would make the
     // compiler wait for the loads of one side before those of the other)
-    const BufRes rt = make_bufres(T, static_cast<uint32_t>((nz > 0 ? nz : 1) * M * r) * 4u);
+    const BufRes rt =
+        make_bufres(T, static_cast<uint32_t>(nz > 0 ? nz * M * r : M * ldt) * 4u);
     const int j = 32 * kw + 8 * g;
     const bool lora_lane = kw < nsteps && li < M && j < r;
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
       const int z = hl + 16 * i;
       const bool ok = nz > 0 ? (hr < nq && z < nz) : (lora_lane && i < 2);
-      const int idx = nz > 0 ? z * M * r + 4 * hr : li * r + j + 4 * i;
+      const int idx = nz > 0 ? z * M * r + 4 * hr : li * ldt + j + 4 * i;
       tq[i] = __builtin_bit_cast(
           f32x4, buf_load16(rt, ok ? static_cast<uint32_t>(idx * 4) : kDecOffNone));
     }
@@ -185,10 +187,10 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // r <= 256), staged in LDS for the LoRA update after the main loop.
   u32x4 bpiece;
   {
-    const BufRes rbl = make_bufres(Bl, static_cast<uint32_t>(r) * static_cast<uint32_t>(N) * 2u);
+    const BufRes rbl = make_bufres(Bl, static_cast<uint32_t>(r) * static_cast<uint32_t>(ldb) * 2u);
     const int j = tid >> 2, c = tid & 3;
     const bool ok = j < r && n0 + 8 * c < N;
-    bpiece = buf_load16(rbl, ok ? static_cast<uint32_t>((j * N + n0 + 8 * c) * 2) : kDecOffNone);
+    bpiece = buf_load16(rbl, ok ? static_cast<uint32_t>((j * ldb + n0 + 8 * c) * 2) : kDecOffNone);
   }
 
   // The code ring: every call issues the same loads, so the compiler can
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     for (int w = 1; w < KS; ++w) t += part(w);
     const int64_t nout = n0 + 16 * po + 4 * g;   // 4 consecutive outputs of token li
     if (li < M && nout < N) {
-      *reinterpret_cast<u32x2*>(Y + (int64_t)li * N + nout) =
+      *reinterpret_cast<u32x2*>(Y + (int64_t)li * ldy + nout) =
           u32x2{pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w)};
     }
   }
@@ -403,7 +405,8 @@ namespace {
 template <int D, int XP, int FR>
 hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w, const float* T,
                                  int nz, float* Tout, const uint16_t* B, int r, float s,
-                                 uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
+                                 uint16_t* Y, const Nf4Tables& tb, hipStream_t stream, int ldt,
+                                 int ldb, int ldy) {
   // allow the largest dynamic LDS (once per variant)
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_fwd_decode<D, XP, FR>),
@@ -415,7 +418,7 @@ hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w,
   const float inv_kb = 1.0f / static_cast<float>(w.K / kBlock);
   hipLaunchKernelGGL((k_fwd_decode<D, XP, FR>), dim3(grid), dim3(kDecThreads), L.total, stream,
                      X, (int)M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, nz, Tout, B,
-                     r, s, Y, tb, L.boff, L.toff, L.coff, L.xoff, inv_kb);
+                     r, s, Y, tb, L.boff, L.toff, L.coff, L.xoff, inv_kb, ldt, ldb, ldy);
   return hipGetLastError();
 }
 
@@ -439,7 +442,11 @@ bool decode_folds_t(int64_t M, int r) {
 
 hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
                              const float* T, int nz, float* Tout, const uint16_t* B, int r,
-                             float s, uint16_t* Y, const Nf4Tables& tb, hipStream_t stream) {
+                             float s, uint16_t* Y, const Nf4Tables& tb, hipStream_t stream,
+                             int ldt, int64_t ldb, int64_t ldy) {
+  if (ldt <= 0) ldt = r;
+  if (ldb <= 0) ldb = w.N;
+  if (ldy <= 0) ldy = w.N;
   prof_begin(2, stream);
   // Two chunks in flight per wave: with all 16 waves of every CU streaming,
   // deeper rings (measured up to 8) only delay the first products.
@@ -451,15 +458,19 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
     const int64_t xbytes = M * w.K * 2;
     const int64_t per_piece = 16 * kDecThreads;
     if (xbytes <= per_piece)
-      e = launch_decode_variant<2, 1, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+      e = launch_decode_variant<2, 1, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream, ldt,
+                                                   static_cast<int>(ldb), static_cast<int>(ldy));
     else if (xbytes <= 2 * per_piece)
-      e = launch_decode_variant<2, 2, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+      e = launch_decode_variant<2, 2, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream, ldt,
+                                                   static_cast<int>(ldb), static_cast<int>(ldy));
     else
-      e = launch_decode_variant<2, kDecXPieces, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+      e = launch_decode_variant<2, kDecXPieces, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream, ldt,
+                                                   static_cast<int>(ldb), static_cast<int>(ldy));
   } else {
     // X from global memory: each wave works on both fragments, so each X
     // piece it loads serves 32 rows.
-    e = launch_decode_variant<2, 0, 2>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream);
+    e = launch_decode_variant<2, 0, 2>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream, ldt,
+                                                   static_cast<int>(ldb), static_cast<int>(ldy));
   }
   prof_end(2, stream);
   return e;

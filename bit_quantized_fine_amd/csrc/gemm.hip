@@ -409,6 +409,8 @@ struct ReduceJob {
   int64_t count;
   float scale;
   void* out;
+  int64_t prow;   // elements per output row (a multiple of 4)
+  int64_t ldo;    // output row stride (prow for a dense output)
 };
 
 template <bool BF16_A, bool BF16_B>
@@ -428,11 +430,12 @@ __global__ __launch_bounds__(256) void k_split_reduce_pair(ReduceJob a, ReduceJo
   for (; z < j.splits; ++z) s0 += *reinterpret_cast<const f32x4*>(j.ws + (int64_t)z * j.count + i);
   f32x4 s = (s0 + s1) + (s2 + s3);
   s *= j.scale;
+  const int64_t row = i / j.prow, o = row * j.ldo + (i - row * j.prow);
   if (first ? BF16_A : BF16_B) {
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(j.out) + i) =
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(j.out) + o) =
         u32x2{pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w)};
   } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(j.out) + i) = s;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(j.out) + o) = s;
   }
 }
 
@@ -664,7 +667,11 @@ hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint1
 
 hipError_t launch_grad_in_and_b(const uint16_t* dY, int64_t M, int64_t N, const uint16_t* B,
                                 const float* T, int r, float s, float* G, uint16_t* dB,
-                                float* ws, hipStream_t stream) {
+                                float* ws, hipStream_t stream, int64_t ldy, int64_t ldb,
+                                int ldt) {
+  if (ldy <= 0) ldy = N;
+  if (ldb <= 0) ldb = N;
+  if (ldt <= 0) ldt = r;
   // G = dY . B^T: tiles (ranks, tokens), split over N
   const int64_t gpt = (r + RB_R - 1) / RB_R, gqt = (M + RB_X - 1) / RB_X;
   const Split gs = choose_split(N, gpt, gqt);
@@ -672,16 +679,16 @@ hipError_t launch_grad_in_and_b(const uint16_t* dY, int64_t M, int64_t N, const 
   const int64_t bpt = (N + RB_X - 1) / RB_X, bqt = (r + RB_R - 1) / RB_R;
   const Split bs = choose_split(M, bpt, bqt);
   float* wsb = ws + (size_t)gs.splits * M * r;
-  const RankJob jg = job(op(B, N, r, N), op(dY, N, M, N), gs, ws, r, M, gpt, gqt);
-  const RankJob jb = job(op(dY, N, N, M), op(T, r, r, M), bs, wsb, N, r, bpt, bqt);
+  const RankJob jg = job(op(B, ldb, r, N), op(dY, ldy, M, N), gs, ws, r, M, gpt, gqt);
+  const RankJob jb = job(op(dY, ldy, N, M), op(T, ldt, r, M), bs, wsb, N, r, bpt, bqt);
   prof_begin(4, stream);
   hipLaunchKernelGGL((k_rank_pair<RB_R, RB_X, Bf16Nat<RB_R>, Bf16Nat<RB_X>, 0, RB_X, RB_R,
                                   Bf16RedMajor<RB_X>, F32RedMajor<RB_R>, 2>),
                      dim3(jg.nblk + jb.nblk), dim3(NT), 0, stream, jg, jb);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess) {
-    const ReduceJob rg{ws, gs.splits, M * r, 1.f, G};
-    const ReduceJob rb{wsb, bs.splits, r * N, s, dB};
+    const ReduceJob rg{ws, gs.splits, M * r, 1.f, G, r, ldt};
+    const ReduceJob rb{wsb, bs.splits, r * N, s, dB, N, ldb};
     const unsigned ga = cdiv(rg.count / 4, 256), gb = cdiv(rb.count / 4, 256);
     hipLaunchKernelGGL((k_split_reduce_pair<false, true>), dim3(ga + gb), dim3(256), 0, stream,
                        rg, rb, static_cast<int>(ga));

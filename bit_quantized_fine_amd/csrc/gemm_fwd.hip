@@ -61,7 +61,7 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
     int64_t N, int64_t K, const float* __restrict__ T, const uint16_t* __restrict__ Bl,
     int r, float s, uint16_t* __restrict__ Y, int ptiles, int qtiles, int cps,
-    float* __restrict__ part, Nf4Tables tb) {
+    float* __restrict__ part, Nf4Tables tb, int ldt, int seg_rows) {
   // Dynamic LDS only (so the table sits at address 0): the replicated level
   // table, then two A tile buffers; after the main loop the same bytes hold
   // the accumulator exchange and the B^T tile of the LoRA update.
@@ -226,6 +226,10 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   // s.T hi / lo halves per lane from global memory.  Each k half takes one
   // of the chunk's two 32-rank steps, before the halves are added.
   if (r > 0 && z == 0) {   // the first split adds the LoRA update
+    // T columns of this tile's segment: rows [j seg_rows, (j + 1) seg_rows)
+    // of W belong to adapter j, whose T occupies columns j r .. of T (row
+    // stride ldt); a single segment is the plain layer.
+    const float* Tt = T + (p0 / seg_rows) * r;
     uint16_t* bt = As;
     for (int j0 = 0; j0 < r; j0 += 64) {
       if (tid < GP) {   // patch tid: rows 8 (tid % 16) .., ranks j0 + 8 (tid / 16) ..
@@ -254,8 +258,8 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
             const int64_t m = q0 + 64 * wt + 16 * b + li;
             uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
             if (m < M && j < r) {
-              const f32x4 t0 = *reinterpret_cast<const f32x4*>(T + m * r + j);
-              const f32x4 t1 = *reinterpret_cast<const f32x4*>(T + m * r + j + 4);
+              const f32x4 t0 = *reinterpret_cast<const f32x4*>(Tt + m * ldt + j);
+              const f32x4 t1 = *reinterpret_cast<const f32x4*>(Tt + m * ldt + j + 4);
               const float v[8] = {t0.x * s, t0.y * s, t0.z * s, t0.w * s,
                                   t1.x * s, t1.y * s, t1.z * s, t1.w * s};
 #pragma unroll
@@ -332,7 +336,8 @@ GemmSplit fwd_gemm_split(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
                             const float* T, const uint16_t* B, int r, float s,
-                            uint16_t* Y, float* part, const Nf4Tables& tb, hipStream_t stream) {
+                            uint16_t* Y, float* part, const Nf4Tables& tb, hipStream_t stream,
+                            int ldt, int64_t seg_rows) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_fwd_gemm), hipFuncAttributeMaxDynamicSharedMemorySize,
       kFwdLds);
@@ -344,7 +349,8 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
   prof_begin(0, stream);
   hipLaunchKernelGGL(k_fwd_gemm, dim3(ptiles * qtiles * sp.splits), dim3(GT), kFwdLds, stream, X,
                      M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, B, r, s, Y, ptiles,
-                     qtiles, sp.cps, sp.splits > 1 ? part : nullptr, tb);
+                     qtiles, sp.cps, sp.splits > 1 ? part : nullptr, tb, ldt > 0 ? ldt : r,
+                     static_cast<int>(seg_rows > 0 ? seg_rows : w.N));
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && sp.splits > 1)
     e = launch_split_reduce_bf16(part, sp.splits, M * w.N, Y, stream);

@@ -44,11 +44,15 @@ hipError_t launch_split_reduce_bf16(const float* part, int splits, int64_t count
 // Y[M,N] = bf16( X . deq(W)^T + s . T . B ), large-M MFMA path with the
 // dequantized weight tiles staged in LDS.  T [M, r] fp32 (may be null when
 // r == 0).  part: fwd_gemm_split(M, N, K).splits * M * N floats when that is
-// above 1 (else unused).
+// above 1 (else unused).  Segments (seg_rows > 0, a multiple of 128): rows
+// [j seg_rows, (j + 1) seg_rows) of W carry adapter j, whose T is columns
+// [j r, (j + 1) r) of T (row stride ldt) and whose B is columns of the same
+// rows of B [r, N]; by default one segment, ldt = r.
 GemmSplit fwd_gemm_split(int64_t M, int64_t N, int64_t K);
 hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
                            const float* T, const uint16_t* B, int r, float s,
-                           uint16_t* Y, float* part, const Nf4Tables& tb, hipStream_t stream);
+                           uint16_t* Y, float* part, const Nf4Tables& tb, hipStream_t stream,
+                           int ldt = 0, int64_t seg_rows = 0);
 
 // Same result, small-M streaming path, for shapes with decode_fits(M, K).
 // decode_folds_t(M, r): the kernel can add up T's partial sums itself.
@@ -56,10 +60,12 @@ bool decode_fits(int64_t M, int64_t K);
 bool decode_folds_t(int64_t M, int r);
 // With nz > 0, T holds nz partial sums [nz][M][r] of X . A which the kernel
 // adds up itself (workgroup 0 also writes the total to Tout); with nz == 0, T
-// is the final [M][r] and Tout is unused.
+// is the final [M][r] with row stride ldt (default r) and Tout is unused.  B
+// and Y have row strides ldb and ldy (default N).
 hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
                              const float* T, int nz, float* Tout, const uint16_t* B, int r,
-                             float s, uint16_t* Y, const Nf4Tables& tb, hipStream_t stream);
+                             float s, uint16_t* Y, const Nf4Tables& tb, hipStream_t stream,
+                             int ldt = 0, int64_t ldb = 0, int64_t ldy = 0);
 
 // dX[M,K] = bf16( dY . deq(W) + s . G . A^T ), MFMA path with the
 // dequantized weight tiles staged in LDS and read back transposed.
@@ -87,10 +93,12 @@ hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K,
                             const uint16_t* A, int r, float* T, float* ws,
                             hipStream_t stream);
 // G[M,r] = dY . B^T (fp32 out) and dB[r,N] = bf16( s . T^T . dY ), both
-// products in one launch and both split reductions in one more.
+// products in one launch and both split reductions in one more.  Row strides
+// (0 = dense): ldy of dY, ldb of B and of dB, ldt of T and of G.
 hipError_t launch_grad_in_and_b(const uint16_t* dY, int64_t M, int64_t N, const uint16_t* B,
                                 const float* T, int r, float s, float* G, uint16_t* dB,
-                                float* ws, hipStream_t stream);
+                                float* ws, hipStream_t stream, int64_t ldy = 0, int64_t ldb = 0,
+                                int ldt = 0);
 // dA[K,r] = bf16( s . X^T . G ).
 hipError_t launch_grad_a(const uint16_t* X, int64_t M, int64_t K, const float* G,
                          int r, float s, uint16_t* dA, float* ws, hipStream_t stream);

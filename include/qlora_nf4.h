@@ -226,6 +226,51 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
                      size_t workspace_bytes, qlora_stream_t stream);
 
 /*
+ * Fused multi-projection block ("LoRA placement: adapters at every layer" of
+ * "QLoRA: Finetuning 65B Models on a Single GPU": adapters on every linear
+ * layer, the query, key and value projections and the MLP's gate and up
+ * projections among them; the rank bullet of the Mathematical Formulation of
+ * "DL0087 QLoRA").  S projections that read the same input X,
+ *     Y_j = X . deq(W_j)^T + s . (X . A_j) . B_j,   j = 0 .. S-1,
+ * computed together: one product T = X . [A_0 .. A_{S-1}] and, for M > 16,
+ * one dequantizing GEMM over all S * nseg weight rows, each row tile adding
+ * its own projection's adapter.
+ *   w  [S*nseg, K]: the S weights stacked along N (nseg = w->N / S), quantized
+ *      as one NF4 weight.  nseg % 128 == 0 and nseg*K % 16384 == 0 (each
+ *      projection starts at a group of 256 block constants, so it equals the
+ *      projection quantized on its own); QLORA_ERR_SHAPE otherwise.
+ *   A  [K, S*r] bf16: A_j in columns j*r .. j*r+r-1.
+ *   B  [r, S*nseg] bf16: B_j in columns j*nseg .. j*nseg+nseg-1.
+ *   Y  [M, S*nseg] bf16 (output): Y_j in the same columns as B_j.
+ *   T  [M, S*r] fp32 (output): T_j = X . A_j in the columns of A_j.
+ *   1 <= r and S*r <= 256, r % 8 == 0 (QLORA_ERR_RANK otherwise).
+ * Workspace: qlora_block_fwd_workspace_bytes(M, S, nseg, K, r) bytes.
+ */
+size_t qlora_block_fwd_workspace_bytes(int64_t M, int S, int64_t nseg, int64_t K, int r);
+int qlora_block_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w, int S,
+                    const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
+                    float* T, void* workspace, size_t workspace_bytes,
+                    qlora_stream_t stream);
+
+/*
+ * Backward of the fused block (list item (4) of "DL0087 QLoRA"): with dY
+ * [M, S*nseg] holding dY_j in the columns of Y_j,
+ *   G_j = dY_j . B_j^T, dB_j = s . T_j^T . dY_j   (dB [r, S*nseg], like B)
+ *   dA  = s . X^T . [G_0 .. G_{S-1}]              (dA [K, S*r], like A)
+ *   dX  = sum_j dY_j . deq(W_j) + s . G_j . A_j^T (one GEMM over all rows;
+ *         skipped if dX == NULL)
+ * T_saved is the forward's T [M, S*r], or NULL to recompute it.  Shapes,
+ * limits and errors as for qlora_block_fwd; workspace:
+ * qlora_block_bwd_workspace_bytes(M, S, nseg, K, r) bytes.
+ */
+size_t qlora_block_bwd_workspace_bytes(int64_t M, int S, int64_t nseg, int64_t K, int r);
+int qlora_block_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
+                    const qlora_nf4_weight* w, int S, const uint16_t* A,
+                    const uint16_t* B, int r, float s, const float* T_saved,
+                    uint16_t* dX, uint16_t* dA, uint16_t* dB, void* workspace,
+                    size_t workspace_bytes, qlora_stream_t stream);
+
+/*
  * Kernel timing for measurement.  When enabled (enable != 0), the library
  * records a pair of HIP events on the launch stream around every launch of
  * the kernel families below and accumulates their elapsed times; reading

@@ -64,3 +64,48 @@ def linear_bwd(dY_bits, X_bits, W_bits, A_bits, B_bits, s, need_dx=True):
     return linear_bwd_f64(bf16_bits_to_f64(dY_bits), bf16_bits_to_f64(X_bits), W,
                           bf16_bits_to_f64(A_bits), bf16_bits_to_f64(B_bits), s,
                           need_dx=need_dx)
+
+
+# ---------------------------------------------------------------------------
+# Several projections that read the same input ("LoRA placement: adapters at
+# every layer" of "QLoRA: Finetuning 65B Models on a Single GPU": adapters on
+# every linear layer -- the query, key and value projections of attention, the
+# gate and up projections of the MLP -- which share their input).
+# ---------------------------------------------------------------------------
+
+def block_fwd_f64(X, Ws, As, Bs, s):
+    """Projections j = 0..S-1 of one input X (float64 operands): lists of Y_j
+    and T_j, each the single-layer forward of projection j."""
+    outs = [linear_fwd_f64(X, W, A, B, s) for W, A, B in zip(Ws, As, Bs)]
+    return [o[0] for o in outs], [o[1] for o in outs]
+
+
+def block_bwd_f64(dYs, X, Ws, As, Bs, s, need_dx=True):
+    """Backward of the projections of one input (float64 operands).  X feeds
+    all of them, so its gradient is the sum of the projections' input
+    gradients; each adapter pair gets its own projection's gradients.
+    Returns (dX or None, list of dA_j, list of dB_j)."""
+    dX, dAs, dBs = None, [], []
+    for dY, W, A, B in zip(dYs, Ws, As, Bs):
+        dXj, dAj, dBj = linear_bwd_f64(dY, X, W, A, B, s, need_dx=need_dx)
+        if need_dx:
+            dX = dXj if dX is None else dX + dXj
+        dAs.append(dAj)
+        dBs.append(dBj)
+    return dX, dAs, dBs
+
+
+def block_fwd(X_bits, W_bits_list, A_bits_list, B_bits_list, s):
+    """block_fwd_f64 from bf16 bit patterns."""
+    return block_fwd_f64(bf16_bits_to_f64(X_bits), [bf16_bits_to_f64(W) for W in W_bits_list],
+                         [bf16_bits_to_f64(A) for A in A_bits_list],
+                         [bf16_bits_to_f64(B) for B in B_bits_list], s)
+
+
+def block_bwd(dY_bits_list, X_bits, W_bits_list, A_bits_list, B_bits_list, s, need_dx=True):
+    """block_bwd_f64 from bf16 bit patterns."""
+    return block_bwd_f64([bf16_bits_to_f64(d) for d in dY_bits_list], bf16_bits_to_f64(X_bits),
+                         [bf16_bits_to_f64(W) for W in W_bits_list] if need_dx
+                         else [None] * len(dY_bits_list),
+                         [bf16_bits_to_f64(A) for A in A_bits_list],
+                         [bf16_bits_to_f64(B) for B in B_bits_list], s, need_dx=need_dx)

@@ -425,3 +425,102 @@ def test_b_zero_gives_zero_dA():
     dX, dA, dB = oracle.linear_bwd_f64(dY, X, W, A, np.zeros((2, 8)), 1.0)
     assert np.all(dA == 0)
     assert np.any(dB != 0)
+
+
+# ---------------------------------------------------------------------------
+# Projections that share their input (the fused block)
+# ---------------------------------------------------------------------------
+
+def test_block_bwd_finite_differences():
+    """L = sum_j <dY_j, Y_j> over three projections of one X: central
+    differences of every entry of X, A_j and B_j (exact for this affine loss)
+    equal the block's gradients; a dropped or doubled projection in dX fails."""
+    rng = np.random.default_rng(14)
+    M, K, N, r, s, S = 2, 64, 16, 2, 0.75, 3
+    X = _rand(rng, M, K)
+    Ws = [_rand(rng, N, K) for _ in range(S)]
+    As = [_rand(rng, K, r) for _ in range(S)]
+    Bs = [_rand(rng, r, N) for _ in range(S)]
+    dYs = [_rand(rng, M, N) for _ in range(S)]
+    dX, dAs, dBs = oracle.block_bwd_f64(dYs, X, Ws, As, Bs, s)
+
+    def L(X_, As_, Bs_):
+        Ys, _ = oracle.block_fwd_f64(X_, Ws, As_, Bs_, s)
+        return float(sum(np.sum(d * y) for d, y in zip(dYs, Ys)))
+
+    h = 0.5
+
+    def fd_of(get, put, shape):
+        g = np.empty(shape)
+        for idx in np.ndindex(shape):
+            v = get()[idx]
+            put(idx, v + h)
+            lp = L(Xc[0], Ac, Bc)
+            put(idx, v - h)
+            lm = L(Xc[0], Ac, Bc)
+            put(idx, v)
+            g[idx] = (lp - lm) / (2 * h)
+        return g
+
+    Xc, Ac, Bc = [X.copy()], [a.copy() for a in As], [b.copy() for b in Bs]
+    fdX = fd_of(lambda: Xc[0], lambda i, v: Xc[0].__setitem__(i, v), X.shape)
+    assert np.linalg.norm(fdX - dX) / np.linalg.norm(dX) < 1e-9
+    for j in range(S):
+        fdA = fd_of(lambda: Ac[j], lambda i, v: Ac[j].__setitem__(i, v), As[j].shape)
+        fdB = fd_of(lambda: Bc[j], lambda i, v: Bc[j].__setitem__(i, v), Bs[j].shape)
+        assert np.linalg.norm(fdA - dAs[j]) / np.linalg.norm(dAs[j]) < 1e-9
+        assert np.linalg.norm(fdB - dBs[j]) / np.linalg.norm(dBs[j]) < 1e-9
+
+
+def test_block_matches_torch_autograd_with_shared_input():
+    """torch: one X tensor feeding three linear + LoRA branches."""
+    rng = np.random.default_rng(15)
+    M, K, N, r, s = 4, 96, 40, 8, 0.25
+    X = _rand(rng, M, K)
+    Ws = [_rand(rng, N, K) for _ in range(3)]
+    As = [_rand(rng, K, r) for _ in range(3)]
+    Bs = [_rand(rng, r, N) for _ in range(3)]
+    dYs = [_rand(rng, M, N) for _ in range(3)]
+    tX = torch.tensor(X, requires_grad=True)
+    tA = [torch.tensor(a, requires_grad=True) for a in As]
+    tB = [torch.tensor(b, requires_grad=True) for b in Bs]
+    loss = 0
+    for j in range(3):
+        Y = torch.nn.functional.linear(tX, torch.from_numpy(Ws[j])) + s * (tX @ tA[j]) @ tB[j]
+        loss = loss + (Y * torch.from_numpy(dYs[j])).sum()
+    loss.backward()
+    dX, dAs, dBs = oracle.block_bwd_f64(dYs, X, Ws, As, Bs, s)
+    np.testing.assert_allclose(dX, tX.grad.numpy(), rtol=1e-12, atol=1e-12)
+    for j in range(3):
+        np.testing.assert_allclose(dAs[j], tA[j].grad.numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dBs[j], tB[j].grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_block_b_zero_is_the_stacked_linear():
+    """With every B_j = 0 the projections' outputs side by side are one linear
+    layer with the weights stacked along N (torch F.linear)."""
+    rng = np.random.default_rng(16)
+    X = _rand(rng, 5, 64)
+    Ws = [_rand(rng, 24, 64) for _ in range(3)]
+    As = [_rand(rng, 64, 8) for _ in range(3)]
+    Bs = [np.zeros((8, 24)) for _ in range(3)]
+    Ys, _ = oracle.block_fwd_f64(X, Ws, As, Bs, 0.5)
+    ref = torch.nn.functional.linear(torch.from_numpy(X),
+                                     torch.from_numpy(np.concatenate(Ws, axis=0))).numpy()
+    np.testing.assert_allclose(np.concatenate(Ys, axis=1), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_stacked_weight_quantizes_like_its_parts():
+    """Weights whose blocks fill whole groups of 256 constants (N K a multiple
+    of 64 * 256) quantize stacked along N exactly as one by one: the codes,
+    8-bit constants and group scales are the parts' side by side.  A part
+    that does not fill its last group changes the next part's scales."""
+    rng = np.random.default_rng(17)
+    parts = [workloads.draw_weight(rng, 128, 128) for _ in range(3)]   # 256 blocks each
+    whole = oracle.quantize(np.concatenate(parts, axis=0))
+    each = [oracle.quantize(p) for p in parts]
+    for i in range(3):
+        np.testing.assert_array_equal(whole[i], np.concatenate([e[i] for e in each]))
+    odd = [workloads.draw_weight(rng, 96, 128) for _ in range(2)]          # 192 blocks each
+    whole = oracle.quantize(np.concatenate(odd, axis=0))
+    assert not np.array_equal(whole[2], np.concatenate([oracle.quantize(p)[2] for p in odd]))
