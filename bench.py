@@ -166,6 +166,95 @@ def run_training(q, torch, steps, warmup, dev, key="llama7b", M=None):
                 fam=fam, fwd_flops=fwd_flops, dx_flops=dx_flops, cfg=cfg)
 
 
+def run_training_fused(q, torch, steps, warmup, dev, M=None):
+    """The LLaMA-7B layer's seven linears as a transformer layer runs them:
+    q, k, v read one input and run as one fused block (S = 3, 4096 rows
+    each), o alone, gate and up as one block (S = 2, 11008 rows each), down
+    alone.  The weights, adapters and output gradients are the per-linear
+    workload's; the blocks take q's and gate's input.  Same flops as the
+    per-linear step (the input gradient of a block is the sum of its
+    projections')."""
+    import numpy as np
+
+    import workloads
+    cfg = workloads.WORKLOADS["llama7b"]
+    M, r, s = (cfg.M[0] if M is None else M), cfg.r, cfg.s
+    ins = list(workloads.workload_inputs("llama7b", M=M))
+    groups = [[0, 1, 2], [3], [4, 5], [6]]
+    units = []
+    for g in groups:
+        lins = [ins[i][0] for i in g]
+        W = np.concatenate([ins[i][1].W for i in g], axis=0)
+        A = np.concatenate([ins[i][1].A for i in g], axis=1)
+        B = np.concatenate([ins[i][1].B for i in g], axis=1)
+        dY = np.concatenate([ins[i][1].dY for i in g], axis=1)
+        S = len(g)
+        u = dict(S=S, lins=lins, w=q.qlora_nf4_quantize(torch.from_numpy(W).to(dev)),
+                 X=bf16_dev(ins[g[0]][1].X, dev), A=bf16_dev(np.ascontiguousarray(A), dev),
+                 B=bf16_dev(np.ascontiguousarray(B), dev), dY=bf16_dev(np.ascontiguousarray(dY), dev))
+        N, K = W.shape
+        u["Y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        u["T"] = torch.empty((M, S * r), dtype=torch.float32, device=dev)
+        u["dX"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        u["dA"] = torch.empty((K, S * r), dtype=torch.bfloat16, device=dev)
+        u["dB"] = torch.empty((r, N), dtype=torch.bfloat16, device=dev)
+        if S > 1:
+            u["wsf"] = torch.empty(q.lib().qlora_block_fwd_workspace_bytes(M, S, N // S, K, r),
+                                   dtype=torch.uint8, device=dev)
+            u["wsb"] = torch.empty(q.lib().qlora_block_bwd_workspace_bytes(M, S, N // S, K, r),
+                                   dtype=torch.uint8, device=dev)
+        else:
+            u["wsf"] = torch.empty(q.lib().qlora_linear_fwd_workspace_bytes(M, N, K, r),
+                                   dtype=torch.uint8, device=dev)
+            u["wsb"] = torch.empty(q.lib().qlora_linear_bwd_workspace_bytes(M, N, K, r),
+                                   dtype=torch.uint8, device=dev)
+        units.append(u)
+    del ins
+    torch.cuda.synchronize()
+
+    def step():
+        for u in units:
+            if u["S"] > 1:
+                q.qlora_block_fwd(u["X"], u["w"], u["S"], u["A"], u["B"], s, Y=u["Y"], T=u["T"],
+                                  workspace=u["wsf"])
+                q.qlora_block_bwd(u["dY"], u["X"], u["w"], u["S"], u["A"], u["B"], s, T=u["T"],
+                                  dX=u["dX"], dA=u["dA"], dB=u["dB"], workspace=u["wsb"])
+            else:
+                q.qlora_linear_fwd(u["X"], u["w"], u["A"], u["B"], s, Y=u["Y"], T=u["T"],
+                                   workspace=u["wsf"])
+                q.qlora_linear_bwd(u["dY"], u["X"], u["w"], u["A"], u["B"], s, T=u["T"],
+                                   dX=u["dX"], dA=u["dA"], dB=u["dB"], workspace=u["wsb"])
+
+    for _ in range(warmup):
+        step()
+    step()
+    torch.cuda.synchronize()
+    outs = ("Y", "T", "dX", "dA", "dB")
+    eager = [[u[k].clone() for k in outs] for u in units]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    for u, ref in zip(units, eager):
+        for k, t in zip(outs, ref):
+            if not torch.equal(u[k], t):
+                raise RuntimeError(f"fused step: graph replay differs from the eager step ({k})")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    del graph
+    flops = sum(linear_flops(M, l.N, l.K, r) for u in units for l in u["lins"])
+    return dict(ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12,
+                step_ms_p10_p50_p90=percentiles(per_step), tokens=M,
+                blocks="q/k/v fused (S=3), o, gate/up fused (S=2), down")
+
+
 def run_stack(q, torch, dev, steps=2, warmup=1):
     """The 65B-shaped stack with the whole NF4 base resident: 80 layers x 7
     linears (hidden 8192, FFN 22016), every weight drawn and quantized on the
@@ -608,6 +697,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured-peak probes (4 GiB streaming read, bf16 MFMA loop)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the extra step with q/k/v and gate/up run as fused blocks")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the extra step at one GPU's share of 8-way data parallelism "
                          "(256 of the 2048 tokens)")
@@ -713,6 +804,12 @@ def main():
     if not args.no_decode:
         decode = run_decode(q, torch, dev, reps=args.decode_reps)
 
+    fused = None
+    if args.workload == "llama7b" and not args.no_fused:
+        fused = run_training_fused(q, torch, args.steps, args.warmup, dev)
+        log(f"fused-block step (q/k/v and gate/up as blocks): {fused['ms_per_step']:.3f} ms, "
+            f"{fused['tflops']:.1f} TFLOP/s")
+
     shard = None
     if args.workload == "llama7b" and not args.no_shard:
         # extra data point: the same step at the per-GPU share of 8-way data
@@ -774,6 +871,7 @@ def main():
         "cpu_baseline": cpu,
         "measured_peaks": peaks,
         "decode_m1_gbs": None if decode is None else decode["M=1"]["gbs_call"],
+        "fused_block_step": fused,
         "dp8_shard": shard,
         "decode": decode,
         "kernels": kernels,
