@@ -76,20 +76,29 @@ def percentiles(xs):
     return [float(v) for v in np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])]
 
 
-def run_training(q, torch, steps, warmup, dev, key="llama7b", M=None):
+def run_training(q, torch, steps, warmup, dev, key="llama7b", M=None, form="nf4"):
     """One step = fwd + bwd of the workload's seven linears.  The 33B workload
     runs the backward as under gradient checkpointing: T is not kept, the
-    backward recomputes it (and dequantizes W again, as every backward does)."""
+    backward recomputes it (and dequantizes W again, as every backward does).
+    form "lora16" runs the same step with bf16 base weights on the same
+    kernels (the 16-bit LoRA comparator) instead of NF4 ones."""
     import numpy as np
 
     import workloads
     cfg = workloads.WORKLOADS[key]
     M, r, s = (cfg.M[0] if M is None else M), cfg.r, cfg.s
     recompute = key == "llama33b_recompute"
+    dense = form == "lora16"
+    ws_fwd = (q.lib().qlora_lora16_fwd_workspace_bytes if dense
+              else q.lib().qlora_linear_fwd_workspace_bytes)
+    ws_bwd = (q.lib().qlora_lora16_bwd_workspace_bytes if dense
+              else q.lib().qlora_linear_bwd_workspace_bytes)
     layers = []
     t0 = time.time()
     for lin, inp in workloads.workload_inputs(key, M=M):
-        w = q.qlora_nf4_quantize(torch.from_numpy(inp.W).to(dev))
+        Wg = torch.from_numpy(inp.W).to(dev)
+        w = Wg.to(torch.bfloat16) if dense else q.qlora_nf4_quantize(Wg)
+        del Wg
         L = dict(lin=lin, w=w, X=bf16_dev(inp.X, dev), A=bf16_dev(inp.A, dev),
                  B=bf16_dev(inp.B, dev), dY=bf16_dev(inp.dY, dev))
         L["Y"] = torch.empty((M, lin.N), dtype=torch.bfloat16, device=dev)
@@ -97,21 +106,20 @@ def run_training(q, torch, steps, warmup, dev, key="llama7b", M=None):
         L["dX"] = torch.empty((M, lin.K), dtype=torch.bfloat16, device=dev)
         L["dA"] = torch.empty((lin.K, r), dtype=torch.bfloat16, device=dev)
         L["dB"] = torch.empty((r, lin.N), dtype=torch.bfloat16, device=dev)
-        L["wsf"] = torch.empty(q.lib().qlora_linear_fwd_workspace_bytes(M, lin.N, lin.K, r),
-                               dtype=torch.uint8, device=dev)
-        L["wsb"] = torch.empty(q.lib().qlora_linear_bwd_workspace_bytes(M, lin.N, lin.K, r),
-                               dtype=torch.uint8, device=dev)
+        L["wsf"] = torch.empty(ws_fwd(M, lin.N, lin.K, r), dtype=torch.uint8, device=dev)
+        L["wsb"] = torch.empty(ws_bwd(M, lin.N, lin.K, r), dtype=torch.uint8, device=dev)
         layers.append(L)
     torch.cuda.synchronize()
-    log(f"setup (draw + upload + quantize {len(layers)} linears): {time.time() - t0:.1f}s")
+    log(f"setup (draw + upload + {'convert' if dense else 'quantize'} {len(layers)} linears): "
+        f"{time.time() - t0:.1f}s")
+    fwd = q.qlora_lora16_fwd if dense else q.qlora_linear_fwd
+    bwd = q.qlora_lora16_bwd if dense else q.qlora_linear_bwd
 
     def step():
         for L in layers:
-            q.qlora_linear_fwd(L["X"], L["w"], L["A"], L["B"], s, Y=L["Y"], T=L["T"],
-                               workspace=L["wsf"])
-            q.qlora_linear_bwd(L["dY"], L["X"], L["w"], L["A"], L["B"], s,
-                               T=None if recompute else L["T"],
-                               dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["wsb"])
+            fwd(L["X"], L["w"], L["A"], L["B"], s, Y=L["Y"], T=L["T"], workspace=L["wsf"])
+            bwd(L["dY"], L["X"], L["w"], L["A"], L["B"], s, T=None if recompute else L["T"],
+                dX=L["dX"], dA=L["dA"], dB=L["dB"], workspace=L["wsb"])
 
     for _ in range(warmup):
         step()
@@ -164,6 +172,74 @@ def run_training(q, torch, steps, warmup, dev, key="llama7b", M=None):
                 step_ms_pct=percentiles(per_step),
                 flops_step=flops_step,
                 fam=fam, fwd_flops=fwd_flops, dx_flops=dx_flops, cfg=cfg)
+
+
+def run_training_torch16(torch, steps, warmup, dev, M=None):
+    """Context for the 16-bit LoRA comparator: the same LLaMA-7B layer step as
+    plain bf16 torch matmuls (the vendor GEMM library), the way a framework's
+    autograd runs a LoRA linear over a bf16 base weight:
+      fwd  T = X A, Y = X W^T + s T B
+      bwd  G = dY B^T, dX = dY W + s G A^T, dA = s X^T G, dB = s T^T dY
+    (T and G in bf16, as autograd keeps them).  Timed by graph replay when the
+    library's calls capture and replay to the eager result, else eagerly."""
+    import torch.nn.functional as F
+
+    import workloads
+    cfg = workloads.WORKLOADS["llama7b"]
+    M, r, s = (cfg.M[0] if M is None else M), cfg.r, cfg.s
+    layers = []
+    for lin, inp in workloads.workload_inputs("llama7b", M=M):
+        layers.append(dict(lin=lin, W=torch.from_numpy(inp.W).to(dev).to(torch.bfloat16),
+                           X=bf16_dev(inp.X, dev), A=bf16_dev(inp.A, dev),
+                           B=bf16_dev(inp.B, dev), dY=bf16_dev(inp.dY, dev)))
+    torch.cuda.synchronize()
+
+    def step():
+        outs = []
+        for L in layers:
+            X, W, A, B, dY = L["X"], L["W"], L["A"], L["B"], L["dY"]
+            T = torch.matmul(X, A)
+            Y = torch.addmm(F.linear(X, W), T, B, alpha=s)
+            G = F.linear(dY, B)
+            dX = torch.addmm(torch.matmul(dY, W), G, A.t(), alpha=s)
+            dA = torch.matmul(X.t(), G).mul_(s)
+            dB = torch.matmul(T.t(), dY).mul_(s)
+            outs.append((Y, dX, dA, dB))
+        return outs
+
+    for _ in range(warmup):
+        step()
+    ref = step()
+    torch.cuda.synchronize()
+    mode = "graph replay"
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            got = step()
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            for a, b in zip(ref, got):
+                for x, y in zip(a, b):
+                    if not torch.equal(x, y):
+                        raise RuntimeError("replay differs from the eager step")
+        run = graph.replay
+    except Exception as e:   # the eager step is the comparator then
+        log(f"torch 16-bit LoRA step: no graph ({e}); timing it eagerly")
+        mode, graph, run = "eager", None, step
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        run()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    del graph
+    flops = sum(linear_flops(M, L["lin"].N, L["lin"].K, r) for L in layers)
+    return dict(ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12, timing=mode,
+                step_ms_p10_p50_p90=percentiles(per_step), tokens=M,
+                what="bf16 torch matmuls (F.linear / addmm / matmul), T and G in bf16")
 
 
 def run_training_fused(q, torch, steps, warmup, dev, M=None):
@@ -697,6 +773,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured-peak probes (4 GiB streaming read, bf16 MFMA loop)")
+    ap.add_argument("--no-lora16", action="store_true",
+                    help="skip the 16-bit LoRA comparator steps (bf16 base weight)")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the extra step with q/k/v and gate/up run as fused blocks")
     ap.add_argument("--no-shard", action="store_true",
@@ -810,6 +888,26 @@ def main():
         log(f"fused-block step (q/k/v and gate/up as blocks): {fused['ms_per_step']:.3f} ms, "
             f"{fused['tflops']:.1f} TFLOP/s")
 
+    lora16 = torch16 = None
+    if args.workload == "llama7b" and not args.no_lora16:
+        l16 = run_training(q, torch, args.steps, args.warmup, dev, key="llama7b", form="lora16")
+        lora16 = dict(ms_per_step=l16["ms_step"],
+                      tflops=l16["flops_step"] / (l16["ms_step"] * 1e-3) / 1e12,
+                      step_ms_p10_p50_p90=l16["step_ms_pct"],
+                      kernels={k: dict(ms_per_step=ms / args.steps,
+                                       avg_launch_us=1e3 * ms / n)
+                               for k, (ms, n) in l16["fam"].items() if n},
+                      nf4_over_lora16_time=tr["ms_step"] / l16["ms_step"],
+                      what="the same step with bf16 base weights on the same kernels "
+                           "(weight tile loaded instead of dequantized)")
+        log(f"16-bit LoRA step (same kernels, bf16 W): {l16['ms_step']:.3f} ms, "
+            f"{lora16['tflops']:.1f} TFLOP/s; NF4/bf16 time {lora16['nf4_over_lora16_time']:.3f}; "
+            f"kernels {lora16['kernels']}")
+        del l16
+        torch16 = run_training_torch16(torch, args.steps, args.warmup, dev)
+        log(f"16-bit LoRA step as torch bf16 matmuls: {torch16['ms_per_step']:.3f} ms "
+            f"({torch16['timing']}), {torch16['tflops']:.1f} TFLOP/s")
+
     shard = None
     if args.workload == "llama7b" and not args.no_shard:
         # extra data point: the same step at the per-GPU share of 8-way data
@@ -872,6 +970,8 @@ def main():
         "measured_peaks": peaks,
         "decode_m1_gbs": None if decode is None else decode["M=1"]["gbs_call"],
         "fused_block_step": fused,
+        "lora16_step": lora16,
+        "torch_lora16_step": torch16,
         "dp8_shard": shard,
         "decode": decode,
         "kernels": kernels,

@@ -77,6 +77,21 @@ _SIGS = {
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]),
+    "qlora_lora16_fwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64,
+                                                           ctypes.c_int64, ctypes.c_int]),
+    "qlora_lora16_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64,
+                                                           ctypes.c_int64, ctypes.c_int]),
+    "qlora_lora16_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]),
+    "qlora_lora16_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]),
     "qlora_probe_hbm_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_void_p]),
     "qlora_probe_mfma_bf16": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
@@ -360,6 +375,94 @@ def qlora_linear_bwd(dY, X, w: NF4Weight, A=None, B=None, s: float = 1.0, T=None
            lib().qlora_linear_bwd(_ptr(dY), _ptr(X), M, ctypes.byref(cw), _ptr(A), _ptr(B),
                                   r, float(s), _ptr(T), _ptr(dX if need_dx else None),
                                   _ptr(dA), _ptr(dB), _ptr(workspace), need, _stream(X)))
+    return (dX if need_dx else None), dA, dB
+
+
+class _Shape(NamedTuple):
+    N: int
+    K: int
+
+
+def _dense_weight(W):
+    import torch
+    if W.dim() != 2:
+        raise ValueError("W must be [N, K]")
+    _need(W, "W", tuple(W.shape), torch.bfloat16)
+    return _Shape(int(W.shape[0]), int(W.shape[1]))
+
+
+def qlora_lora16_fwd(X, W, A=None, B=None, s: float = 1.0, Y=None, T=None, workspace=None):
+    """16-bit LoRA forward on the same kernels: Y = X . W^T + s . (X . A) . B
+    with a bf16 base weight W [N, K].  Returns (Y bf16 [M,N], T fp32 [M,r])."""
+    import torch
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    w = _dense_weight(W)
+    M = X.shape[0]
+    _need(X, "X", (M, w.K), torch.bfloat16)
+    r = _check_adapters(A, B, w)
+    if Y is not None:
+        _need(Y, "Y", (M, w.N), torch.bfloat16)
+    if T is not None and r > 0:
+        _need(T, "T", (M, r), torch.float32)
+    if workspace is not None:
+        _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
+    _on_gpu([("X", X), ("W", W), ("A", A), ("B", B), ("Y", Y), ("T", T if r > 0 else None),
+             ("workspace", workspace)])
+    dev = X.device
+    if Y is None:
+        Y = torch.empty((M, w.N), dtype=torch.bfloat16, device=dev)
+    if T is None and r > 0:
+        T = torch.empty((M, r), dtype=torch.float32, device=dev)
+    need = lib().qlora_lora16_fwd_workspace_bytes(M, w.N, w.K, r)
+    if workspace is None or workspace.numel() < need:
+        workspace = _ws(need, dev)
+    _check("qlora_lora16_fwd",
+           lib().qlora_lora16_fwd(_ptr(X), M, _ptr(W), w.N, w.K, _ptr(A), _ptr(B), r, float(s),
+                                  _ptr(Y), _ptr(T), _ptr(workspace), need, _stream(X)))
+    return Y, T
+
+
+def qlora_lora16_bwd(dY, X, W, A=None, B=None, s: float = 1.0, T=None, need_dx: bool = True,
+                     dX=None, dA=None, dB=None, workspace=None):
+    """16-bit LoRA backward: (dX bf16 [M,K] or None, dA bf16 [K,r], dB bf16
+    [r,N]) with a bf16 base weight W [N, K]; T None recomputes X . A."""
+    import torch
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    w = _dense_weight(W)
+    M = X.shape[0]
+    _need(X, "X", (M, w.K), torch.bfloat16)
+    _need(dY, "dY", (M, w.N), torch.bfloat16)
+    r = _check_adapters(A, B, w)
+    if T is not None and r > 0:
+        _need(T, "T", (M, r), torch.float32)
+    if need_dx and dX is not None:
+        _need(dX, "dX", (M, w.K), torch.bfloat16)
+    if r > 0 and dA is not None:
+        _need(dA, "dA", (w.K, r), torch.bfloat16)
+    if r > 0 and dB is not None:
+        _need(dB, "dB", (r, w.N), torch.bfloat16)
+    if workspace is not None:
+        _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
+    _on_gpu([("X", X), ("dY", dY), ("W", W), ("A", A), ("B", B), ("T", T if r > 0 else None),
+             ("dX", dX if need_dx else None), ("dA", dA if r > 0 else None),
+             ("dB", dB if r > 0 else None), ("workspace", workspace)])
+    dev = X.device
+    if need_dx and dX is None:
+        dX = torch.empty((M, w.K), dtype=torch.bfloat16, device=dev)
+    if r > 0:
+        if dA is None:
+            dA = torch.empty((w.K, r), dtype=torch.bfloat16, device=dev)
+        if dB is None:
+            dB = torch.empty((r, w.N), dtype=torch.bfloat16, device=dev)
+    need = lib().qlora_lora16_bwd_workspace_bytes(M, w.N, w.K, r)
+    if workspace is None or workspace.numel() < need:
+        workspace = _ws(need, dev)
+    _check("qlora_lora16_bwd",
+           lib().qlora_lora16_bwd(_ptr(dY), _ptr(X), M, _ptr(W), w.N, w.K, _ptr(A), _ptr(B), r,
+                                  float(s), _ptr(T), _ptr(dX if need_dx else None), _ptr(dA),
+                                  _ptr(dB), _ptr(workspace), need, _stream(X)))
     return (dX if need_dx else None), dA, dB
 
 

@@ -189,6 +189,75 @@ int fwd_impl(const uint16_t* X, int64_t M, const qlora_nf4_weight* w, const uint
   return hip_status(e);
 }
 
+// The backward once the weight is checked (either form); ws as bwd_ws_bytes.
+int bwd_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const Nf4View& v,
+             const uint16_t* A, const uint16_t* B, int r, float s, const float* T_saved,
+             uint16_t* dX, uint16_t* dA, uint16_t* dB, void* workspace, size_t workspace_bytes,
+             hipStream_t hs) {
+  int st = check_rank(r);
+  if (st) return st;
+  if (!dY || !X) return QLORA_ERR_NULL;
+  if (r > 0 && (!A || !B || !dA || !dB)) return QLORA_ERR_NULL;
+  if (M < 1 || v.N % 8 != 0) return QLORA_ERR_SHAPE;
+  if (!aligned16(dY) || !aligned16(X) || (dX && !aligned16(dX)) ||
+      (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB) ||
+                 (T_saved && !aligned16(T_saved)))))
+    return QLORA_ERR_ALIGN;
+  const size_t need = bwd_ws_bytes(M, v.N, v.K, r);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return QLORA_ERR_ALIGN;
+
+  hipError_t e = hipSuccess;
+  float* G = nullptr;
+  char* base = static_cast<char*>(workspace);
+  const size_t mr = r > 0 ? round_up((size_t)M * r * sizeof(float), 256) : 0;
+  float* part = base ? reinterpret_cast<float*>(base + 2 * mr) : nullptr;
+  if (r > 0) {
+    G = reinterpret_cast<float*>(base);
+    float* Tr = reinterpret_cast<float*>(base + mr);
+    const float* T = T_saved;
+    if (!T) {
+      e = launch_lora_down(X, M, v.K, A, r, Tr, part, hs);
+      T = Tr;
+    }
+    if (e == hipSuccess) e = launch_grad_in_and_b(dY, M, v.N, B, T, r, s, G, dB, part, hs);
+    if (e == hipSuccess) e = launch_grad_a(X, M, v.K, G, r, s, dA, part, hs);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+  }
+  if (dX) e = launch_dx_gemm(dY, M, v, G, A, r, s, dX, part, tables(), hs);
+  return hip_status(e);
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit LoRA: the same kernels over a bf16 weight [N, K] (no quantization),
+// the baseline QLoRA's speed is set against.
+// ---------------------------------------------------------------------------
+
+// The kernels address the bf16 weight with 32-bit byte offsets below 2^31.
+constexpr int64_t kMaxDenseElems = int64_t(1) << 30;
+
+int check_dense(const uint16_t* W, int64_t N, int64_t K) {
+  if (!W) return QLORA_ERR_NULL;
+  if (N < 1 || N % 8 != 0 || K < kBlock || K % kBlock != 0) return QLORA_ERR_SHAPE;
+  if (K > kMaxK || N > kMaxN || N > kMaxDenseElems / K) return QLORA_ERR_SHAPE;
+  if (!aligned16(W)) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+Nf4View dense_view(const uint16_t* W, int64_t N, int64_t K) {
+  Nf4View v{nullptr, nullptr, nullptr, N, K};
+  v.dense = W;
+  return v;
+}
+
+// The tiled GEMM at every M (no streaming path for the bf16 weight).
+size_t dense_fwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
+  size_t f = lora_down_ws_floats(M, K, r);
+  const GemmSplit sp = fwd_gemm_split(M, N, K);
+  if (sp.splits > 1) f = std::max<size_t>(f, (size_t)sp.splits * M * N);
+  return round_up(f * sizeof(float), 256);
+}
+
 // ---------------------------------------------------------------------------
 // Fused multi-projection block: S projections that share their input, stored
 // as one NF4 weight of S * nseg rows with their adapters side by side.
@@ -409,41 +478,53 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
                      const qlora_nf4_weight* w, const uint16_t* A, const uint16_t* B, int r,
                      float s, const float* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB,
                      void* workspace, size_t workspace_bytes, qlora_stream_t stream) {
-  int st = check_weight(w);
+  const int st = check_weight(w);
+  if (st) return st;
+  return bwd_impl(dY, X, M, view(w), A, B, r, s, T_saved, dX, dA, dB, workspace,
+                  workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t qlora_lora16_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
+  if (M < 1 || N < 1 || K < 1 || r < 0) return 0;
+  return dense_fwd_ws_bytes(M, N, K, r);
+}
+
+size_t qlora_lora16_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
+  if (M < 1 || N < 1 || K < 1 || r < 0) return 0;
+  return bwd_ws_bytes(M, N, K, r);
+}
+
+int qlora_lora16_fwd(const uint16_t* X, int64_t M, const uint16_t* W, int64_t N, int64_t K,
+                     const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
+                     float* T, void* workspace, size_t workspace_bytes,
+                     qlora_stream_t stream) {
+  int st = check_dense(W, N, K);
   if (st) return st;
   if ((st = check_rank(r))) return st;
-  if (!dY || !X) return QLORA_ERR_NULL;
-  if (r > 0 && (!A || !B || !dA || !dB)) return QLORA_ERR_NULL;
-  if (M < 1 || w->N % 8 != 0) return QLORA_ERR_SHAPE;
-  if (!aligned16(dY) || !aligned16(X) || (dX && !aligned16(dX)) ||
-      (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB) ||
-                 (T_saved && !aligned16(T_saved)))))
+  if (!X || !Y) return QLORA_ERR_NULL;
+  if (r > 0 && (!A || !B || !T)) return QLORA_ERR_NULL;
+  if (M < 1) return QLORA_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(Y) || (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(T))))
     return QLORA_ERR_ALIGN;
-  const size_t need = bwd_ws_bytes(M, w->N, w->K, r);
+  const size_t need = dense_fwd_ws_bytes(M, N, K, r);
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return QLORA_ERR_ALIGN;
-
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  const Nf4View v = view(w);
+  float* ws = static_cast<float*>(workspace);
   hipError_t e = hipSuccess;
-  float* G = nullptr;
-  char* base = static_cast<char*>(workspace);
-  const size_t mr = r > 0 ? round_up((size_t)M * r * sizeof(float), 256) : 0;
-  float* part = base ? reinterpret_cast<float*>(base + 2 * mr) : nullptr;
-  if (r > 0) {
-    G = reinterpret_cast<float*>(base);
-    float* Tr = reinterpret_cast<float*>(base + mr);
-    const float* T = T_saved;
-    if (!T) {
-      e = launch_lora_down(X, M, w->K, A, r, Tr, part, hs);
-      T = Tr;
-    }
-    if (e == hipSuccess) e = launch_grad_in_and_b(dY, M, w->N, B, T, r, s, G, dB, part, hs);
-    if (e == hipSuccess) e = launch_grad_a(X, M, w->K, G, r, s, dA, part, hs);
-    if (e != hipSuccess) return QLORA_ERR_HIP;
-  }
-  if (dX) e = launch_dx_gemm(dY, M, v, G, A, r, s, dX, part, tables(), hs);
+  if (r > 0) e = launch_lora_down(X, M, K, A, r, T, ws, hs);
+  if (e == hipSuccess) e = launch_fwd_gemm(X, M, dense_view(W, N, K), T, B, r, s, Y, ws, tables(), hs);
   return hip_status(e);
+}
+
+int qlora_lora16_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const uint16_t* W,
+                     int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int r, float s,
+                     const float* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                     void* workspace, size_t workspace_bytes, qlora_stream_t stream) {
+  const int st = check_dense(W, N, K);
+  if (st) return st;
+  return bwd_impl(dY, X, M, dense_view(W, N, K), A, B, r, s, T_saved, dX, dA, dB, workspace,
+                  workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 size_t qlora_block_fwd_workspace_bytes(int64_t M, int S, int64_t nseg, int64_t K, int r) {

@@ -22,6 +22,12 @@
 //
 // The LoRA update is appended as extra reduction steps over the rank: B^T is
 // staged in LDS through 8x8 transposes, s.T enters as bf16 hi and lo halves.
+//
+// kDense instantiates the same kernel over a bf16 weight [N, K] (16-bit LoRA,
+// the baseline of "Performance Reality" in "QLoRA: Quantized Low Rank
+// Adaptation at Extreme Scale"): each thread loads its 16 weights (32 bytes)
+// instead of 16 codes and stores them into the same operand pieces, so the
+// two forms differ only in the weight's bytes and the dequantization.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -56,8 +62,10 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
 
 }  // namespace
 
+template <bool kDense>
 __global__ __launch_bounds__(GT) void k_fwd_gemm(
-    const uint16_t* __restrict__ X, int64_t M, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ X, int64_t M, const uint16_t* __restrict__ Wd,
+    const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
     int64_t N, int64_t K, const float* __restrict__ T, const uint16_t* __restrict__ Bl,
     int r, float s, uint16_t* __restrict__ Y, int ptiles, int qtiles, int cps,
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   const int wave = wave_id(), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int wt = wave % GWT, ks = wave / GWT;
-  build_rep_pair_table<GT>(tab, load_levels(tb), tid);
+  if constexpr (!kDense) build_rep_pair_table<GT>(tab, load_levels(tb), tid);
 
   // With a split reduction (few tiles), workgroup b takes chunks
   // [z cps, (z + 1) cps) of its tile and writes fp32 partial sums.
@@ -92,6 +100,8 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   const BufRes rc = make_bufres(codes, static_cast<uint32_t>(N * K / 2));
   const BufRes re = make_bufres(absmax_q, nb);
   const BufRes rd = make_bufres(absmax_scale, ((nb + kGroup - 1) / kGroup) * 4u);
+  // the bf16 weight (kDense; N K 2 < 2^31 bytes)
+  const BufRes rw = make_bufres(Wd, static_cast<uint32_t>(kDense ? N * K * 2 : 0));
   // X is addressed from the tile's first token (its 256 rows span less
   // than 2^31 bytes for K <= 2^22).  (A plain conditional, not min(): the
   // 64-bit min is opaque to the compiler's uniformity analysis and would put
@@ -106,16 +116,25 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   const int64_t dn = p0 + 16 * wave + li;
   const uint32_t dcode = static_cast<uint32_t>(dn * (K / 2)) + 16u * sd + 8u * h;   // + 32 c
   const uint32_t dblk = static_cast<uint32_t>(dn * KB);                           // + c
+  // kDense: the same 16 weights as bf16, byte offset (+ 128 c)
+  const uint32_t dw = static_cast<uint32_t>(dn * K * 2) + 64u * sd + 32u * h;
   u32x2 cw[2];
   uint32_t ce[2];
   float cd[2];
+  u32x4 ww[2][2];
   auto load_codes = [&](int c, int st) {
     const bool live = c < nchunks;
-    const uint32_t blk = dblk + static_cast<uint32_t>(c);
-    cw[st] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                           rc, live ? dcode + 32u * c : 0x80000000u, 0, 0));
-    ce[st] = buf_load_u8(re, live ? blk : 0x80000000u);
-    cd[st] = buf_load_f32(rd, live ? (blk / kGroup) * 4u : 0x80000000u);
+    if constexpr (kDense) {
+      const uint32_t o = live ? dw + 128u * c : 0x80000000u;
+      ww[st][0] = buf_load16(rw, o);
+      ww[st][1] = buf_load16(rw, live ? o + 16u : 0x80000000u);
+    } else {
+      const uint32_t blk = dblk + static_cast<uint32_t>(c);
+      cw[st] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             rc, live ? dcode + 32u * c : 0x80000000u, 0, 0));
+      ce[st] = buf_load_u8(re, live ? blk : 0x80000000u);
+      cd[st] = buf_load_f32(rd, live ? (blk / kGroup) * 4u : 0x80000000u);
+    }
   };
   // bf16_rne(fl32(level * fl32(e * d))) of 16 codes -> two operand pieces
   uint32_t ta[4];
@@ -123,6 +142,12 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   for (int b = 0; b < 4; ++b) ta[b] = rep_lane_base(lane);
   uint16_t* const dpiece = As + (2 * wave + sd) * kAFrag + (32 * h + li) * 8;
   auto dequant = [&](int st, int buf) {
+    if constexpr (kDense) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<u32x4*>(dpiece + buf * kATile + 16 * 8 * i) = ww[st][i];
+      return;
+    }
     const float chat = static_cast<float>(ce[st]) * cd[st];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -338,17 +363,21 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
                             const float* T, const uint16_t* B, int r, float s,
                             uint16_t* Y, float* part, const Nf4Tables& tb, hipStream_t stream,
                             int ldt, int64_t seg_rows) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_fwd_gemm), hipFuncAttributeMaxDynamicSharedMemorySize,
-      kFwdLds);
-  if (attr != hipSuccess) return attr;
+  static const hipError_t attr[2] = {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_gemm<false>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kFwdLds),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_gemm<true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kFwdLds)};
+  const bool dense = w.dense != nullptr;
+  if (attr[dense] != hipSuccess) return attr[dense];
   const int ptiles = static_cast<int>((w.N + GP - 1) / GP);
   const int qtiles = static_cast<int>((M + GQ - 1) / GQ);
   const GemmSplit sp = fwd_gemm_split(M, w.N, w.K);
   if (sp.splits > 1 && !part) return hipErrorInvalidValue;
   prof_begin(0, stream);
-  hipLaunchKernelGGL(k_fwd_gemm, dim3(ptiles * qtiles * sp.splits), dim3(GT), kFwdLds, stream, X,
-                     M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, B, r, s, Y, ptiles,
+  hipLaunchKernelGGL(dense ? k_fwd_gemm<true> : k_fwd_gemm<false>,
+                     dim3(ptiles * qtiles * sp.splits), dim3(GT), kFwdLds, stream, X, M, w.dense,
+                     w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, B, r, s, Y, ptiles,
                      qtiles, sp.cps, sp.splits > 1 ? part : nullptr, tb, ldt > 0 ? ldt : r,
                      static_cast<int>(seg_rows > 0 ? seg_rows : w.N));
   hipError_t e = hipGetLastError();

@@ -23,6 +23,9 @@ struct Nf4View {
   const uint8_t* absmax_q;
   const float* absmax_scale;
   int64_t N, K;
+  // When set, the GEMM launchers read this bf16 weight [N, K] instead of the
+  // NF4 fields (the 16-bit LoRA baseline); N K 2 must stay below 2^31 bytes.
+  const uint16_t* dense = nullptr;
 };
 
 // Profiling hook: the launchers call these around the launches of one

@@ -271,13 +271,45 @@ int qlora_block_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
                     size_t workspace_bytes, qlora_stream_t stream);
 
 /*
+ * 16-bit LoRA on the same kernels: the layer with a bf16 base weight instead
+ * of an NF4 one, the baseline QLoRA is set against ("Performance Reality" of
+ * "QLoRA: Quantized Low Rank Adaptation at Extreme Scale": QLoRA compared
+ * with full 16-bit LoRA; the opening of "DL0087 QLoRA").  It runs the tiled
+ * GEMMs of qlora_linear_fwd / qlora_linear_bwd with the weight tile loaded
+ * instead of dequantized, and the same rank products and LoRA epilogue, so
+ * the two forms differ only in the weight's bytes and the dequantization:
+ *   Y  = X . W^T + s . T . B,  T = X . A
+ *   dX = dY . W + s . G . A^T, dA = s . X^T . G, dB = s . T^T . dY, G = dY . B^T
+ *   W  [N, K] bf16 (device, read-only), row-major, 16-byte aligned;
+ *      N % 8 == 0, K % 64 == 0, N, K <= 2^22 and N*K <= 2^30
+ *      (QLORA_ERR_SHAPE otherwise: the kernels address W with 32-bit byte
+ *      offsets below 2^31).
+ * Every other argument, output, limit and error is that of
+ * qlora_linear_fwd / qlora_linear_bwd.  The tiled GEMM runs at every M
+ * (there is no streaming path for M <= 16).  Workspace:
+ * qlora_lora16_fwd_workspace_bytes / qlora_lora16_bwd_workspace_bytes.
+ */
+size_t qlora_lora16_fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
+size_t qlora_lora16_bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
+int qlora_lora16_fwd(const uint16_t* X, int64_t M, const uint16_t* W, int64_t N, int64_t K,
+                     const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
+                     float* T, void* workspace, size_t workspace_bytes,
+                     qlora_stream_t stream);
+int qlora_lora16_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const uint16_t* W,
+                     int64_t N, int64_t K, const uint16_t* A, const uint16_t* B, int r,
+                     float s, const float* T_saved, uint16_t* dX, uint16_t* dA,
+                     uint16_t* dB, void* workspace, size_t workspace_bytes,
+                     qlora_stream_t stream);
+
+/*
  * Kernel timing for measurement.  When enabled (enable != 0), the library
  * records a pair of HIP events on the launch stream around every launch of
  * the kernel families below and accumulates their elapsed times; reading
  * synchronises on the recorded events.  Disabled by default; enabling adds
  * two event records per timed launch.
- *   family 0: dequantizing GEMM (forward, M > 16)
- *   family 1: dequantizing GEMM (backward dX)
+ *   family 0: tiled forward GEMM (dequantizing at M > 16; also the bf16
+ *             weight of qlora_lora16_fwd)
+ *   family 1: tiled dX GEMM (dequantizing; also qlora_lora16_bwd)
  *   family 2: decode GEMV (forward, M <= 16)
  *   family 3: quantize
  *   family 4: small rank-r GEMMs and reductions (T, G, dA, dB)
