@@ -9,7 +9,9 @@ table or constant generator with it.
 Sources are the pages on QLoRA: "DL0087 QLoRA: 4-bit Quantized LoRA"
 (numbered list items (1)-(4), Figure 1, Mathematical Formulation),
 "QLoRA: Finetuning 65B Models on a Single GPU with 4-Bit Quantization"
-(sections "4-bit NormalFloat" and "Double Quantization and Paged Optimizers"),
+(sections "4-bit NormalFloat" and "Double Quantization and Paged Optimizers";
+the INT4 / FP4 codebooks and fp32 constants it sets NF4 against live in
+oracle.codebooks),
 "QLoRA: Quantized Low Rank Adaptation at Extreme Scale" (The Quantization
 Layer) and "QLoRA (Quantized Low-Rank Adaptation)" (The Efficient Symphony
 of the QLoRA Workflow).
@@ -28,6 +30,7 @@ from .nf4 import (BLOCK, GROUP, normal_quantile, nf4_levels_f64, nf4_levels,
                   bf16_rne_bits, bf16_bits_to_f64, encode, quantize,
                   unpack_codes, dequantize, dequantize_at, code_boundaries,
                   storage_bytes, bits_per_param)
+from . import codebooks
 from .linear import (linear_fwd_f64, linear_bwd_f64, linear_fwd, linear_bwd, block_fwd_f64,
                      block_bwd_f64, block_fwd, block_bwd)
 
@@ -36,5 +39,5 @@ __all__ = [
     "bf16_rne_bits", "bf16_bits_to_f64", "encode", "quantize", "unpack_codes",
     "dequantize", "dequantize_at", "code_boundaries", "storage_bytes",
     "bits_per_param", "linear_fwd_f64", "linear_bwd_f64", "linear_fwd",
-    "linear_bwd", "block_fwd_f64", "block_bwd_f64", "block_fwd", "block_bwd",
+    "linear_bwd", "block_fwd_f64", "block_bwd_f64", "block_fwd", "block_bwd", "codebooks",
 ]
