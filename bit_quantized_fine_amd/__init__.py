@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 
 QLORA_OK = 0
 QLORA_ERR_SCRATCH = 7
+QLORA_ERR_FORMAT = 8
+CODEBOOKS = {"nf4": 0, "int4": 1, "fp4": 2}   # qlora_codebook of the header
 NOALLOC_SCRATCH_BYTES = 32 << 20   # QLORA_NOALLOC_SCRATCH_BYTES of the header
 _lib = None
 
@@ -25,6 +27,13 @@ class _Nf4Weight(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
                 ("absmax_scale", ctypes.c_void_p), ("N", ctypes.c_int64),
                 ("K", ctypes.c_int64)]
+
+
+class _Q4Weight(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("absmax_q", ctypes.c_void_p),
+                ("absmax_scale", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("codebook", ctypes.c_int32),
+                ("double_quant", ctypes.c_int32)]
 
 
 _SIGS = {
@@ -92,6 +101,25 @@ _SIGS = {
                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]),
+    "qlora_q4_levels": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p]),
+    "qlora_q4_thresholds": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p]),
+    "qlora_q4_scale_count": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
+    "qlora_q4_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "qlora_q4_dequantize": (ctypes.c_int, [ctypes.POINTER(_Q4Weight), ctypes.c_void_p,
+                                           ctypes.c_void_p]),
+    "qlora_q4_linear_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.POINTER(_Q4Weight), ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_size_t, ctypes.c_void_p]),
+    "qlora_q4_linear_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.POINTER(_Q4Weight), ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p]),
     "qlora_probe_hbm_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_void_p]),
     "qlora_probe_mfma_bf16": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
@@ -268,15 +296,11 @@ def _ws(nbytes: int, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def qlora_linear_fwd(X, w: NF4Weight, A=None, B=None, s: float = 1.0,
-                     Y=None, T=None, workspace=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
-    """Y = X . deq(W)^T + s . (X . A) . B.  Returns (Y bf16 [M,N], T fp32 [M,r])."""
+def _fwd(fn, X, w, wt, cw, A, B, s, Y, T, workspace):
+    """Marshal a forward call: fn is the C entry point's name, wt the weight's
+    tensors (checked), cw its C struct."""
     import torch
-    if X.dim() != 2:
-        raise ValueError("X must be [M, K]")
     M = X.shape[0]
-    _need(X, "X", (M, w.K), torch.bfloat16)
-    wt = _check_weight(w)
     r = _check_adapters(A, B, w)
     if Y is not None:
         _need(Y, "Y", (M, w.N), torch.bfloat16)
@@ -294,12 +318,24 @@ def qlora_linear_fwd(X, w: NF4Weight, A=None, B=None, s: float = 1.0,
     need = lib().qlora_linear_fwd_workspace_bytes(M, w.N, w.K, r)
     if workspace is None or workspace.numel() < need:
         workspace = _ws(need, X.device)
-    cw = w._c()
-    _check("qlora_linear_fwd",
-           lib().qlora_linear_fwd(_ptr(X), M, ctypes.byref(cw), _ptr(A), _ptr(B), r,
-                                  float(s), _ptr(Y), _ptr(T), _ptr(workspace), need,
-                                  _stream(X)))
+    _check(fn, getattr(lib(), fn)(_ptr(X), M, ctypes.byref(cw), _ptr(A), _ptr(B), r, float(s),
+                                  _ptr(Y), _ptr(T), _ptr(workspace), need, _stream(X)))
     return Y, T
+
+
+def _x_rows(X, K):
+    import torch
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    _need(X, "X", (X.shape[0], K), torch.bfloat16)
+    return X.shape[0]
+
+
+def qlora_linear_fwd(X, w: NF4Weight, A=None, B=None, s: float = 1.0,
+                     Y=None, T=None, workspace=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Y = X . deq(W)^T + s . (X . A) . B.  Returns (Y bf16 [M,N], T fp32 [M,r])."""
+    _x_rows(X, w.K)
+    return _fwd("qlora_linear_fwd", X, w, _check_weight(w), w._c(), A, B, s, Y, T, workspace)
 
 
 def qlora_linear_fwd_noalloc(X, w: NF4Weight, A=None, B=None, s: float = 1.0,
@@ -331,19 +367,11 @@ def qlora_linear_fwd_noalloc(X, w: NF4Weight, A=None, B=None, s: float = 1.0,
     return Y, T
 
 
-def qlora_linear_bwd(dY, X, w: NF4Weight, A=None, B=None, s: float = 1.0, T=None,
-                     need_dx: bool = True, dX=None, dA=None, dB=None, workspace=None):
-    """Returns (dX bf16 [M,K] or None, dA bf16 [K,r], dB bf16 [r,N]).
-
-    T is the forward's T = X . A; None recomputes it (gradient checkpointing).
-    """
+def _bwd(fn, dY, X, w, wt, cw, A, B, s, T, need_dx, dX, dA, dB, workspace):
+    """Marshal a backward call (as _fwd)."""
     import torch
-    if X.dim() != 2:
-        raise ValueError("X must be [M, K]")
     M = X.shape[0]
-    _need(X, "X", (M, w.K), torch.bfloat16)
     _need(dY, "dY", (M, w.N), torch.bfloat16)
-    wt = _check_weight(w)
     r = _check_adapters(A, B, w)
     if T is not None and r > 0:
         _need(T, "T", (M, r), torch.float32)
@@ -370,12 +398,129 @@ def qlora_linear_bwd(dY, X, w: NF4Weight, A=None, B=None, s: float = 1.0, T=None
     need = lib().qlora_linear_bwd_workspace_bytes(M, w.N, w.K, r)
     if workspace is None or workspace.numel() < need:
         workspace = _ws(need, dev)
-    cw = w._c()
-    _check("qlora_linear_bwd",
-           lib().qlora_linear_bwd(_ptr(dY), _ptr(X), M, ctypes.byref(cw), _ptr(A), _ptr(B),
-                                  r, float(s), _ptr(T), _ptr(dX if need_dx else None),
-                                  _ptr(dA), _ptr(dB), _ptr(workspace), need, _stream(X)))
+    _check(fn, getattr(lib(), fn)(_ptr(dY), _ptr(X), M, ctypes.byref(cw), _ptr(A), _ptr(B), r,
+                                  float(s), _ptr(T), _ptr(dX if need_dx else None), _ptr(dA),
+                                  _ptr(dB), _ptr(workspace), need, _stream(X)))
     return (dX if need_dx else None), dA, dB
+
+
+def qlora_linear_bwd(dY, X, w: NF4Weight, A=None, B=None, s: float = 1.0, T=None,
+                     need_dx: bool = True, dX=None, dA=None, dB=None, workspace=None):
+    """Returns (dX bf16 [M,K] or None, dA bf16 [K,r], dB bf16 [r,N]).
+
+    T is the forward's T = X . A; None recomputes it (gradient checkpointing).
+    """
+    _x_rows(X, w.K)
+    return _bwd("qlora_linear_bwd", dY, X, w, _check_weight(w), w._c(), A, B, s, T, need_dx,
+                dX, dA, dB, workspace)
+
+
+class Q4Weight(NamedTuple):
+    """A 4-bit weight of any codebook: with double quantization the NF4
+    format's constants, else absmax_q is None and absmax_scale holds one
+    fp32 absmax per 64-block."""
+    codes: "torch.Tensor"                    # uint8 [N*K/2]
+    absmax_q: Optional["torch.Tensor"]       # uint8 [N*K/64], or None
+    absmax_scale: "torch.Tensor"             # float32 [ceil(N*K/16384)] or [N*K/64]
+    N: int
+    K: int
+    codebook: str                            # "nf4", "int4" or "fp4"
+    double_quant: bool
+
+    def _c(self) -> _Q4Weight:
+        return _Q4Weight(self.codes.data_ptr(),
+                         self.absmax_q.data_ptr() if self.absmax_q is not None else None,
+                         self.absmax_scale.data_ptr(), self.N, self.K,
+                         CODEBOOKS[self.codebook], int(self.double_quant))
+
+    def nbytes(self) -> int:
+        return (self.codes.numel() + (self.absmax_q.numel() if self.absmax_q is not None else 0)
+                + 4 * self.absmax_scale.numel())
+
+
+def _codebook_id(codebook: str) -> int:
+    if codebook not in CODEBOOKS:
+        raise ValueError(f"codebook must be one of {sorted(CODEBOOKS)}, got {codebook!r}")
+    return CODEBOOKS[codebook]
+
+
+def _check_q4_weight(w: Q4Weight):
+    import torch
+    _codebook_id(w.codebook)
+    n_codes, n_blocks = w.N * w.K // 2, w.N * w.K // 64
+    _need(w.codes, "w.codes", (n_codes,), torch.uint8)
+    if w.double_quant:
+        _need(w.absmax_q, "w.absmax_q", (n_blocks,), torch.uint8)
+        _need(w.absmax_scale, "w.absmax_scale", ((n_blocks + 255) // 256,), torch.float32)
+    else:
+        _need(w.absmax_scale, "w.absmax_scale", (n_blocks,), torch.float32)
+    return [("w.codes", w.codes), ("w.absmax_q", w.absmax_q),
+            ("w.absmax_scale", w.absmax_scale)]
+
+
+def qlora_q4_levels(codebook: str = "nf4"):
+    """The 16 levels of a codebook (list of float)."""
+    buf = (ctypes.c_float * 16)()
+    _check("qlora_q4_levels", lib().qlora_q4_levels(_codebook_id(codebook), buf))
+    return list(buf)
+
+
+def qlora_q4_thresholds(codebook: str = "nf4"):
+    """The 15 quantizer thresholds of a codebook (code = #{j : x > t_j})."""
+    buf = (ctypes.c_float * 15)()
+    _check("qlora_q4_thresholds", lib().qlora_q4_thresholds(_codebook_id(codebook), buf))
+    return list(buf)
+
+
+def qlora_q4_quantize(W, codebook: str = "nf4", double_quant: bool = True) -> Q4Weight:
+    """Quantize a float32 [N, K] CUDA tensor with a codebook ("nf4", "int4",
+    "fp4"), with double-quantized or fp32 block constants."""
+    import torch
+    cb = _codebook_id(codebook)
+    if W.dim() != 2:
+        raise ValueError("W must be [N, K]")
+    N, K = W.shape
+    _need(W, "W", (N, K), torch.float32)
+    _on_gpu([("W", W)])
+    L = lib()
+    dq = bool(double_quant)
+    out = Q4Weight(
+        torch.empty(L.qlora_nf4_codes_bytes(N, K), dtype=torch.uint8, device=W.device),
+        torch.empty(L.qlora_nf4_absmax_q_bytes(N, K), dtype=torch.uint8, device=W.device)
+        if dq else None,
+        torch.empty(L.qlora_q4_scale_count(N, K, int(dq)), dtype=torch.float32, device=W.device),
+        N, K, codebook, dq)
+    _check("qlora_q4_quantize",
+           L.qlora_q4_quantize(_ptr(W), N, K, cb, int(dq), _ptr(out.codes), _ptr(out.absmax_q),
+                               _ptr(out.absmax_scale), _stream(W)))
+    return out
+
+
+def qlora_q4_dequantize(w: Q4Weight):
+    """bf16 [N, K] dequantized copy of a 4-bit weight."""
+    import torch
+    _on_gpu(_check_q4_weight(w))
+    out = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=w.codes.device)
+    cw = w._c()
+    _check("qlora_q4_dequantize",
+           lib().qlora_q4_dequantize(ctypes.byref(cw), _ptr(out), _stream(out)))
+    return out
+
+
+def qlora_q4_linear_fwd(X, w: Q4Weight, A=None, B=None, s: float = 1.0, Y=None, T=None,
+                        workspace=None):
+    """qlora_linear_fwd for a weight of any codebook and constant format."""
+    _x_rows(X, w.K)
+    return _fwd("qlora_q4_linear_fwd", X, w, _check_q4_weight(w), w._c(), A, B, s, Y, T,
+                workspace)
+
+
+def qlora_q4_linear_bwd(dY, X, w: Q4Weight, A=None, B=None, s: float = 1.0, T=None,
+                        need_dx: bool = True, dX=None, dA=None, dB=None, workspace=None):
+    """qlora_linear_bwd for a weight of any codebook and constant format."""
+    _x_rows(X, w.K)
+    return _bwd("qlora_q4_linear_bwd", dY, X, w, _check_q4_weight(w), w._c(), A, B, s, T,
+                need_dx, dX, dA, dB, workspace)
 
 
 class _Shape(NamedTuple):

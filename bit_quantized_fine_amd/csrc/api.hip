@@ -39,29 +39,62 @@ long double normal_quantile(long double p) {
   return z;
 }
 
+// Thresholds of a level table for the quantizer's rule code = #{j : x > t_j}:
+// the code of x is the nearest level, ties to the lower index, so t_j is the
+// largest fp32 not above the midpoint of level j and the next larger distinct
+// level (a level equal to the one before it is never chosen: FP4's -0).  The
+// fp64 sum of two fp32 levels is exact.
+void fill_thresholds(Nf4Tables& t) {
+  for (int j = 0; j < 15; ++j) {
+    int n = j + 1;
+    while (n < 15 && !(t.q[n] > t.q[j])) ++n;
+    const double mid = (static_cast<double>(t.q[j]) + static_cast<double>(t.q[n])) * 0.5;
+    float th = static_cast<float>(mid);
+    if (static_cast<double>(th) > mid) th = std::nextafter(th, -INFINITY);
+    t.t[j] = th;
+  }
+}
+
+// The 4-bit types "4-bit NormalFloat" of "QLoRA: Finetuning 65B Models on a
+// Single GPU" sets against each other: NF4 above; INT4 with sixteen levels
+// spaced uniformly over [-1, 1], (2k - 15) / 15; FP4 as the sixteen E2M1
+// values (sign, 2 exponent bits with bias 1, 1 mantissa bit) over their
+// largest magnitude 6, ascending with +0 before -0.
 struct Tables {
-  Nf4Tables t;
+  Nf4Tables t[3];
   Tables() {
     long double pos[8], neg[7];
     for (int j = 1; j <= 8; ++j) pos[j - 1] = normal_quantile(0.5L + (j - 0.5L) / 16.0L);
     for (int j = 1; j <= 7; ++j) neg[j - 1] = normal_quantile(0.5L + (j - 0.5L) / 14.0L);
     // ascending: -neg[6]/neg[6] ... -neg[0]/neg[6], 0, pos[0]/pos[7] ... 1
-    for (int i = 0; i < 7; ++i) t.q[i] = static_cast<float>(-neg[6 - i] / neg[6]);
-    t.q[7] = 0.0f;
-    for (int i = 0; i < 8; ++i) t.q[8 + i] = static_cast<float>(pos[i] / pos[7]);
-    // thresholds: largest fp32 <= exact midpoint (the fp64 sum of two fp32 is exact)
-    for (int j = 0; j < 15; ++j) {
-      const double mid = (static_cast<double>(t.q[j]) + static_cast<double>(t.q[j + 1])) * 0.5;
-      float th = static_cast<float>(mid);
-      if (static_cast<double>(th) > mid) th = std::nextafter(th, -INFINITY);
-      t.t[j] = th;
+    Nf4Tables& nf = t[QLORA_CODEBOOK_NF4];
+    for (int i = 0; i < 7; ++i) nf.q[i] = static_cast<float>(-neg[6 - i] / neg[6]);
+    nf.q[7] = 0.0f;
+    for (int i = 0; i < 8; ++i) nf.q[8 + i] = static_cast<float>(pos[i] / pos[7]);
+
+    Nf4Tables& in = t[QLORA_CODEBOOK_INT4];
+    for (int k = 0; k < 16; ++k) in.q[k] = static_cast<float>((2.0 * k - 15.0) / 15.0);
+
+    // E2M1 magnitudes of the bit patterns 0..7: 0, 0.5 (subnormal), then
+    // 2^(e-1) (1 + m/2) for exponent fields e = 1..3
+    double mag[8];
+    for (int b = 0; b < 8; ++b) {
+      const int e = b >> 1, m = b & 1;
+      mag[b] = e == 0 ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
     }
+    Nf4Tables& fp = t[QLORA_CODEBOOK_FP4];
+    for (int i = 0; i < 7; ++i) fp.q[i] = static_cast<float>(-mag[7 - i] / 6.0);
+    fp.q[7] = 0.0f;
+    fp.q[8] = -0.0f;
+    for (int i = 1; i < 8; ++i) fp.q[8 + i] = static_cast<float>(mag[i] / 6.0);
+
+    for (Nf4Tables& x : t) fill_thresholds(x);
   }
 };
 
-const Nf4Tables& tables() {
+const Nf4Tables& tables(int codebook = QLORA_CODEBOOK_NF4) {
   static const Tables tb;
-  return tb.t;
+  return tb.t[codebook];
 }
 
 // ---------------------------------------------------------------------------
@@ -120,17 +153,45 @@ size_t bwd_ws_bytes(int64_t M, int64_t N, int64_t K, int r) {
   return 2 * mr + round_up(f * sizeof(float), 256);
 }
 
-int check_fwd_args(const uint16_t* X, int64_t M, const qlora_nf4_weight* w, const uint16_t* A,
-                   const uint16_t* B, int r, const uint16_t* Y, const float* T) {
-  int st = check_weight(w);
+// Forward arguments other than the weight (N: the weight's rows).
+int check_fwd_rest(const uint16_t* X, int64_t M, int64_t N, const uint16_t* A, const uint16_t* B,
+                   int r, const uint16_t* Y, const float* T) {
+  int st = check_rank(r);
   if (st) return st;
-  if ((st = check_rank(r))) return st;
   if (!X || !Y) return QLORA_ERR_NULL;
   if (r > 0 && (!A || !B || !T)) return QLORA_ERR_NULL;
-  if (M < 1 || w->N % 8 != 0) return QLORA_ERR_SHAPE;
+  if (M < 1 || N % 8 != 0) return QLORA_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(Y) || (r > 0 && (!aligned16(A) || !aligned16(B) || !aligned16(T))))
     return QLORA_ERR_ALIGN;
   return QLORA_OK;
+}
+
+int check_fwd_args(const uint16_t* X, int64_t M, const qlora_nf4_weight* w, const uint16_t* A,
+                   const uint16_t* B, int r, const uint16_t* Y, const float* T) {
+  const int st = check_weight(w);
+  return st ? st : check_fwd_rest(X, M, w->N, A, B, r, Y, T);
+}
+
+// A 4-bit weight of any codebook and constant format.
+int check_q4_weight(const qlora_q4_weight* w) {
+  if (!w) return QLORA_ERR_NULL;
+  if (w->codebook < QLORA_CODEBOOK_NF4 || w->codebook > QLORA_CODEBOOK_FP4 ||
+      (w->double_quant != 0 && w->double_quant != 1))
+    return QLORA_ERR_FORMAT;
+  if (!w->codes || !w->absmax_scale || (w->double_quant && !w->absmax_q)) return QLORA_ERR_NULL;
+  if (w->N < 1 || w->K < kBlock || w->K % kBlock != 0) return QLORA_ERR_SHAPE;
+  if (w->K > kMaxK || w->N > kMaxN || w->N > kMaxElems / w->K) return QLORA_ERR_SHAPE;
+  // fp32 constants are read 16 bytes at a time by the streaming kernel
+  if (!aligned16(w->codes) || (reinterpret_cast<uintptr_t>(w->absmax_scale) &
+                               (w->double_quant ? 3u : 15u)))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+Nf4View q4_view(const qlora_q4_weight* w) {
+  Nf4View v{w->codes, w->absmax_q, w->absmax_scale, w->N, w->K};
+  v.dq = w->double_quant != 0;
+  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -165,33 +226,32 @@ int scratch_for_current_device(float** out) {
 
 // The forward once its arguments are checked; ws holds at least
 // fwd_ws_bytes(M, N, K, r) bytes.
-int fwd_impl(const uint16_t* X, int64_t M, const qlora_nf4_weight* w, const uint16_t* A,
-             const uint16_t* B, int r, float s, uint16_t* Y, float* T, float* ws,
-             hipStream_t hs) {
-  const Nf4View v = view(w);
+int fwd_impl(const uint16_t* X, int64_t M, const Nf4View& v, const Nf4Tables& tb,
+             const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y, float* T,
+             float* ws, hipStream_t hs) {
   hipError_t e = hipSuccess;
-  const bool decode = decode_fits(M, w->K);
+  const bool decode = decode_fits(M, v.K);
   if (decode && decode_folds_t(M, r)) {
     // T's partial sums are added up inside the decode kernel (no reduction
     // launch); its workgroup 0 writes T.
     int nz = 0;
-    e = launch_lora_down_partials(X, M, w->K, A, r, decode_max_t_partials(M, w->K, r), ws, &nz,
+    e = launch_lora_down_partials(X, M, v.K, A, r, decode_max_t_partials(M, v.K, r), ws, &nz,
                                   hs);
-    if (e == hipSuccess) e = launch_fwd_decode(X, M, v, ws, nz, T, B, r, s, Y, tables(), hs);
+    if (e == hipSuccess) e = launch_fwd_decode(X, M, v, ws, nz, T, B, r, s, Y, tb, hs);
     return hip_status(e);
   }
-  if (r > 0) e = launch_lora_down(X, M, w->K, A, r, T, ws, hs);
+  if (r > 0) e = launch_lora_down(X, M, v.K, A, r, T, ws, hs);
   if (e != hipSuccess) return QLORA_ERR_HIP;
   if (decode)
-    e = launch_fwd_decode(X, M, v, T, 0, nullptr, B, r, s, Y, tables(), hs);
+    e = launch_fwd_decode(X, M, v, T, 0, nullptr, B, r, s, Y, tb, hs);
   else
-    e = launch_fwd_gemm(X, M, v, T, B, r, s, Y, ws, tables(), hs);
+    e = launch_fwd_gemm(X, M, v, T, B, r, s, Y, ws, tb, hs);
   return hip_status(e);
 }
 
 // The backward once the weight is checked (either form); ws as bwd_ws_bytes.
 int bwd_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const Nf4View& v,
-             const uint16_t* A, const uint16_t* B, int r, float s, const float* T_saved,
+             const Nf4Tables& tb, const uint16_t* A, const uint16_t* B, int r, float s, const float* T_saved,
              uint16_t* dX, uint16_t* dA, uint16_t* dB, void* workspace, size_t workspace_bytes,
              hipStream_t hs) {
   int st = check_rank(r);
@@ -224,7 +284,7 @@ int bwd_impl(const uint16_t* dY, const uint16_t* X, int64_t M, const Nf4View& v,
     if (e == hipSuccess) e = launch_grad_a(X, M, v.K, G, r, s, dA, part, hs);
     if (e != hipSuccess) return QLORA_ERR_HIP;
   }
-  if (dX) e = launch_dx_gemm(dY, M, v, G, A, r, s, dX, part, tables(), hs);
+  if (dX) e = launch_dx_gemm(dY, M, v, G, A, r, s, dX, part, tb, hs);
   return hip_status(e);
 }
 
@@ -383,6 +443,8 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_SCRATCH:
       return "the call needs more workspace than the fixed scratch of qlora_linear_fwd_noalloc "
              "(QLORA_NOALLOC_SCRATCH_BYTES)";
+    case QLORA_ERR_FORMAT:
+      return "unknown codebook or constant format (codebook 0..2, double_quant 0 or 1)";
     default: return "unknown status";
   }
 }
@@ -459,7 +521,7 @@ int qlora_linear_fwd(const uint16_t* X, int64_t M, const qlora_nf4_weight* w,
   const size_t need = fwd_ws_bytes(M, w->N, w->K, r);
   if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return QLORA_ERR_ALIGN;
-  return fwd_impl(X, M, w, A, B, r, s, Y, T, static_cast<float*>(workspace),
+  return fwd_impl(X, M, view(w), tables(), A, B, r, s, Y, T, static_cast<float*>(workspace),
                   static_cast<hipStream_t>(stream));
 }
 
@@ -471,7 +533,8 @@ int qlora_linear_fwd_noalloc(const uint16_t* X, int64_t M, const qlora_nf4_weigh
   if (fwd_ws_bytes(M, w->N, w->K, r) > kScratchBytes) return QLORA_ERR_SCRATCH;
   float* ws = nullptr;
   if ((st = scratch_for_current_device(&ws))) return st;
-  return fwd_impl(X, M, w, A, B, r, s, Y, T, ws, static_cast<hipStream_t>(stream));
+  return fwd_impl(X, M, view(w), tables(), A, B, r, s, Y, T, ws,
+                  static_cast<hipStream_t>(stream));
 }
 
 int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
@@ -480,7 +543,7 @@ int qlora_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
                      void* workspace, size_t workspace_bytes, qlora_stream_t stream) {
   const int st = check_weight(w);
   if (st) return st;
-  return bwd_impl(dY, X, M, view(w), A, B, r, s, T_saved, dX, dA, dB, workspace,
+  return bwd_impl(dY, X, M, view(w), tables(), A, B, r, s, T_saved, dX, dA, dB, workspace,
                   workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -523,8 +586,83 @@ int qlora_lora16_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const uin
                      void* workspace, size_t workspace_bytes, qlora_stream_t stream) {
   const int st = check_dense(W, N, K);
   if (st) return st;
-  return bwd_impl(dY, X, M, dense_view(W, N, K), A, B, r, s, T_saved, dX, dA, dB, workspace,
+  return bwd_impl(dY, X, M, dense_view(W, N, K), tables(), A, B, r, s, T_saved, dX, dA, dB,
+                  workspace,
                   workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int qlora_q4_levels(int codebook, float* out16) {
+  if (!out16) return QLORA_ERR_NULL;
+  if (codebook < QLORA_CODEBOOK_NF4 || codebook > QLORA_CODEBOOK_FP4) return QLORA_ERR_FORMAT;
+  std::memcpy(out16, tables(codebook).q, sizeof(float) * 16);
+  return QLORA_OK;
+}
+
+int qlora_q4_thresholds(int codebook, float* out15) {
+  if (!out15) return QLORA_ERR_NULL;
+  if (codebook < QLORA_CODEBOOK_NF4 || codebook > QLORA_CODEBOOK_FP4) return QLORA_ERR_FORMAT;
+  std::memcpy(out15, tables(codebook).t, sizeof(float) * 15);
+  return QLORA_OK;
+}
+
+size_t qlora_q4_scale_count(int64_t N, int64_t K, int double_quant) {
+  if (N < 0 || K < 0 || K % kBlock) return 0;
+  const size_t nb = static_cast<size_t>(N) * static_cast<size_t>(K) / kBlock;
+  return double_quant ? (nb + kGroup - 1) / kGroup : nb;
+}
+
+int qlora_q4_quantize(const float* W, int64_t N, int64_t K, int codebook, int double_quant,
+                      uint8_t* codes, uint8_t* absmax_q, float* absmax_scale,
+                      qlora_stream_t stream) {
+  if (codebook < QLORA_CODEBOOK_NF4 || codebook > QLORA_CODEBOOK_FP4 ||
+      (double_quant != 0 && double_quant != 1))
+    return QLORA_ERR_FORMAT;
+  if (!W || !codes || !absmax_scale || (double_quant && !absmax_q)) return QLORA_ERR_NULL;
+  if (N < 1 || K < kBlock || K % kBlock != 0) return QLORA_ERR_SHAPE;
+  if (K > kMaxK || N > kMaxN || N > kMaxElems / K) return QLORA_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(codes) ||
+      (reinterpret_cast<uintptr_t>(absmax_scale) & (double_quant ? 3u : 15u)))
+    return QLORA_ERR_ALIGN;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  prof_begin(3, st);
+  const hipError_t e = launch_quantize(W, N, K, codes, absmax_q, absmax_scale, tables(codebook),
+                                       st, double_quant != 0);
+  prof_end(3, st);
+  return hip_status(e);
+}
+
+int qlora_q4_dequantize(const qlora_q4_weight* w, uint16_t* W_bf16, qlora_stream_t stream) {
+  const int st = check_q4_weight(w);
+  if (st) return st;
+  if (!W_bf16) return QLORA_ERR_NULL;
+  if (!aligned16(W_bf16)) return QLORA_ERR_ALIGN;
+  return hip_status(launch_dequantize(w->codes, w->absmax_q, w->absmax_scale, w->N, w->K,
+                                      W_bf16, tables(w->codebook),
+                                      static_cast<hipStream_t>(stream), w->double_quant != 0));
+}
+
+int qlora_q4_linear_fwd(const uint16_t* X, int64_t M, const qlora_q4_weight* w,
+                        const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
+                        float* T, void* workspace, size_t workspace_bytes,
+                        qlora_stream_t stream) {
+  int st = check_q4_weight(w);
+  if (st) return st;
+  if ((st = check_fwd_rest(X, M, w->N, A, B, r, Y, T))) return st;
+  const size_t need = fwd_ws_bytes(M, w->N, w->K, r);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QLORA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return QLORA_ERR_ALIGN;
+  return fwd_impl(X, M, q4_view(w), tables(w->codebook), A, B, r, s, Y, T,
+                  static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int qlora_q4_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
+                        const qlora_q4_weight* w, const uint16_t* A, const uint16_t* B, int r,
+                        float s, const float* T_saved, uint16_t* dX, uint16_t* dA, uint16_t* dB,
+                        void* workspace, size_t workspace_bytes, qlora_stream_t stream) {
+  const int st = check_q4_weight(w);
+  if (st) return st;
+  return bwd_impl(dY, X, M, q4_view(w), tables(w->codebook), A, B, r, s, T_saved, dX, dA, dB,
+                  workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 size_t qlora_block_fwd_workspace_bytes(int64_t M, int S, int64_t nseg, int64_t K, int r) {

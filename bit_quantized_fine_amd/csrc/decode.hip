@@ -28,6 +28,13 @@
 // extra column is zero), the workgroup's columns of B, and X itself when it
 // fits.  The waves' partial sums meet in LDS; the LoRA update is added as
 // extra MFMA steps over the rank before that reduction.
+//
+// The level table is an argument (NF4, or the INT4 / FP4 tables of "4-bit
+// NormalFloat" in "QLoRA: Finetuning 65B Models on a Single GPU"), and the
+// NODQ instantiation stages fp32 block constants c_b (no double
+// quantization) in place of e_b . d_g.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -85,7 +92,7 @@ struct DecLds {
 
 }  // namespace
 
-template <int D, int XP, int FR>
+template <int D, int XP, int FR, bool NODQ>
 __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
@@ -124,7 +131,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   const uint32_t nb = static_cast<uint32_t>(N * K / kBlock);
   const BufRes rc = make_bufres(codes, static_cast<uint32_t>(N * K / 2));
   const BufRes re = make_bufres(absmax_q, nb);
-  const BufRes rd = make_bufres(absmax_scale, ((nb + kGroup - 1) / kGroup) * 4u);
+  // second-level scales, or (NODQ) one fp32 constant per block
+  const BufRes rd =
+      make_bufres(absmax_scale, (NODQ ? nb : (nb + kGroup - 1) / kGroup) * 4u);
   const BufRes rx = make_bufres(X, static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u);
 
   // Staging loads first, a fixed number per thread, so that waiting for them
@@ -138,13 +147,21 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   const int erange = ROWS * KB;                         // bytes, a multiple of 8
   u32x2 ev[kDecEPieces];
   float dv[kDecEPieces];
+  u32x4 cv[NODQ ? kDecEPieces : 1][2];   // NODQ: the 8 blocks' fp32 constants
 #pragma unroll
   for (int i = 0; i < kDecEPieces; ++i) {
     const int idx = tid + i * kDecThreads;
     const bool ok = 8 * idx < erange;
-    ev[i] = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_raw_buffer_load_b64(re, ok ? e0 + 8u * idx : kDecOffNone, 0, 0));
-    dv[i] = buf_load_f32(rd, ok ? ((e0 + 8u * idx) / kGroup) * 4u : kDecOffNone);
+    if constexpr (NODQ) {
+      const uint32_t o = (e0 + 8u * idx) * 4u;
+      cv[i][0] = buf_load16(rd, ok ? o : kDecOffNone);
+      cv[i][1] = buf_load16(rd, ok ? o + 16u : kDecOffNone);
+    } else {
+      ev[i] = __builtin_bit_cast(
+          u32x2,
+          __builtin_amdgcn_raw_buffer_load_b64(re, ok ? e0 + 8u * idx : kDecOffNone, 0, 0));
+      dv[i] = buf_load_f32(rd, ok ? ((e0 + 8u * idx) / kGroup) * 4u : kDecOffNone);
+    }
   }
   // X: XP pieces per thread, as many as M K 2 bytes need (a load whose lanes
   // all fall outside the range still occupies the address unit, and at kernel
@@ -246,9 +263,17 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
       for (int b = 0; b < 8; ++b) {
         const int f = 8 * idx + b;   // row-major index: row f / KB, column f % KB
         const int row = static_cast<int>((static_cast<float>(f) + 0.5f) * inv_kb);
-        const uint32_t w = b < 4 ? ev[i].x : ev[i].y;
-        const float e = static_cast<float>((w >> (8 * (b % 4))) & 0xFFu);
-        csc[(f - row * KB) * ROWS + row] = e * dv[i];
+        float c;
+        if constexpr (NODQ) {
+          // (the element is converted to a plain value first: this compiler
+          // reads element 0 when __builtin_bit_cast is given a vector
+          // element directly)
+          c = __builtin_bit_cast(float, static_cast<uint32_t>(cv[NODQ ? i : 0][b / 4][b % 4]));
+        } else {
+          const uint32_t w = b < 4 ? ev[i].x : ev[i].y;
+          c = static_cast<float>((w >> (8 * (b % 4))) & 0xFFu) * dv[i];
+        }
+        csc[(f - row * KB) * ROWS + row] = c;
       }
     }
   }
@@ -402,21 +427,21 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 
 namespace {
 
-template <int D, int XP, int FR>
+template <int D, int XP, int FR, bool NODQ>
 hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w, const float* T,
                                  int nz, float* Tout, const uint16_t* B, int r, float s,
                                  uint16_t* Y, const Nf4Tables& tb, hipStream_t stream, int ldt,
                                  int ldb, int ldy) {
   // allow the largest dynamic LDS (once per variant)
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_fwd_decode<D, XP, FR>),
+      reinterpret_cast<const void*>(&k_fwd_decode<D, XP, FR, NODQ>),
       hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
   if (attr != hipSuccess) return attr;
   const DecLds L(M, w.K, r, XP > 0, FR);
   if (L.total > kDecLdsMax || nz > 16 * dec_tq(FR)) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>((w.N + kDecRows - 1) / kDecRows);
   const float inv_kb = 1.0f / static_cast<float>(w.K / kBlock);
-  hipLaunchKernelGGL((k_fwd_decode<D, XP, FR>), dim3(grid), dim3(kDecThreads), L.total, stream,
+  hipLaunchKernelGGL((k_fwd_decode<D, XP, FR, NODQ>), dim3(grid), dim3(kDecThreads), L.total, stream,
                      X, (int)M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, nz, Tout, B,
                      r, s, Y, tb, L.boff, L.toff, L.coff, L.xoff, inv_kb, ldt, ldb, ldy);
   return hipGetLastError();
@@ -450,28 +475,31 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
   prof_begin(2, stream);
   // Two chunks in flight per wave: with all 16 waves of every CU streaming,
   // deeper rings (measured up to 8) only delay the first products.
-  hipError_t e;
   // X goes to LDS when it fits next to the rest (M = 1 up to K = 22016 with
   // r <= 64; M = 4 up to K = 8192), in as few 16-byte pieces per thread as it
   // needs; otherwise each wave reads its X pieces from global memory.
-  if (decode_x_in_lds(M, w.K, r)) {
-    const int64_t xbytes = M * w.K * 2;
-    const int64_t per_piece = 16 * kDecThreads;
-    if (xbytes <= per_piece)
-      e = launch_decode_variant<2, 1, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream, ldt,
-                                                   static_cast<int>(ldb), static_cast<int>(ldy));
-    else if (xbytes <= 2 * per_piece)
-      e = launch_decode_variant<2, 2, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream, ldt,
-                                                   static_cast<int>(ldb), static_cast<int>(ldy));
-    else
-      e = launch_decode_variant<2, kDecXPieces, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream, ldt,
-                                                   static_cast<int>(ldb), static_cast<int>(ldy));
-  } else {
+  auto run = [&](auto nodq) {
+    constexpr bool ND = decltype(nodq)::value;
+    const int lb = static_cast<int>(ldb), ly = static_cast<int>(ldy);
+    if (decode_x_in_lds(M, w.K, r)) {
+      const int64_t xbytes = M * w.K * 2;
+      const int64_t per_piece = 16 * kDecThreads;
+      if (xbytes <= per_piece)
+        return launch_decode_variant<2, 1, 1, ND>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream,
+                                                  ldt, lb, ly);
+      if (xbytes <= 2 * per_piece)
+        return launch_decode_variant<2, 2, 1, ND>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream,
+                                                  ldt, lb, ly);
+      return launch_decode_variant<2, kDecXPieces, 1, ND>(X, M, w, T, nz, Tout, B, r, s, Y, tb,
+                                                          stream, ldt, lb, ly);
+    }
     // X from global memory: each wave works on both fragments, so each X
     // piece it loads serves 32 rows.
-    e = launch_decode_variant<2, 0, 2>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream, ldt,
-                                                   static_cast<int>(ldb), static_cast<int>(ldy));
-  }
+    return launch_decode_variant<2, 0, 2, ND>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream, ldt,
+                                              lb, ly);
+  };
+  const hipError_t e =
+      w.dq ? run(std::false_type{}) : run(std::true_type{});
   prof_end(2, stream);
   return e;
 }

@@ -226,12 +226,18 @@ __device__ __forceinline__ float buf_load_f32(BufRes r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-// Block constant c_hat = fl32(e * d).
+// Block constant: c_hat = fl32(e * d) with double quantization (8-bit e per
+// block, one fp32 d per 256 blocks), else the block's stored fp32 absmax.
 __device__ __forceinline__ float block_scale(const uint8_t* absmax_q,
                                              const float* absmax_scale,
-                                             int64_t block) {
-  return static_cast<float>(absmax_q[block]) * absmax_scale[block >> 8];
+                                             int64_t block, bool dq) {
+  return dq ? static_cast<float>(absmax_q[block]) * absmax_scale[block >> 8]
+            : absmax_scale[block];
 }
+
+// Weight forms the tiled GEMMs read: 4-bit codes with double-quantized block
+// constants, 4-bit codes with fp32 block constants, or a bf16 weight.
+enum WeightForm : int { kFormDq = 0, kFormNoDq = 1, kFormDense = 2 };
 
 // D += A . B for one 16x16x32 bf16 MFMA.  Lane l supplies row (l % 16) of A
 // and column (l % 16) of B, each with the 8 reduction elements 8*(l/16)..+7;

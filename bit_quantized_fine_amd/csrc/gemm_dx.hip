@@ -25,9 +25,10 @@
 // rank: A^T fragments come straight from A [K, r], s.G enters as bf16 hi and
 // lo halves.
 //
-// kDense instantiates the same kernel over a bf16 weight [N, K] (the 16-bit
+// kFormDense instantiates the same kernel over a bf16 weight [N, K] (the 16-bit
 // LoRA baseline): each thread loads its 16 weights of row t/8 (32 bytes) and
-// stores them where the dequantized values would go.
+// stores them where the dequantized values would go.  kFormNoDq reads one
+// fp32 constant per block (codes without double quantization).
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -69,7 +70,7 @@ typedef __attribute__((address_space(3))) v4i16 LdsV4i16;
 
 }  // namespace
 
-template <bool kDense>
+template <int kForm>
 __global__ __launch_bounds__(XT) void k_dx_gemm(
     const uint16_t* __restrict__ dY, int64_t M, const uint16_t* __restrict__ Wd,
     const uint8_t* __restrict__ codes,
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
   const int wave = wave_id(), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int wt = wave % XWT, ks = wave / XWT;
-  if constexpr (!kDense) build_rep_pair_table<XT>(tab, load_levels(tb), tid);
+  if constexpr (kForm != kFormDense) build_rep_pair_table<XT>(tab, load_levels(tb), tid);
 
   // With a split reduction (few tiles), workgroup b takes row chunks
   // [z cps, (z + 1) cps) of its tile and writes fp32 partial sums.
@@ -107,9 +108,11 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
   const uint32_t nb = static_cast<uint32_t>(N * K / kBlock);
   const BufRes rc = make_bufres(codes, static_cast<uint32_t>(N * K / 2));
   const BufRes re = make_bufres(absmax_q, nb);
-  const BufRes rd = make_bufres(absmax_scale, ((nb + kGroup - 1) / kGroup) * 4u);
-  // the bf16 weight (kDense; N K 2 < 2^31 bytes)
-  const BufRes rw = make_bufres(Wd, static_cast<uint32_t>(kDense ? N * K * 2 : 0));
+  // second-level scales, or one fp32 constant per block (kFormNoDq)
+  const BufRes rd = make_bufres(
+      absmax_scale, (kForm == kFormNoDq ? nb : (nb + kGroup - 1) / kGroup) * 4u);
+  // the bf16 weight (kFormDense; N K 2 < 2^31 bytes)
+  const BufRes rw = make_bufres(Wd, static_cast<uint32_t>(kForm == kFormDense ? N * K * 2 : 0));
   // dY is addressed from the tile's first token (its 256 rows span less
   // than 2^31 bytes for N <= 2^22).  (A plain conditional, not min(): the
   // 64-bit min is opaque to the compiler's uniformity analysis and would put
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
   const bool dkok = k0 + 16 * dp < K;
   const uint32_t dcode = static_cast<uint32_t>(dr * (K / 2) + k0 / 2 + 8 * dp);   // + c 64 K/2
   const uint32_t dblk = static_cast<uint32_t>(dr * KB + (k0 + 16 * dp) / kBlock);   // + c 64 KB
-  // kDense: the same 16 weights as bf16, byte offset (+ c 64 K 2)
+  // kFormDense: the same 16 weights as bf16, byte offset (+ c 64 K 2)
   const uint32_t dw = static_cast<uint32_t>((dr * K + k0 + 16 * dp) * 2);
   u32x2 cw[2];
   uint32_t ce[2];
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
   u32x4 ww[2][2];
   auto load_codes = [&](int c, int st) {
     const bool live = c < nchunks && dkok;
-    if constexpr (kDense) {
+    if constexpr (kForm == kFormDense) {
       const uint32_t o = dw + static_cast<uint32_t>(c * XN) * static_cast<uint32_t>(K * 2);
       ww[st][0] = buf_load16(rw, live ? o : 0x80000000u);
       ww[st][1] = buf_load16(rw, live ? o + 16u : 0x80000000u);
@@ -141,8 +144,13 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
           u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                      rc, live ? dcode + static_cast<uint32_t>(c * XN) * static_cast<uint32_t>(K / 2)
                               : 0x80000000u, 0, 0));
-      ce[st] = buf_load_u8(re, live ? blk : 0x80000000u);
-      cd[st] = buf_load_f32(rd, live ? (blk / kGroup) * 4u : 0x80000000u);
+      if constexpr (kForm == kFormNoDq) {   // e = 1, d = the block's absmax
+        ce[st] = 1u;
+        cd[st] = buf_load_f32(rd, live ? blk * 4u : 0x80000000u);
+      } else {
+        ce[st] = buf_load_u8(re, live ? blk : 0x80000000u);
+        cd[st] = buf_load_f32(rd, live ? (blk / kGroup) * 4u : 0x80000000u);
+      }
     }
   };
   uint32_t ta[4];
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(XT) void k_dx_gemm(
   for (int b = 0; b < 4; ++b) ta[b] = rep_lane_base(lane);
   auto dequant = [&](int st, int buf) {
     uint16_t* dst = Ws + buf * kXA + dr * XAS;
-    if constexpr (kDense) {
+    if constexpr (kForm == kFormDense) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         *reinterpret_cast<u32x4*>(dst + 8 * wslot(dr, 2 * dp + i)) = ww[st][i];
@@ -361,19 +369,23 @@ GemmSplit dx_gemm_split(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_dx_gemm(const uint16_t* dY, int64_t M, const Nf4View& w,
                           const float* G, const uint16_t* A, int r, float s,
                           uint16_t* dX, float* part, const Nf4Tables& tb, hipStream_t stream) {
-  static const hipError_t attr[2] = {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dx_gemm<false>),
+  static const hipError_t attr[3] = {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dx_gemm<kFormDq>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kDxLds),
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dx_gemm<true>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dx_gemm<kFormNoDq>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kDxLds),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dx_gemm<kFormDense>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kDxLds)};
-  const bool dense = w.dense != nullptr;
-  if (attr[dense] != hipSuccess) return attr[dense];
+  const int form = w.dense ? kFormDense : (w.dq ? kFormDq : kFormNoDq);
+  if (attr[form] != hipSuccess) return attr[form];
+  decltype(&k_dx_gemm<kFormDq>) kern =
+      form == kFormDense ? k_dx_gemm<kFormDense> : (form == kFormNoDq ? k_dx_gemm<kFormNoDq> : k_dx_gemm<kFormDq>);
   const int ptiles = static_cast<int>((w.K + XP - 1) / XP);
   const int qtiles = static_cast<int>((M + XQ - 1) / XQ);
   const GemmSplit sp = dx_gemm_split(M, w.N, w.K);
   if (sp.splits > 1 && !part) return hipErrorInvalidValue;
   prof_begin(1, stream);
-  hipLaunchKernelGGL(dense ? k_dx_gemm<true> : k_dx_gemm<false>,
+  hipLaunchKernelGGL(kern,
                      dim3(ptiles * qtiles * sp.splits), dim3(XT), kDxLds, stream, dY, M, w.dense,
                      w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, G, A, r, s, dX, ptiles,
                      qtiles, sp.cps, sp.splits > 1 ? part : nullptr, tb);

@@ -23,11 +23,14 @@
 // The LoRA update is appended as extra reduction steps over the rank: B^T is
 // staged in LDS through 8x8 transposes, s.T enters as bf16 hi and lo halves.
 //
-// kDense instantiates the same kernel over a bf16 weight [N, K] (16-bit LoRA,
+// kFormDense instantiates the same kernel over a bf16 weight [N, K] (16-bit LoRA,
 // the baseline of "Performance Reality" in "QLoRA: Quantized Low Rank
 // Adaptation at Extreme Scale"): each thread loads its 16 weights (32 bytes)
 // instead of 16 codes and stores them into the same operand pieces, so the
 // two forms differ only in the weight's bytes and the dequantization.
+// kFormNoDq reads one fp32 constant per block in place of the 8-bit constant
+// and its group's scale (4-bit codes without double quantization); the level
+// table is an argument (NF4, INT4 or FP4).
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -62,7 +65,7 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
 
 }  // namespace
 
-template <bool kDense>
+template <int kForm>
 __global__ __launch_bounds__(GT) void k_fwd_gemm(
     const uint16_t* __restrict__ X, int64_t M, const uint16_t* __restrict__ Wd,
     const uint8_t* __restrict__ codes,
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   const int wave = wave_id(), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int wt = wave % GWT, ks = wave / GWT;
-  if constexpr (!kDense) build_rep_pair_table<GT>(tab, load_levels(tb), tid);
+  if constexpr (kForm != kFormDense) build_rep_pair_table<GT>(tab, load_levels(tb), tid);
 
   // With a split reduction (few tiles), workgroup b takes chunks
   // [z cps, (z + 1) cps) of its tile and writes fp32 partial sums.
@@ -99,9 +102,11 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   const uint32_t nb = static_cast<uint32_t>(N * K / kBlock);
   const BufRes rc = make_bufres(codes, static_cast<uint32_t>(N * K / 2));
   const BufRes re = make_bufres(absmax_q, nb);
-  const BufRes rd = make_bufres(absmax_scale, ((nb + kGroup - 1) / kGroup) * 4u);
-  // the bf16 weight (kDense; N K 2 < 2^31 bytes)
-  const BufRes rw = make_bufres(Wd, static_cast<uint32_t>(kDense ? N * K * 2 : 0));
+  // second-level scales, or one fp32 constant per block (kFormNoDq)
+  const BufRes rd = make_bufres(
+      absmax_scale, (kForm == kFormNoDq ? nb : (nb + kGroup - 1) / kGroup) * 4u);
+  // the bf16 weight (kFormDense; N K 2 < 2^31 bytes)
+  const BufRes rw = make_bufres(Wd, static_cast<uint32_t>(kForm == kFormDense ? N * K * 2 : 0));
   // X is addressed from the tile's first token (its 256 rows span less
   // than 2^31 bytes for K <= 2^22).  (A plain conditional, not min(): the
   // 64-bit min is opaque to the compiler's uniformity analysis and would put
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   const int64_t dn = p0 + 16 * wave + li;
   const uint32_t dcode = static_cast<uint32_t>(dn * (K / 2)) + 16u * sd + 8u * h;   // + 32 c
   const uint32_t dblk = static_cast<uint32_t>(dn * KB);                           // + c
-  // kDense: the same 16 weights as bf16, byte offset (+ 128 c)
+  // kFormDense: the same 16 weights as bf16, byte offset (+ 128 c)
   const uint32_t dw = static_cast<uint32_t>(dn * K * 2) + 64u * sd + 32u * h;
   u32x2 cw[2];
   uint32_t ce[2];
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   u32x4 ww[2][2];
   auto load_codes = [&](int c, int st) {
     const bool live = c < nchunks;
-    if constexpr (kDense) {
+    if constexpr (kForm == kFormDense) {
       const uint32_t o = live ? dw + 128u * c : 0x80000000u;
       ww[st][0] = buf_load16(rw, o);
       ww[st][1] = buf_load16(rw, live ? o + 16u : 0x80000000u);
@@ -132,8 +137,13 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
       const uint32_t blk = dblk + static_cast<uint32_t>(c);
       cw[st] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                                              rc, live ? dcode + 32u * c : 0x80000000u, 0, 0));
-      ce[st] = buf_load_u8(re, live ? blk : 0x80000000u);
-      cd[st] = buf_load_f32(rd, live ? (blk / kGroup) * 4u : 0x80000000u);
+      if constexpr (kForm == kFormNoDq) {   // e = 1, d = the block's absmax
+        ce[st] = 1u;
+        cd[st] = buf_load_f32(rd, live ? blk * 4u : 0x80000000u);
+      } else {
+        ce[st] = buf_load_u8(re, live ? blk : 0x80000000u);
+        cd[st] = buf_load_f32(rd, live ? (blk / kGroup) * 4u : 0x80000000u);
+      }
     }
   };
   // bf16_rne(fl32(level * fl32(e * d))) of 16 codes -> two operand pieces
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
   for (int b = 0; b < 4; ++b) ta[b] = rep_lane_base(lane);
   uint16_t* const dpiece = As + (2 * wave + sd) * kAFrag + (32 * h + li) * 8;
   auto dequant = [&](int st, int buf) {
-    if constexpr (kDense) {
+    if constexpr (kForm == kFormDense) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         *reinterpret_cast<u32x4*>(dpiece + buf * kATile + 16 * 8 * i) = ww[st][i];
@@ -363,19 +373,23 @@ hipError_t launch_fwd_gemm(const uint16_t* X, int64_t M, const Nf4View& w,
                             const float* T, const uint16_t* B, int r, float s,
                             uint16_t* Y, float* part, const Nf4Tables& tb, hipStream_t stream,
                             int ldt, int64_t seg_rows) {
-  static const hipError_t attr[2] = {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_gemm<false>),
+  static const hipError_t attr[3] = {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_gemm<kFormDq>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kFwdLds),
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_gemm<true>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_gemm<kFormNoDq>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kFwdLds),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_gemm<kFormDense>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kFwdLds)};
-  const bool dense = w.dense != nullptr;
-  if (attr[dense] != hipSuccess) return attr[dense];
+  const int form = w.dense ? kFormDense : (w.dq ? kFormDq : kFormNoDq);
+  if (attr[form] != hipSuccess) return attr[form];
+  decltype(&k_fwd_gemm<kFormDq>) kern =
+      form == kFormDense ? k_fwd_gemm<kFormDense> : (form == kFormNoDq ? k_fwd_gemm<kFormNoDq> : k_fwd_gemm<kFormDq>);
   const int ptiles = static_cast<int>((w.N + GP - 1) / GP);
   const int qtiles = static_cast<int>((M + GQ - 1) / GQ);
   const GemmSplit sp = fwd_gemm_split(M, w.N, w.K);
   if (sp.splits > 1 && !part) return hipErrorInvalidValue;
   prof_begin(0, stream);
-  hipLaunchKernelGGL(dense ? k_fwd_gemm<true> : k_fwd_gemm<false>,
+  hipLaunchKernelGGL(kern,
                      dim3(ptiles * qtiles * sp.splits), dim3(GT), kFwdLds, stream, X, M, w.dense,
                      w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, B, r, s, Y, ptiles,
                      qtiles, sp.cps, sp.splits > 1 ? part : nullptr, tb, ldt > 0 ? ldt : r,

@@ -10,13 +10,16 @@ namespace qnf4 {
 
 struct Nf4Tables;
 
+// dq: double-quantized constants (absmax_q [nb] bytes, absmax_scale one fp32
+// per 256 blocks), else absmax_scale holds each block's fp32 absmax.
 hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
                            uint8_t* absmax_q, float* absmax_scale,
-                           const Nf4Tables& tb, hipStream_t stream);
+                           const Nf4Tables& tb, hipStream_t stream, bool dq = true);
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
                              const float* absmax_scale, int64_t N, int64_t K,
-                             uint16_t* out, const Nf4Tables& tb, hipStream_t stream);
+                             uint16_t* out, const Nf4Tables& tb, hipStream_t stream,
+                             bool dq = true);
 
 struct Nf4View {
   const uint8_t* codes;
@@ -26,6 +29,8 @@ struct Nf4View {
   // When set, the GEMM launchers read this bf16 weight [N, K] instead of the
   // NF4 fields (the 16-bit LoRA baseline); N K 2 must stay below 2^31 bytes.
   const uint16_t* dense = nullptr;
+  // false: fp32 block constants in absmax_scale [N K / 64], absmax_q unused.
+  bool dq = true;
 };
 
 // Profiling hook: the launchers call these around the launches of one

@@ -4,7 +4,11 @@
 // Format (list items (2) and (3) of "DL0087 QLoRA: 4-bit Quantized LoRA";
 // "Double Quantization and Paged Optimizers" of "QLoRA: Finetuning 65B Models
 // on a Single GPU"): blocks of 64 weights with one absmax each; the absmax
-// constants quantized to 8 bits with one fp32 scale per 256 of them.
+// constants quantized to 8 bits with one fp32 scale per 256 of them.  The
+// level and threshold tables come in as arguments (NF4, or the INT4 / FP4
+// tables of "4-bit NormalFloat" in the same page), and with dq == 0 each
+// block keeps its fp32 absmax instead (the format double quantization
+// improves on).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -18,7 +22,7 @@ namespace qnf4 {
 __global__ __launch_bounds__(256) void k_quantize(
     const float* __restrict__ W, int64_t nblocks, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ absmax_q, float* __restrict__ absmax_scale,
-    Nf4Tables tb) {
+    Nf4Tables tb, int dq) {
   __shared__ float cs[kGroup];
   __shared__ float wmax[4];
   const int tid = threadIdx.x;
@@ -55,8 +59,12 @@ __global__ __launch_bounds__(256) void k_quantize(
   }
   __syncthreads();
 
-  // Second level: group max, d = fl32(max / 255), e = rint(fl32(c / d)).
   const float c = tid < nblk ? cs[tid] : 0.f;
+  if (!dq) {   // fp32 constants: the absmax of every block as it is
+    if (tid < nblk) absmax_scale[b0 + tid] = c;
+    return;
+  }
+  // Second level: group max, d = fl32(max / 255), e = rint(fl32(c / d)).
   float m = c;
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if ((tid & 63) == 0) wmax[tid >> 6] = m;
@@ -81,12 +89,12 @@ __global__ __launch_bounds__(256) void k_quantize(
 __global__ __launch_bounds__(256) void k_dequantize(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ absmax_q,
     const float* __restrict__ absmax_scale, int64_t nchunks,
-    uint16_t* __restrict__ out, Nf4Tables tb) {
+    uint16_t* __restrict__ out, Nf4Tables tb, int dq) {
   const Levels lv = load_levels(tb);
   for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < nchunks;
        c += (int64_t)gridDim.x * blockDim.x) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(codes + c * 16);
-    const Bf16Planes t = block_planes(lv, block_scale(absmax_q, absmax_scale, c >> 1));
+    const Bf16Planes t = block_planes(lv, block_scale(absmax_q, absmax_scale, c >> 1, dq));
     u32x4* dst = reinterpret_cast<u32x4*>(out + c * 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = dequant8_planes(w[i], t);
@@ -95,23 +103,23 @@ __global__ __launch_bounds__(256) void k_dequantize(
 
 hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
                            uint8_t* absmax_q, float* absmax_scale,
-                           const Nf4Tables& tb, hipStream_t stream) {
+                           const Nf4Tables& tb, hipStream_t stream, bool dq) {
   const int64_t nblocks = N * K / kBlock;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
   hipLaunchKernelGGL(k_quantize, dim3(static_cast<unsigned>(ngroups)), dim3(256), 0,
-                     stream, W, nblocks, codes, absmax_q, absmax_scale, tb);
+                     stream, W, nblocks, codes, absmax_q, absmax_scale, tb, dq ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax_q,
                              const float* absmax_scale, int64_t N, int64_t K,
                              uint16_t* out, const Nf4Tables& tb,
-                             hipStream_t stream) {
+                             hipStream_t stream, bool dq) {
   const int64_t nchunks = N * K / 32;
   int64_t grid = (nchunks + 255) / 256;
   if (grid > 65536) grid = 65536;
   hipLaunchKernelGGL(k_dequantize, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                     stream, codes, absmax_q, absmax_scale, nchunks, out, tb);
+                     stream, codes, absmax_q, absmax_scale, nchunks, out, tb, dq ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -73,8 +73,10 @@ typedef enum {
   QLORA_ERR_ALIGN = 4,      /* a device pointer is not 16-byte aligned */
   QLORA_ERR_HIP = 5,        /* a HIP runtime call or kernel launch failed */
   QLORA_ERR_WORKSPACE = 6,  /* workspace too small */
-  QLORA_ERR_SCRATCH = 7     /* qlora_linear_fwd_noalloc: the call needs more than
+  QLORA_ERR_SCRATCH = 7,    /* qlora_linear_fwd_noalloc: the call needs more than
                                QLORA_NOALLOC_SCRATCH_BYTES of workspace */
+  QLORA_ERR_FORMAT = 8      /* qlora_q4_*: unknown codebook, or double_quant
+                               not 0 or 1 */
 } qlora_status;
 
 /* A hipStream_t, passed as an opaque pointer so this header needs no HIP. */
@@ -88,6 +90,45 @@ typedef struct {
   int64_t N;
   int64_t K;
 } qlora_nf4_weight;
+
+/*
+ * 16-entry codebooks of the qlora_q4_* calls: the 4-bit types "4-bit
+ * NormalFloat" of "QLoRA: Finetuning 65B Models on a Single GPU" sets against
+ * each other (NF4 is information-theoretically optimal for normally
+ * distributed weights and beats INT4 and FP4).  Each is 16 fp32 levels over
+ * [-1, 1], ascending; the code of a normalised weight is its nearest level,
+ * ties to the lower index.
+ *   NF4:  the NF4 levels (as qlora_nf4_levels).
+ *   INT4: sixteen levels spaced uniformly, (2k - 15) / 15 for k = 0..15 (no
+ *         zero level).
+ *   FP4:  the sixteen E2M1 floats (sign, 2 exponent bits with bias 1, 1
+ *         mantissa bit) divided by their largest magnitude 6; +0 is code 7,
+ *         -0 code 8 (never produced by quantization).
+ */
+typedef enum {
+  QLORA_CODEBOOK_NF4 = 0,
+  QLORA_CODEBOOK_INT4 = 1,
+  QLORA_CODEBOOK_FP4 = 2
+} qlora_codebook;
+
+/*
+ * Read-only view of a 4-bit weight W [N, K] of any codebook and constant
+ * format.  double_quant = 1: the NF4 format's constants (absmax_q N*K/64
+ * bytes, absmax_scale ceil(N*K/64/256) floats, 4-byte aligned).
+ * double_quant = 0: one fp32 absmax per 64-block in absmax_scale (N*K/64
+ * floats, 16-byte aligned; absmax_q unused and may be NULL): the 0.5
+ * bits-per-parameter format double quantization improves on (list item (3)
+ * of "DL0087 QLoRA": 0.5 to about 0.127 bits).
+ */
+typedef struct {
+  const uint8_t* codes;        /* N*K/2 bytes, 16-byte aligned */
+  const uint8_t* absmax_q;
+  const float* absmax_scale;
+  int64_t N;
+  int64_t K;
+  int32_t codebook;            /* qlora_codebook */
+  int32_t double_quant;        /* 1 or 0 */
+} qlora_q4_weight;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* qlora_status_string(int status);
@@ -300,6 +341,42 @@ int qlora_lora16_bwd(const uint16_t* dY, const uint16_t* X, int64_t M, const uin
                      float s, const float* T_saved, uint16_t* dX, uint16_t* dA,
                      uint16_t* dB, void* workspace, size_t workspace_bytes,
                      qlora_stream_t stream);
+
+/*
+ * The NF4 calls for any codebook and constant format (qlora_q4_weight): the
+ * same kernels with the codebook's level and threshold tables and, without
+ * double quantization, fp32 block constants.  Dequantization is
+ * bf16_rne(fl32(q[code] * c)) with c = fl32(e * d) (double_quant = 1) or the
+ * stored fp32 absmax (double_quant = 0).
+ *   qlora_q4_levels / qlora_q4_thresholds: a codebook's 16 levels and the 15
+ *     fp32 thresholds t_j of its quantizer (code = #{j : x > t_j}), into host
+ *     memory.
+ *   qlora_q4_scale_count: floats of absmax_scale for the format.
+ *   qlora_q4_quantize: as qlora_nf4_quantize, with absmax_q written only when
+ *     double_quant = 1 (may be NULL otherwise).
+ *   qlora_q4_dequantize, qlora_q4_linear_fwd, qlora_q4_linear_bwd: as the
+ *     qlora_nf4 / qlora_linear calls, with the same arguments, limits, path
+ *     selection and workspace sizes (qlora_linear_fwd_workspace_bytes,
+ *     qlora_linear_bwd_workspace_bytes).
+ * Errors: as those calls, plus QLORA_ERR_FORMAT for an unknown codebook or
+ * a double_quant other than 0 or 1.
+ */
+int qlora_q4_levels(int codebook, float* out16);
+int qlora_q4_thresholds(int codebook, float* out15);
+size_t qlora_q4_scale_count(int64_t N, int64_t K, int double_quant);
+int qlora_q4_quantize(const float* W, int64_t N, int64_t K, int codebook, int double_quant,
+                      uint8_t* codes, uint8_t* absmax_q, float* absmax_scale,
+                      qlora_stream_t stream);
+int qlora_q4_dequantize(const qlora_q4_weight* w, uint16_t* W_bf16, qlora_stream_t stream);
+int qlora_q4_linear_fwd(const uint16_t* X, int64_t M, const qlora_q4_weight* w,
+                        const uint16_t* A, const uint16_t* B, int r, float s, uint16_t* Y,
+                        float* T, void* workspace, size_t workspace_bytes,
+                        qlora_stream_t stream);
+int qlora_q4_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
+                        const qlora_q4_weight* w, const uint16_t* A, const uint16_t* B, int r,
+                        float s, const float* T_saved, uint16_t* dX, uint16_t* dA,
+                        uint16_t* dB, void* workspace, size_t workspace_bytes,
+                        qlora_stream_t stream);
 
 /*
  * Kernel timing for measurement.  When enabled (enable != 0), the library

@@ -52,6 +52,53 @@ def test_thresholds_are_oracle_boundaries():
     np.testing.assert_array_equal(nxt.view(np.uint32), oracle.code_boundaries().view(np.uint32))
 
 
+@pytest.mark.parametrize("name", ["nf4", "int4", "fp4"])
+def test_codebook_tables_match_oracle(name):
+    """The library's level table of each codebook equals the oracle's bit for
+    bit, and counting thresholds (code = #{j : x > t_j}) reproduces the
+    oracle's nearest-level code at every threshold and the float above it,
+    which fixes the step function on every float32 in [-1, 1]."""
+    from oracle import codebooks as cb
+    lv = np.array(q.qlora_q4_levels(name), dtype=np.float32)
+    np.testing.assert_array_equal(lv.view(np.uint32), cb.levels(name).view(np.uint32))
+    t = np.array(q.qlora_q4_thresholds(name), dtype=np.float32)
+    assert np.all(np.diff(t.astype(np.float64)) >= 0)
+    probes = np.concatenate([t, np.nextafter(t, np.float32(2), dtype=np.float32),
+                             np.array([-1.0, 0.0, 1.0], np.float32)])
+    rule = (probes[:, None] > t[None, :]).sum(axis=1)
+    np.testing.assert_array_equal(rule, cb.encode_levels(probes, cb.levels(name)))
+    if name == "nf4":
+        np.testing.assert_array_equal(t, np.array(q.qlora_nf4_thresholds(), np.float32))
+
+
+def test_q4_size_and_format_validation():
+    L = q.lib()
+    assert L.qlora_q4_scale_count(64, 1024, 1) == L.qlora_nf4_scale_count(64, 1024)
+    assert L.qlora_q4_scale_count(64, 1024, 0) == 64 * 1024 // 64
+    buf = (ctypes.c_float * 16)()
+    assert L.qlora_q4_levels(3, buf) == q.QLORA_ERR_FORMAT
+    assert L.qlora_q4_levels(-1, buf) == q.QLORA_ERR_FORMAT
+    p = ctypes.c_void_p(4096)
+    # unknown codebook / double_quant flag, before any other check
+    assert L.qlora_q4_quantize(p, 4, 64, 5, 1, p, p, p, None) == q.QLORA_ERR_FORMAT
+    assert L.qlora_q4_quantize(p, 4, 64, 0, 2, p, p, p, None) == q.QLORA_ERR_FORMAT
+    # without double quantization absmax_q may be NULL, but fp32 constants
+    # must be 16-byte aligned
+    assert L.qlora_q4_quantize(p, 4, 100, 1, 0, p, None, p, None) == 2
+    assert L.qlora_q4_quantize(p, 4, 64, 1, 1, p, None, p, None) == 1
+    assert L.qlora_q4_quantize(p, 4, 64, 2, 0, p, None, ctypes.c_void_p(4100), None) == 4
+    w = q._Q4Weight(4096, None, 4096, 64, 128, 1, 0)
+    ws = L.qlora_linear_fwd_workspace_bytes(16, 64, 128, 16)
+    assert L.qlora_q4_linear_fwd(None, 16, ctypes.byref(w), p, p, 16, 1.0, p, p, p, ws,
+                                 None) == 1
+    w.codebook = 7
+    assert L.qlora_q4_linear_fwd(p, 16, ctypes.byref(w), p, p, 16, 1.0, p, p, p, ws,
+                                 None) == q.QLORA_ERR_FORMAT
+    w.codebook, w.double_quant = 2, 1   # double quantization needs absmax_q
+    assert L.qlora_q4_linear_bwd(p, p, 16, ctypes.byref(w), p, p, 16, 1.0, None, p, p, p, p,
+                                 ws, None) == 1
+
+
 def test_size_helpers():
     L = q.lib()
     for N, K in [(1, 64), (1024, 1024), (11008, 4096), (3, 64 * 257)]:
@@ -66,7 +113,7 @@ def test_size_helpers():
 
 def test_status_strings_and_version():
     L = q.lib()
-    for s in range(8):
+    for s in range(9):
         assert L.qlora_status_string(s) != b"unknown status"
     assert L.qlora_status_string(99) == b"unknown status"
     assert L.qlora_version().decode().count(".") == 2
