@@ -30,7 +30,7 @@ from .nf4 import (BLOCK, GROUP, normal_quantile, nf4_levels_f64, nf4_levels,
                   bf16_rne_bits, bf16_bits_to_f64, encode, quantize,
                   unpack_codes, dequantize, dequantize_at, code_boundaries,
                   storage_bytes, bits_per_param)
-from . import codebooks
+from . import adamw, codebooks
 from .linear import (linear_fwd_f64, linear_bwd_f64, linear_fwd, linear_bwd, block_fwd_f64,
                      block_bwd_f64, block_fwd, block_bwd)
 
@@ -39,5 +39,5 @@ __all__ = [
     "bf16_rne_bits", "bf16_bits_to_f64", "encode", "quantize", "unpack_codes",
     "dequantize", "dequantize_at", "code_boundaries", "storage_bytes",
     "bits_per_param", "linear_fwd_f64", "linear_bwd_f64", "linear_fwd",
-    "linear_bwd", "block_fwd_f64", "block_bwd_f64", "block_fwd", "block_bwd", "codebooks",
+    "linear_bwd", "block_fwd_f64", "block_bwd_f64", "block_fwd", "block_bwd", "adamw", "codebooks",
 ]
