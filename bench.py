@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 METRIC = "QLoRA linear fwd+bwd TFLOP/s at M=2048; decode (M=1) effective HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-FAMILIES = {0: "k_fwd_gemm", 1: "k_dx_gemm", 2: "k_fwd_decode", 3: "k_quantize", 4: "rank"}
+FAMILIES = {0: "k_fwd_gemm", 1: "k_dx_gemm", 2: "k_fwd_decode", 3: "k_quantize", 4: "rank",
+            5: "k_adamw"}
 
 
 def log(*a):
@@ -549,6 +550,51 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
     return out
 
 
+def run_adamw(q, torch, dev, reps=20, M=2048):
+    """The adapters' AdamW step over the LLaMA-7B layer's seven adapters (A
+    and B of q, k, v, o, gate, up, down at r = 64: one flat buffer), with the
+    fp32 moments resident in HBM and paged out to pinned host memory; and the
+    page-out / page-in times.  22 bytes move per parameter (bf16 p read and
+    written, bf16 g read, fp32 m and v read and written)."""
+    import workloads
+    cfg = workloads.WORKLOADS["llama7b"]
+    n = sum(l.K * cfg.r + cfg.r * l.N for l in cfg.linears)
+    P = (torch.randn(n, device=dev) * 0.02).to(torch.bfloat16)
+    G = (torch.randn(n, device=dev) * 1e-3).to(torch.bfloat16)
+    st = q.PagedState(n)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(k0):
+        st.step(P, G, k0)   # warm
+        torch.cuda.synchronize()
+        ev[0].record()
+        for k in range(reps):
+            st.step(P, G, k0 + 1 + k)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    ms_dev = timed(1)
+    t0 = time.perf_counter()
+    st.page_out()
+    ms_out = (time.perf_counter() - t0) * 1e3
+    ms_host = timed(100)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    st.page_in()
+    torch.cuda.synchronize()
+    ms_in = (time.perf_counter() - t0) * 1e3
+    st.close()
+    bytes_step = 22 * n
+    return dict(params=n, bytes_per_step=bytes_step,
+                resident_us=1e3 * ms_dev, resident_gbs=bytes_step / (ms_dev * 1e-3) / 1e9,
+                paged_out_us=1e3 * ms_host,
+                paged_out_link_gbs=16 * n / (ms_host * 1e-3) / 1e9,
+                page_out_ms=ms_out, page_in_ms=ms_in, state_mb=8 * n / 1e6,
+                note="moments paged out: the kernel reads and writes them in pinned host memory "
+                     "(16 of the 22 bytes per parameter cross the host link)")
+
+
 def run_peaks(q, torch, dev):
     """Rates this GPU reaches on a plain 4 GiB streaming read and on a loop of
     independent bf16 32x32x16 MFMAs (the library's probe kernels), best of
@@ -773,6 +819,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured-peak probes (4 GiB streaming read, bf16 MFMA loop)")
+    ap.add_argument("--no-adamw", action="store_true",
+                    help="skip the adapters' AdamW step (resident and paged-out moments)")
     ap.add_argument("--no-lora16", action="store_true",
                     help="skip the 16-bit LoRA comparator steps (bf16 base weight)")
     ap.add_argument("--no-fused", action="store_true",
@@ -922,6 +970,14 @@ def main():
             f"kernels (ms per step, eager): {shard['kernels_ms_per_step']}")
         del sh
 
+    opt = None
+    if args.workload == "llama7b" and not args.no_adamw:
+        opt = run_adamw(q, torch, dev)
+        log(f"adamw over {opt['params'] / 1e6:.2f} M adapter parameters: resident "
+            f"{opt['resident_us']:.1f} us ({opt['resident_gbs']:.0f} GB/s), paged out "
+            f"{opt['paged_out_us']:.1f} us ({opt['paged_out_link_gbs']:.1f} GB/s over the link); "
+            f"page-out {opt['page_out_ms']:.2f} ms, page-in {opt['page_in_ms']:.2f} ms")
+
     peaks = None
     if not args.no_peaks:
         peaks = run_peaks(q, torch, dev)
@@ -933,6 +989,9 @@ def main():
             for mk, dv in decode.items():
                 dv["frac_hbm_vendor"] = dv["gbs_call"] / PEAK_HBM_GBS
                 dv["frac_hbm_measured"] = dv["gbs_call"] / peaks["hbm_read_gbs"]
+        if opt is not None:
+            opt["frac_hbm_vendor"] = opt["resident_gbs"] / PEAK_HBM_GBS
+            opt["frac_hbm_measured"] = opt["resident_gbs"] / peaks["hbm_read_gbs"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -971,6 +1030,7 @@ def main():
         "decode_m1_gbs": None if decode is None else decode["M=1"]["gbs_call"],
         "fused_block_step": fused,
         "lora16_step": lora16,
+        "adamw": opt,
         "torch_lora16_step": torch16,
         "dp8_shard": shard,
         "decode": decode,

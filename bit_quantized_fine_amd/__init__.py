@@ -36,6 +36,11 @@ class _Q4Weight(ctypes.Structure):
                 ("double_quant", ctypes.c_int32)]
 
 
+class _AdamWConfig(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
+
+
 _SIGS = {
     "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qlora_version": (ctypes.c_char_p, []),
@@ -120,6 +125,23 @@ _SIGS = {
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_void_p]),
+    "qlora_adamw_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.POINTER(_AdamWConfig), ctypes.c_int64,
+                                        ctypes.c_void_p]),
+    "qlora_paged_state_create": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int,
+                                                ctypes.POINTER(ctypes.c_void_p)]),
+    "qlora_paged_state_destroy": (ctypes.c_int, [ctypes.c_void_p]),
+    "qlora_paged_state_page_out": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "qlora_paged_state_page_in": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "qlora_paged_state_pointers": (ctypes.c_int, [ctypes.c_void_p,
+                                                  ctypes.POINTER(ctypes.c_void_p),
+                                                  ctypes.POINTER(ctypes.c_void_p)]),
+    "qlora_paged_state_resident": (ctypes.c_int, [ctypes.c_void_p]),
+    "qlora_paged_state_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]),
+    "qlora_paged_state_write": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p]),
     "qlora_probe_hbm_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_void_p]),
     "qlora_probe_mfma_bf16": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
@@ -521,6 +543,102 @@ def qlora_q4_linear_bwd(dY, X, w: Q4Weight, A=None, B=None, s: float = 1.0, T=No
     _x_rows(X, w.K)
     return _bwd("qlora_q4_linear_bwd", dY, X, w, _check_q4_weight(w), w._c(), A, B, s, T,
                 need_dx, dX, dA, dB, workspace)
+
+
+def _addr(x):
+    """A torch tensor's data pointer, or an int address as it is."""
+    return ctypes.c_void_p(x if isinstance(x, int) else x.data_ptr())
+
+
+def qlora_adamw_step(param, grad, exp_avg, exp_avg_sq, step: int, lr: float = 2e-4,
+                     beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                     weight_decay: float = 0.0):
+    """One AdamW step, in place: param (bf16, 1-D) and the fp32 moments.
+    exp_avg / exp_avg_sq are fp32 tensors on param's GPU, or device-visible
+    addresses (ints) such as PagedState.pointers() gives."""
+    import torch
+    if param.dim() != 1:
+        raise ValueError("param must be a flat [n] tensor (adapters as slices of one buffer)")
+    n = param.numel()
+    _need(param, "param", (n,), torch.bfloat16)
+    _need(grad, "grad", (n,), torch.bfloat16)
+    named = [("param", param), ("grad", grad)]
+    for name, t in (("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        if not isinstance(t, int):
+            _need(t, name, (n,), torch.float32)
+            named.append((name, t))
+    _on_gpu(named)
+    cfg = _AdamWConfig(lr, beta1, beta2, eps, weight_decay)
+    _check("qlora_adamw_step",
+           lib().qlora_adamw_step(_ptr(param), _ptr(grad), _addr(exp_avg), _addr(exp_avg_sq), n,
+                                  ctypes.byref(cfg), int(step), _stream(param)))
+
+
+class PagedState:
+    """The library's paged optimizer state for n parameters: fp32 moments in
+    HBM while resident, in pinned host memory (read and written by the GPU
+    directly) when paged out."""
+
+    def __init__(self, n: int, on_host: bool = False):
+        h = ctypes.c_void_p()
+        _check("qlora_paged_state_create",
+               lib().qlora_paged_state_create(int(n), int(bool(on_host)), ctypes.byref(h)))
+        self._h, self.n = h, int(n)
+
+    def close(self):
+        if self._h:
+            _check("qlora_paged_state_destroy", lib().qlora_paged_state_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _stream(self):
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def page_out(self):
+        _check("qlora_paged_state_page_out",
+               lib().qlora_paged_state_page_out(self._h, self._stream()))
+
+    def page_in(self):
+        _check("qlora_paged_state_page_in",
+               lib().qlora_paged_state_page_in(self._h, self._stream()))
+
+    @property
+    def resident(self) -> bool:
+        return bool(lib().qlora_paged_state_resident(self._h))
+
+    def pointers(self):
+        """(exp_avg, exp_avg_sq) device-visible addresses of the current copy."""
+        m, v = ctypes.c_void_p(), ctypes.c_void_p()
+        _check("qlora_paged_state_pointers",
+               lib().qlora_paged_state_pointers(self._h, ctypes.byref(m), ctypes.byref(v)))
+        return m.value, v.value
+
+    def read(self, out=None):
+        """The moments as a [2, n] fp32 tensor (m, v) on the current GPU."""
+        import torch
+        if out is None:
+            out = torch.empty((2, self.n), dtype=torch.float32, device="cuda")
+        _need(out, "out", (2, self.n), torch.float32)
+        _check("qlora_paged_state_read",
+               lib().qlora_paged_state_read(self._h, _ptr(out), self._stream()))
+        return out
+
+    def write(self, src):
+        """Set the moments from a [2, n] fp32 tensor (m, v)."""
+        import torch
+        _need(src, "src", (2, self.n), torch.float32)
+        _check("qlora_paged_state_write",
+               lib().qlora_paged_state_write(self._h, _ptr(src), self._stream()))
+
+    def step(self, param, grad, step: int, **hp):
+        m, v = self.pointers()
+        qlora_adamw_step(param, grad, m, v, step, **hp)
 
 
 class _Shape(NamedTuple):

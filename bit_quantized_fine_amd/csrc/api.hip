@@ -355,7 +355,7 @@ size_t block_bwd_ws_bytes(int64_t M, int S, int64_t nseg, int64_t K, int r) {
 // Kernel timing: event pairs around launches, accumulated per family.
 // ---------------------------------------------------------------------------
 
-constexpr int kFamilies = 5;
+constexpr int kFamilies = 6;
 
 struct Profiler {
   std::mutex mu;

@@ -111,4 +111,11 @@ hipError_t launch_grad_in_and_b(const uint16_t* dY, int64_t M, int64_t N, const 
 hipError_t launch_grad_a(const uint16_t* X, int64_t M, int64_t K, const float* G,
                          int r, float s, uint16_t* dA, float* ws, hipStream_t stream);
 
+// One AdamW step over n parameters (bf16 p, g; fp32 m, v, device or
+// device-visible pinned host memory, 16-byte aligned), bias corrections for
+// step `step` (>= 1).
+hipError_t launch_adamw(uint16_t* p, const uint16_t* g, float* m, float* v, int64_t n,
+                        float lr, float beta1, float beta2, float eps, float weight_decay,
+                        int64_t step, hipStream_t stream);
+
 }  // namespace qnf4

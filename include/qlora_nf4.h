@@ -379,6 +379,75 @@ int qlora_q4_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
                         qlora_stream_t stream);
 
 /*
+ * Optimizer step on the adapters, and its state paged between HBM and host
+ * memory (numbered list items (4) and (5) of "DL0087 QLoRA": only the
+ * adapters train, so optimizer state scales with the adapter rank, and the
+ * optimizer states are paged to host RAM during transient memory spikes;
+ * "Memory Management Details" of "QLoRA: Quantized Low Rank Adaptation at
+ * Extreme Scale": paged optimizers offload their states to CPU memory).
+ *
+ * qlora_adamw_step: one AdamW step (decoupled weight decay) over n
+ * parameters, step = 1, 2, ...:
+ *     p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2
+ *     p <- p - lr (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps)
+ * computed in fp32.  param [n] bf16 (updated in place), grad [n] bf16, the
+ * moments exp_avg, exp_avg_sq [n] fp32 (updated in place) -- HBM or the
+ * device-visible address of pinned host memory (qlora_paged_state_pointers
+ * gives either).  All four 16-byte aligned.  Adapters kept in one flat
+ * buffer (A and B of every layer as slices) take one call per step.
+ * Errors: QLORA_ERR_NULL, QLORA_ERR_ALIGN, QLORA_ERR_SHAPE (n < 1, step < 1,
+ * betas outside [0, 1), eps <= 0, lr or weight_decay < 0), QLORA_ERR_HIP.
+ */
+typedef struct {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+} qlora_adamw_config;
+
+int qlora_adamw_step(uint16_t* param, const uint16_t* grad, float* exp_avg, float* exp_avg_sq,
+                     int64_t n, const qlora_adamw_config* cfg, int64_t step,
+                     qlora_stream_t stream);
+
+/*
+ * Paged optimizer state: the moments m and v of n parameters (fp32, zero at
+ * creation), owned by the library.  Resident, they live in HBM of the device
+ * current at creation; paged out, in a pinned host home that the GPU reads
+ * and writes directly (a step on paged-out state runs at the host link's
+ * rate, with the same results bit for bit).  Paging is explicit: there is no
+ * demand paging.
+ *   qlora_paged_state_create: n >= 1; on_host != 0 starts paged out.
+ *   qlora_paged_state_page_out: copies the moments to the host home
+ *     (allocated on first use), waits for the copy on `stream`, frees the HBM
+ *     copy.  A no-op when already paged out.
+ *   qlora_paged_state_page_in: allocates HBM and copies the moments back
+ *     (ordered on `stream`).  If the allocation fails the state stays paged
+ *     out, usable, and QLORA_ERR_HIP is returned.  A no-op when resident.
+ *   qlora_paged_state_pointers: the current m and v (device-visible), to
+ *     pass to qlora_adamw_step; they change with every page-out and page-in.
+ *   qlora_paged_state_resident: 1 when the moments are in HBM, else 0.
+ *   qlora_paged_state_read / _write: copy the moments, as [2][n] fp32 (m
+ *     then v), to or from caller memory (device or host; ordered on
+ *     `stream`), e.g. to checkpoint and restore them.
+ * The page calls allocate or free memory, so they stay outside HIP graph
+ * capture, and run with the creation device current (QLORA_ERR_SHAPE
+ * otherwise); work that uses the state must be ordered before a page-out on
+ * `stream`, which page-out synchronizes.
+ */
+typedef struct qlora_paged_state qlora_paged_state;
+
+int qlora_paged_state_create(int64_t n, int on_host, qlora_paged_state** out);
+int qlora_paged_state_destroy(qlora_paged_state* st);
+int qlora_paged_state_page_out(qlora_paged_state* st, qlora_stream_t stream);
+int qlora_paged_state_page_in(qlora_paged_state* st, qlora_stream_t stream);
+int qlora_paged_state_pointers(const qlora_paged_state* st, float** exp_avg,
+                               float** exp_avg_sq);
+int qlora_paged_state_resident(const qlora_paged_state* st);
+int qlora_paged_state_read(const qlora_paged_state* st, float* dst, qlora_stream_t stream);
+int qlora_paged_state_write(qlora_paged_state* st, const float* src, qlora_stream_t stream);
+
+/*
  * Kernel timing for measurement.  When enabled (enable != 0), the library
  * records a pair of HIP events on the launch stream around every launch of
  * the kernel families below and accumulates their elapsed times; reading
@@ -390,6 +459,7 @@ int qlora_q4_linear_bwd(const uint16_t* dY, const uint16_t* X, int64_t M,
  *   family 2: decode GEMV (forward, M <= 16)
  *   family 3: quantize
  *   family 4: small rank-r GEMMs and reductions (T, G, dA, dB)
+ *   family 5: AdamW step (qlora_adamw_step)
  * qlora_profile_read writes the total milliseconds and launch count of a
  * family (either pointer may be NULL) and returns QLORA_ERR_SHAPE for an
  * unknown family.  qlora_profile_reset clears all totals.
