@@ -233,3 +233,53 @@ def test_noalloc_forward_refuses_calls_beyond_its_scratch():
     # argument errors come first, as in qlora_linear_fwd
     assert L.qlora_linear_fwd_noalloc(None, 4, ctypes.byref(w), 16, 16, 8, 1.0, 16, 16,
                                       None) == 1
+
+
+def test_lora16_validation_before_launch():
+    L = q.lib()
+    p = ctypes.c_void_p(4096)
+    ws = L.qlora_lora16_fwd_workspace_bytes(16, 64, 128, 16)
+    assert ws > 0 and L.qlora_lora16_bwd_workspace_bytes(16, 64, 128, 16) > 0
+    # null weight, K % 64, N % 8, N K above 2^30 (32-bit byte offsets below 2^31)
+    assert L.qlora_lora16_fwd(p, 16, None, 64, 128, p, p, 16, 1.0, p, p, p, ws, None) == 1
+    assert L.qlora_lora16_fwd(p, 16, p, 64, 100, p, p, 16, 1.0, p, p, p, ws, None) == 2
+    assert L.qlora_lora16_fwd(p, 16, p, 60, 128, p, p, 16, 1.0, p, p, p, ws, None) == 2
+    assert L.qlora_lora16_fwd(p, 16, p, 1 << 16, 1 << 15, p, p, 16, 1.0, p, p, p, ws, None) == 2
+    assert L.qlora_lora16_fwd(p, 16, ctypes.c_void_p(4098), 64, 128, p, p, 16, 1.0, p, p, p, ws,
+                              None) == 4
+    # too small a workspace
+    assert L.qlora_lora16_fwd(p, 16, p, 64, 128, p, p, 16, 1.0, p, p, p, 16, None) == 6
+    assert L.qlora_lora16_bwd(p, p, 16, p, 64, 128, p, p, 7, 1.0, None, p, p, p, p, ws,
+                              None) == 3
+
+
+def test_adamw_and_paged_state_validation():
+    L = q.lib()
+    p = ctypes.c_void_p(4096)
+    cfg = q._AdamWConfig(1e-3, 0.9, 0.999, 1e-8, 0.0)
+    assert L.qlora_adamw_step(None, p, p, p, 8, ctypes.byref(cfg), 1, None) == 1
+    assert L.qlora_adamw_step(p, p, p, p, 8, None, 1, None) == 1
+    assert L.qlora_adamw_step(p, p, p, p, 0, ctypes.byref(cfg), 1, None) == 2
+    assert L.qlora_adamw_step(p, p, p, p, 8, ctypes.byref(cfg), 0, None) == 2
+    bad = q._AdamWConfig(1e-3, 0.9, 1.0, 1e-8, 0.0)
+    assert L.qlora_adamw_step(p, p, p, p, 8, ctypes.byref(bad), 1, None) == 2
+    assert L.qlora_adamw_step(p, p, ctypes.c_void_p(4100), p, 8, ctypes.byref(cfg), 1, None) == 4
+    h = ctypes.c_void_p()
+    assert L.qlora_paged_state_create(0, 0, ctypes.byref(h)) == 2
+    assert L.qlora_paged_state_create(8, 0, None) == 1
+    assert L.qlora_paged_state_page_out(None, None) == 1
+    assert L.qlora_paged_state_page_in(None, None) == 1
+    assert L.qlora_paged_state_resident(None) == 0
+    assert L.qlora_paged_state_destroy(None) == 0
+
+
+def test_block_validation_before_launch():
+    L = q.lib()
+    p = ctypes.c_void_p(4096)
+    w = _w(4096, 4096, 4096, 384, 128)
+    ws = L.qlora_block_fwd_workspace_bytes(16, 3, 128, 128, 16)
+    assert ws > 0
+    # S r above 256, r = 0, segments not on 128-row tiles
+    assert L.qlora_block_fwd(p, 16, ctypes.byref(w), 3, p, p, 96, 1.0, p, p, p, ws, None) == 3
+    assert L.qlora_block_fwd(p, 16, ctypes.byref(w), 3, p, p, 0, 1.0, p, p, p, ws, None) == 3
+    assert L.qlora_block_fwd(p, 16, ctypes.byref(w), 2, p, p, 16, 1.0, p, p, p, ws, None) == 2
