@@ -29,6 +29,14 @@
 // fits.  The waves' partial sums meet in LDS; the LoRA update is added as
 // extra MFMA steps over the rank before that reduction.
 //
+// When X does not fit whole and has more than 8 token rows, the SL
+// instantiations stage it in K-slices of 2048 columns (up to 64 KB),
+// together with that slice's block constants: the next slice is loaded into
+// registers while the current one is consumed, and stored at the slice
+// boundary between two workgroup barriers.  Every wave takes the same number
+// of chunks of every slice, so all waves meet at each boundary, and the code
+// ring runs on across it.
+//
 // The level table is an argument (NF4, or the INT4 / FP4 tables of "4-bit
 // NormalFloat" in "QLoRA: Finetuning 65B Models on a Single GPU"), and the
 // NODQ instantiation stages fp32 block constants c_b (no double
@@ -63,7 +71,7 @@ constexpr int kDecXPad = 8;                    // X rows in LDS are K + 8 elemen
 // takes up to 64 partials (TQ = 4); the one reading X from global memory, 32
 // (TQ = 2, registers are short there).  With a final T, the lanes of the
 // LoRA waves use the first two loads for their 8 values.
-constexpr int dec_tq(int fr) { return fr == 1 ? 4 : 2; }
+constexpr int dec_tq(int fr, int sl = 0) { return fr == 1 && sl == 0 ? 4 : 2; }
 constexpr int kDecTSumMaxMR = 4 * (kDecThreads / 16);
 static_assert(kMaxDownPartials <= dec_tq(1) * 16, "partials per lane of a 16-lane row");
 static_assert(kMaxDownPartials / 2 <= dec_tq(2) * 16, "partials per lane of a 16-lane row");
@@ -75,33 +83,41 @@ int round16(int64_t v) { return static_cast<int>((v + 15) / 16 * 16); }
 // Dynamic LDS of one workgroup, in order: the level table, B's columns
 // [r][32], the summed T, the block scales [K/64 + 1][32] fp32, and (XLDS) X
 // [M][K + kDecXPad] (the padding puts the rows' equal columns in different
-// banks) followed by kDecXZero zero bytes.  After the main loop the waves'
-// partial sums [kDecThreads] f32x4 reuse the bytes from the block scales on.
+// banks) followed by kDecXZero zero bytes.  With K-slices of ksl columns the
+// scales and X hold one slice: K is replaced by ksl.  After the main loop the
+// waves' partial sums [kDecThreads] f32x4 reuse the bytes from the block
+// scales on.
 struct DecLds {
   int boff, toff, coff, xoff, total;
-  DecLds(int64_t M, int64_t K, int r, bool xlds, int fr = 1) {
-    const int64_t kb = K / kBlock;
+  DecLds(int64_t M, int64_t K, int r, bool xlds, int fr = 1, int ksl = 0) {
+    const int64_t kx = ksl > 0 ? ksl : K;
+    const int64_t kb = kx / kBlock;
     boff = kRepTabBytes;
     toff = boff + round16(int64_t(64) * r);
     coff = toff + kDecTSumMaxMR * 4;
     xoff = coff + round16(kDecRows * (kb + 1) * 4);
-    const int end = xoff + (xlds ? round16(M * (K + kDecXPad) * 2) + kDecXZero : 0);
+    const int end = xoff + (xlds ? round16(M * (kx + kDecXPad) * 2) + kDecXZero : 0);
     total = end > coff + kDecThreads * 16 * fr ? end : coff + kDecThreads * 16 * fr;
   }
 };
 
 }  // namespace
 
-template <int D, int XP, int FR, bool NODQ>
+template <int D, int XP, int FR, bool NODQ, int SL>
 __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
     int64_t N, int64_t K, const float* __restrict__ T, int nz, float* __restrict__ Tout,
     const uint16_t* __restrict__ Bl, int r, float s, uint16_t* __restrict__ Y,
     Nf4Tables tb, int boff, int toff, int coff, int xoff, float inv_kb, int ldt, int ldb,
-    int ldy) {
+    int ldy, int ksl) {
   constexpr int ROWS = kDecRows;
   constexpr bool XLDS = XP > 0;   // X staged in LDS, XP 16-byte pieces per thread
+  // SL > 0: X and the block constants staged in K-slices of ksl = 2048 SL
+  // columns (every wave takes ksl / 1024 chunks of each slice, a multiple of
+  // the ring depth), SL constants per thread and slice.
+  static_assert(SL == 0 || (XP == 4 && FR == 1 && D == 2), "sliced form");
+  constexpr int CP = SL > 0 ? SL : 1;
   // FR = 1: eight waves per fragment; FR = 2: every wave works on both
   // fragments, and 16 waves split K (each X piece then serves 32 rows).
   constexpr int KS = kDecKSlots * FR;   // waves splitting K
@@ -123,6 +139,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   const int nchunks = (K32 + 127) / 128;
   const int nmine = nchunks > kw ? (nchunks - kw + KS - 1) / KS : 0;
   auto frag = [&](int f) { return FR == 1 ? p : f; };   // fragment of the wave's slot f
+  const int KX = SL > 0 ? ksl : K32;   // columns of X and of the block scales in LDS
+  const int KXB = KX / kBlock;
+  const int nslices = (K32 + KX - 1) / KX;
 
   // Buffer descriptors: rows n >= N fall outside the code / constant buffers
   // and read as zero, and so do token rows li >= M of X.  The second block of
@@ -148,19 +167,21 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   u32x2 ev[kDecEPieces];
   float dv[kDecEPieces];
   u32x4 cv[NODQ ? kDecEPieces : 1][2];   // NODQ: the 8 blocks' fp32 constants
+  if constexpr (SL == 0) {
 #pragma unroll
-  for (int i = 0; i < kDecEPieces; ++i) {
-    const int idx = tid + i * kDecThreads;
-    const bool ok = 8 * idx < erange;
-    if constexpr (NODQ) {
-      const uint32_t o = (e0 + 8u * idx) * 4u;
-      cv[i][0] = buf_load16(rd, ok ? o : kDecOffNone);
-      cv[i][1] = buf_load16(rd, ok ? o + 16u : kDecOffNone);
-    } else {
-      ev[i] = __builtin_bit_cast(
-          u32x2,
-          __builtin_amdgcn_raw_buffer_load_b64(re, ok ? e0 + 8u * idx : kDecOffNone, 0, 0));
-      dv[i] = buf_load_f32(rd, ok ? ((e0 + 8u * idx) / kGroup) * 4u : kDecOffNone);
+    for (int i = 0; i < kDecEPieces; ++i) {
+      const int idx = tid + i * kDecThreads;
+      const bool ok = 8 * idx < erange;
+      if constexpr (NODQ) {
+        const uint32_t o = (e0 + 8u * idx) * 4u;
+        cv[i][0] = buf_load16(rd, ok ? o : kDecOffNone);
+        cv[i][1] = buf_load16(rd, ok ? o + 16u : kDecOffNone);
+      } else {
+        ev[i] = __builtin_bit_cast(
+            u32x2,
+            __builtin_amdgcn_raw_buffer_load_b64(re, ok ? e0 + 8u * idx : kDecOffNone, 0, 0));
+        dv[i] = buf_load_f32(rd, ok ? ((e0 + 8u * idx) / kGroup) * 4u : kDecOffNone);
+      }
     }
   }
   // X: XP pieces per thread, as many as M K 2 bytes need (a load whose lanes
@@ -168,13 +189,59 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // start the staging loads of 16 waves queue there ahead of the code stream)
   u32x4 xw[XLDS ? XP : 1];
   const int xrange = M * K32 * 2;
-  if constexpr (XLDS) {
+  if constexpr (XLDS && SL == 0) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int idx = tid + i * kDecThreads;
       xw[i] = buf_load16(rx, 16 * idx < xrange ? 16u * idx : kDecOffNone);
     }
   }
+  // One K-slice (SL): X piece idx holds columns 8 (idx % (KX / 8)) .. + 7 of
+  // token row idx / (KX / 8); constant entry f is block f / ROWS of the
+  // slice in row f % ROWS (its place in the transposed LDS layout).  Columns
+  // and blocks past K read zero, so the half chunk past K multiplies zeros.
+  uint32_t se[CP];   // e bytes
+  float sd[CP];      // their group scales d, or (NODQ) the fp32 constants
+  const int lgp = SL > 0 ? __builtin_ctz(static_cast<unsigned>(KX / 8)) : 0;
+  auto slice_load = [&](int sg) {
+    const bool any = sg < nslices;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int idx = tid + i * kDecThreads;
+      const int row = idx >> lgp, col = 8 * (idx & ((1 << lgp) - 1));
+      const int gk = sg * KX + col;
+      const bool ok = any && row < M && gk < K32;
+      xw[i] = buf_load16(rx, ok ? static_cast<uint32_t>(row * K32 + gk) * 2u : kDecOffNone);
+    }
+#pragma unroll
+    for (int i = 0; i < CP; ++i) {
+      const int f = tid + i * kDecThreads;
+      const int row = f % ROWS, blk = f / ROWS;
+      const int gb = sg * KXB + blk;
+      const bool ok = any && blk < KXB && gb < KB;
+      const uint32_t b = static_cast<uint32_t>(n0 + row) * KB + gb;   // rows past N: zeros
+      if constexpr (NODQ) {
+        sd[i] = buf_load_f32(rd, ok ? b * 4u : kDecOffNone);
+      } else {
+        se[i] = buf_load_u8(re, ok ? b : kDecOffNone);
+        sd[i] = buf_load_f32(rd, ok ? (b / kGroup) * 4u : kDecOffNone);
+      }
+    }
+  };
+  auto slice_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int idx = tid + i * kDecThreads;
+      const int row = idx >> lgp, col = 8 * (idx & ((1 << lgp) - 1));
+      if (row < M) *reinterpret_cast<u32x4*>(xs + row * (KX + kDecXPad) + col) = xw[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CP; ++i) {
+      const int f = tid + i * kDecThreads;
+      if (f < ROWS * KXB) csc[f] = NODQ ? sd[i] : static_cast<float>(se[i]) * sd[i];
+    }
+  };
+  if constexpr (SL > 0) slice_load(0);
   // T for the LoRA update, used only after the main loop.  With nz > 0, the
   // 16-lane row h sums quad h (4 ranks of one token) over the partials, lane
   // z loading partials z + 16 i; with nz == 0 T is final and the lanes of the
@@ -182,7 +249,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   const int nsteps = (r + 31) / 32;
   const int nq = M * r / 4;
   const int hr = tid >> 4, hl = tid & 15;
-  constexpr int TQ = dec_tq(FR);
+  constexpr int TQ = dec_tq(FR, SL);
   f32x4 tq[TQ];
   {
     // (one load sequence for both cases: a branch here would make the
@@ -241,7 +308,14 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 
   // Stage into LDS: level table, X, block scales, B.
   build_rep_pair_table<kDecThreads>(tab, lv, tid);
-  if constexpr (XLDS) {
+  if constexpr (SL > 0) {
+    slice_store();
+    if (tid < kDecXZero / 16)
+      *reinterpret_cast<u32x4*>(xs + M * (KX + kDecXPad) + 8 * tid) = u32x4{0, 0, 0, 0};
+    if (tid < M)
+      *reinterpret_cast<u32x4*>(xs + tid * (KX + kDecXPad) + KX) = u32x4{0, 0, 0, 0};
+    if (tid < ROWS) csc[KXB * ROWS + tid] = 0.f;
+  } else if constexpr (XLDS) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int idx = tid + i * kDecThreads;
@@ -256,7 +330,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // Block scales c = e . d, transposed so that the four rows of a lane's
   // outputs read 16 consecutive bytes; column KB is zero.
 #pragma unroll
-  for (int i = 0; i < kDecEPieces; ++i) {
+  for (int i = 0; i < (SL > 0 ? 0 : kDecEPieces); ++i) {
     const int idx = tid + i * kDecThreads;
     if (8 * idx < erange) {
 #pragma unroll
@@ -277,14 +351,14 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
       }
     }
   }
-  if (tid < ROWS) csc[KB * ROWS + tid] = 0.f;
+  if (SL == 0 && tid < ROWS) csc[KB * ROWS + tid] = 0.f;
   if ((tid >> 2) < r) reinterpret_cast<u32x4*>(bst)[tid] = bpiece;
 
   // Lanes past M read X from the zero bytes with stride 0.  Past K (the
   // second block of a chunk when K % 128 == 64) the X reads of lanes 32-63
   // stay inside the next token row or the zero bytes, and their weights are
   // zero: their block constant is the zero column KB.
-  const int xrow = K32 + kDecXPad;
+  const int xrow = KX + kDecXPad;
   const uint16_t* xlane = li < M ? xs + li * xrow + xo0 : xs + M * xrow + xo0;
   const int xstep = li < M ? 128 : 0;
   // block constant of the lane's row li and block 2 c + g / 2: + 16 fragment
@@ -301,8 +375,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // are issued before any of their products, so one LDS round trip serves
   // its MFMAs; with two fragments a wave (X from global memory) takes them
   // one after the other, which keeps the lookups of one in registers.
+  int cbase = 0;   // (SL) first chunk of the slice in LDS
   auto compute = [&](int t, int st) {
-    const int c = kw + KS * t;
+    const int c = kw + KS * t - cbase;   // chunk, counted from the first in LDS
     u32x4 xf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -334,12 +409,36 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     }
   };
   __syncthreads();
-  for (int t0 = 0; t0 < nmine; t0 += D) {
+  if constexpr (SL > 0) {
+    // Slice sg: its X and constants are in LDS, the next slice's in flight
+    // to registers; at the boundary, one barrier once every wave is done
+    // with the slice, the stores, and one more before the next slice is read.
+    const int tps = KX / (128 * KS);   // chunks per wave and slice
+    for (int sg = 0; sg < nslices; ++sg) {
+      if (sg > 0) {
+        __syncthreads();
+        slice_store();
+        __syncthreads();
+      }
+      cbase = sg * KS * tps;
+      slice_load(sg + 1);
+      for (int t0 = sg * tps; t0 < (sg + 1) * tps; t0 += D) {
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int t = t0 + u;
-      if (t < nmine) compute(t, u);
-      load(t + D, u);
+        for (int u = 0; u < D; ++u) {
+          const int t = t0 + u;
+          if (t < nmine) compute(t, u);
+          load(t + D, u);
+        }
+      }
+    }
+  } else {
+    for (int t0 = 0; t0 < nmine; t0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int t = t0 + u;
+        if (t < nmine) compute(t, u);
+        load(t + D, u);
+      }
     }
   }
 
@@ -427,28 +526,37 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 
 namespace {
 
-template <int D, int XP, int FR, bool NODQ>
+template <int D, int XP, int FR, bool NODQ, int SL = 0>
 hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w, const float* T,
                                  int nz, float* Tout, const uint16_t* B, int r, float s,
                                  uint16_t* Y, const Nf4Tables& tb, hipStream_t stream, int ldt,
-                                 int ldb, int ldy) {
+                                 int ldb, int ldy, int ksl = 0) {
   // allow the largest dynamic LDS (once per variant)
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_fwd_decode<D, XP, FR, NODQ>),
+      reinterpret_cast<const void*>(&k_fwd_decode<D, XP, FR, NODQ, SL>),
       hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
   if (attr != hipSuccess) return attr;
-  const DecLds L(M, w.K, r, XP > 0, FR);
-  if (L.total > kDecLdsMax || nz > 16 * dec_tq(FR)) return hipErrorInvalidValue;
+  if (SL > 0 && ksl != 2048 * SL) return hipErrorInvalidValue;
+  const DecLds L(M, w.K, r, XP > 0, FR, ksl);
+  if (L.total > kDecLdsMax || nz > 16 * dec_tq(FR, SL)) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>((w.N + kDecRows - 1) / kDecRows);
   const float inv_kb = 1.0f / static_cast<float>(w.K / kBlock);
-  hipLaunchKernelGGL((k_fwd_decode<D, XP, FR, NODQ>), dim3(grid), dim3(kDecThreads), L.total, stream,
-                     X, (int)M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, nz, Tout, B,
-                     r, s, Y, tb, L.boff, L.toff, L.coff, L.xoff, inv_kb, ldt, ldb, ldy);
+  hipLaunchKernelGGL((k_fwd_decode<D, XP, FR, NODQ, SL>), dim3(grid), dim3(kDecThreads), L.total,
+                     stream, X, (int)M, w.codes, w.absmax_q, w.absmax_scale, w.N, w.K, T, nz, Tout,
+                     B, r, s, Y, tb, L.boff, L.toff, L.coff, L.xoff, inv_kb, ldt, ldb, ldy, ksl);
   return hipGetLastError();
 }
 
 bool decode_x_in_lds(int64_t M, int64_t K, int r) {
   return M * K * 2 <= kDecXLdsBytes && DecLds(M, K, r, true).total <= kDecLdsMax;
+}
+
+// Slice width for X in K-slices: 2048 columns when that slice of X (M rows)
+// fits the 64 KB and the layout fits the LDS (always, for M <= 16), else 0.
+int decode_slice(int64_t M, int64_t K, int r) {
+  constexpr int ksl = 2048;
+  return M * ksl * 2 <= kDecXLdsBytes && DecLds(M, K, r, true, 1, ksl).total <= kDecLdsMax
+             ? ksl : 0;
 }
 
 }  // namespace
@@ -477,7 +585,10 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
   // deeper rings (measured up to 8) only delay the first products.
   // X goes to LDS when it fits next to the rest (M = 1 up to K = 22016 with
   // r <= 64; M = 4 up to K = 8192), in as few 16-byte pieces per thread as it
-  // needs; otherwise each wave reads its X pieces from global memory.
+  // needs.  Otherwise, for more than 8 tokens, in K-slices: each wave's X
+  // loads from global memory touch one cache line per token, and at M = 16
+  // the sliced form runs 41 against 46 us at 8192 x 22016; with 4 tokens it
+  // is the slower one (37 against 34 us).
   auto run = [&](auto nodq) {
     constexpr bool ND = decltype(nodq)::value;
     const int lb = static_cast<int>(ldb), ly = static_cast<int>(ldy);
@@ -492,6 +603,13 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
                                                   ldt, lb, ly);
       return launch_decode_variant<2, kDecXPieces, 1, ND>(X, M, w, T, nz, Tout, B, r, s, Y, tb,
                                                           stream, ldt, lb, ly);
+    }
+    switch (M > 8 ? decode_slice(M, w.K, r) : 0) {
+      case 2048:
+        return launch_decode_variant<2, 4, 1, ND, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream,
+                                                     ldt, lb, ly, 2048);
+      default:
+        break;
     }
     // X from global memory: each wave works on both fragments, so each X
     // piece it loads serves 32 rows.

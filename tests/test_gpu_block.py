@@ -63,7 +63,8 @@ BLOCK_CASES = [
     # (M, S, nseg, K, r, s)
     (1, 3, 128, 128, 8, 1.0),        # streaming path, one projection per launch
     (4, 3, 256, 256, 16, 0.5),
-    (16, 2, 128, 512, 64, 0.25),     # streaming path, X from global memory
+    (16, 2, 128, 512, 64, 0.25),     # streaming path, 16 tokens
+    (16, 3, 128, 4096, 16, 0.5),     # streaming path, X in K-slices
     (17, 3, 128, 128, 8, 1.0),       # first GEMM size
     (64, 3, 128, 256, 32, 0.5),      # GEMM with split reductions (few tiles)
     (300, 2, 256, 448, 64, 0.25),    # ragged tokens, K not a multiple of 128

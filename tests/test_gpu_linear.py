@@ -54,12 +54,14 @@ FWD_CASES = [
     (4, 1024, 1024, 16, 1.0),
     (16, 1024, 1024, 16, 1.0),
     (7, 200, 320, 8, 0.5),           # ragged N (not a multiple of 16), K = 5 * 64
-    (16, 1000, 64 * 33, 64, 0.25),   # K with a half chunk; X read from global memory
+    (16, 1000, 64 * 33, 64, 0.25),   # X in two K-slices, the second half a chunk
     (1, 232, 64 * 33, 32, 0.5),      # K with a half chunk; X staged in LDS
-    (4, 96, 16384, 64, 0.25),        # T folded, X too large for LDS
+    (4, 96, 16384, 64, 0.25),        # T folded, X too large for LDS (read from global memory)
     (2, 64, 16384, 8, 0.5),          # X of exactly the LDS staging limit (64 KB); 64 T partials
     (1, 96, 16384 + 64 * 5, 64, 0.25),   # 33 T partial sums, ragged last 256-k slice
     (1, 64, 32768, 64, 0.5),         # one token, X from global memory: at most 32 partials
+    (8, 264, 64 * 133, 16, 0.5),     # 8 tokens, X from global memory, ragged rows
+    (12, 264, 64 * 133, 16, 0.5),    # X in K-slices, the last ragged (half a chunk), ragged rows
     (4, 96, 1024, 256, 0.25),        # M * r too large to fold T into the decode kernel
     (2, 64, 32768 + 64, 8, 0.5),     # K beyond the decode kernel: GEMM path at M = 2
     (17, 1024, 1024, 16, 1.0),       # first GEMM size
@@ -91,7 +93,7 @@ def test_fwd_parity(M, N, K, r, s):
     (1, 256, 8192),       # decode, X in LDS (one 16-byte piece a thread)
     (1, 256, 22016),      # decode, X in LDS (four pieces a thread), 65B FFN width
     (4, 256, 8192),       # decode, X in LDS (four pieces a thread), T folded
-    (16, 256, 8192),      # decode, X from global memory (both fragments a wave)
+    (16, 256, 8192),      # decode, X in K-slices
     (16, 256, 22016),     # the same at the 65B FFN width
     (1, 200, 64 * 33),    # decode, half chunk past K (K % 128 == 64)
     (16, 200, 64 * 33),
