@@ -30,12 +30,12 @@
 // extra MFMA steps over the rank before that reduction.
 //
 // When X does not fit whole and has more than 8 token rows, the SL
-// instantiations stage it in K-slices of 2048 columns (up to 64 KB),
-// together with that slice's block constants: the next slice is loaded into
-// registers while the current one is consumed, and stored at the slice
-// boundary between two workgroup barriers.  Every wave takes the same number
-// of chunks of every slice, so all waves meet at each boundary, and the code
-// ring runs on across it.
+// instantiations stage it in K-slices of 1024 columns (32 KB at 16 tokens),
+// together with that slice's block constants, in two LDS copies used in
+// turn: every wave takes one chunk of every slice, one workgroup barrier
+// ends each slice, and the slice after next is stored into the copy just
+// freed while the waves work on the other, from registers loaded two slices
+// ahead.  The code ring runs on across the boundaries.
 //
 // The level table is an argument (NF4, or the INT4 / FP4 tables of "4-bit
 // NormalFloat" in "QLoRA: Finetuning 65B Models on a Single GPU"), and the
@@ -89,21 +89,21 @@ int round16(int64_t v) { return static_cast<int>((v + 15) / 16 * 16); }
 // scales on.
 struct DecLds {
   int boff, toff, coff, xoff, total;
-  DecLds(int64_t M, int64_t K, int r, bool xlds, int fr = 1, int ksl = 0) {
+  DecLds(int64_t M, int64_t K, int r, bool xlds, int fr = 1, int ksl = 0, int nbuf = 1) {
     const int64_t kx = ksl > 0 ? ksl : K;
     const int64_t kb = kx / kBlock;
     boff = kRepTabBytes;
     toff = boff + round16(int64_t(64) * r);
     coff = toff + kDecTSumMaxMR * 4;
-    xoff = coff + round16(kDecRows * (kb + 1) * 4);
-    const int end = xoff + (xlds ? round16(M * (kx + kDecXPad) * 2) + kDecXZero : 0);
+    xoff = coff + nbuf * round16(kDecRows * (kb + 1) * 4);
+    const int end = xoff + (xlds ? nbuf * round16(M * (kx + kDecXPad) * 2) + kDecXZero : 0);
     total = end > coff + kDecThreads * 16 * fr ? end : coff + kDecThreads * 16 * fr;
   }
 };
 
 }  // namespace
 
-template <int D, int XP, int FR, bool NODQ, int SL>
+template <int D, int XP, int FR, bool NODQ, bool SL>
 __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ absmax_q, const float* __restrict__ absmax_scale,
@@ -113,11 +113,12 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     int ldy, int ksl) {
   constexpr int ROWS = kDecRows;
   constexpr bool XLDS = XP > 0;   // X staged in LDS, XP 16-byte pieces per thread
-  // SL > 0: X and the block constants staged in K-slices of ksl = 2048 SL
-  // columns (every wave takes ksl / 1024 chunks of each slice, a multiple of
-  // the ring depth), SL constants per thread and slice.
-  static_assert(SL == 0 || (XP == 4 && FR == 1 && D == 2), "sliced form");
-  constexpr int CP = SL > 0 ? SL : 1;
+  // SL: X and the block constants staged in K-slices of ksl = 1024 columns
+  // (one chunk of each of the eight waves of a fragment), in two LDS copies
+  // and two register sets used in turn; slice t sits in copy t % 2, which is
+  // also the code ring's slot of chunk t.
+  static_assert(!SL || (XP == 2 && FR == 1 && D == 2), "sliced form");
+  constexpr int NB = SL ? 2 : 1;   // LDS copies of X and of the block constants
   // FR = 1: eight waves per fragment; FR = 2: every wave works on both
   // fragments, and 16 waves split K (each X piece then serves 32 rows).
   constexpr int KS = kDecKSlots * FR;   // waves splitting K
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   const int nchunks = (K32 + 127) / 128;
   const int nmine = nchunks > kw ? (nchunks - kw + KS - 1) / KS : 0;
   auto frag = [&](int f) { return FR == 1 ? p : f; };   // fragment of the wave's slot f
-  const int KX = SL > 0 ? ksl : K32;   // columns of X and of the block scales in LDS
+  const int KX = SL ? ksl : K32;   // columns of X and of the block scales in LDS
   const int KXB = KX / kBlock;
   const int nslices = (K32 + KX - 1) / KX;
 
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   u32x2 ev[kDecEPieces];
   float dv[kDecEPieces];
   u32x4 cv[NODQ ? kDecEPieces : 1][2];   // NODQ: the 8 blocks' fp32 constants
-  if constexpr (SL == 0) {
+  if constexpr (!SL) {
 #pragma unroll
     for (int i = 0; i < kDecEPieces; ++i) {
       const int idx = tid + i * kDecThreads;
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // start the staging loads of 16 waves queue there ahead of the code stream)
   u32x4 xw[XLDS ? XP : 1];
   const int xrange = M * K32 * 2;
-  if constexpr (XLDS && SL == 0) {
+  if constexpr (XLDS && !SL) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int idx = tid + i * kDecThreads;
@@ -197,13 +198,17 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     }
   }
   // One K-slice (SL): X piece idx holds columns 8 (idx % (KX / 8)) .. + 7 of
-  // token row idx / (KX / 8); constant entry f is block f / ROWS of the
-  // slice in row f % ROWS (its place in the transposed LDS layout).  Columns
-  // and blocks past K read zero, so the half chunk past K multiplies zeros.
-  uint32_t se[CP];   // e bytes
-  float sd[CP];      // their group scales d, or (NODQ) the fp32 constants
-  const int lgp = SL > 0 ? __builtin_ctz(static_cast<unsigned>(KX / 8)) : 0;
-  auto slice_load = [&](int sg) {
+  // token row idx / (KX / 8); constant entry f (one per thread) is block
+  // f / ROWS of the slice in row f % ROWS (its place in the transposed LDS
+  // layout).  Columns and blocks past K read zero, so the half chunk past K
+  // multiplies zeros.
+  u32x4 xn[SL ? XP : 1];   // the second register set for X
+  uint32_t se[NB];         // e bytes
+  float sd[NB];            // their group scales d, or (NODQ) the fp32 constants
+  const int lgp = SL ? __builtin_ctz(static_cast<unsigned>(KX / 8)) : 0;
+  // one slice's X and constants in LDS: elements / floats per copy
+  const int xcopy = M * (KX + kDecXPad), ccopy = ROWS * (KXB + 1);
+  auto slice_load = [&](int set, int sg) {
     const bool any = sg < nslices;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
@@ -211,37 +216,33 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
       const int row = idx >> lgp, col = 8 * (idx & ((1 << lgp) - 1));
       const int gk = sg * KX + col;
       const bool ok = any && row < M && gk < K32;
-      xw[i] = buf_load16(rx, ok ? static_cast<uint32_t>(row * K32 + gk) * 2u : kDecOffNone);
+      const u32x4 v = buf_load16(rx, ok ? static_cast<uint32_t>(row * K32 + gk) * 2u : kDecOffNone);
+      if (set == 0) xw[i] = v; else xn[SL ? i : 0] = v;
     }
-#pragma unroll
-    for (int i = 0; i < CP; ++i) {
-      const int f = tid + i * kDecThreads;
-      const int row = f % ROWS, blk = f / ROWS;
-      const int gb = sg * KXB + blk;
-      const bool ok = any && blk < KXB && gb < KB;
-      const uint32_t b = static_cast<uint32_t>(n0 + row) * KB + gb;   // rows past N: zeros
-      if constexpr (NODQ) {
-        sd[i] = buf_load_f32(rd, ok ? b * 4u : kDecOffNone);
-      } else {
-        se[i] = buf_load_u8(re, ok ? b : kDecOffNone);
-        sd[i] = buf_load_f32(rd, ok ? (b / kGroup) * 4u : kDecOffNone);
-      }
+    const int row = tid % ROWS, blk = tid / ROWS;
+    const int gb = sg * KXB + blk;
+    const bool ok = any && blk < KXB && gb < KB;
+    const uint32_t b = static_cast<uint32_t>(n0 + row) * KB + gb;   // rows past N: zeros
+    if constexpr (NODQ) {
+      sd[set] = buf_load_f32(rd, ok ? b * 4u : kDecOffNone);
+    } else {
+      se[set] = buf_load_u8(re, ok ? b : kDecOffNone);
+      sd[set] = buf_load_f32(rd, ok ? (b / kGroup) * 4u : kDecOffNone);
     }
   };
-  auto slice_store = [&]() {
+  auto slice_store = [&](int set, int copy) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       const int idx = tid + i * kDecThreads;
       const int row = idx >> lgp, col = 8 * (idx & ((1 << lgp) - 1));
-      if (row < M) *reinterpret_cast<u32x4*>(xs + row * (KX + kDecXPad) + col) = xw[i];
+      if (row < M)
+        *reinterpret_cast<u32x4*>(xs + copy * xcopy + row * (KX + kDecXPad) + col) =
+            set == 0 ? xw[i] : xn[SL ? i : 0];
     }
-#pragma unroll
-    for (int i = 0; i < CP; ++i) {
-      const int f = tid + i * kDecThreads;
-      if (f < ROWS * KXB) csc[f] = NODQ ? sd[i] : static_cast<float>(se[i]) * sd[i];
-    }
+    if (tid < ROWS * KXB)
+      csc[copy * ccopy + tid] = NODQ ? sd[set] : static_cast<float>(se[set]) * sd[set];
   };
-  if constexpr (SL > 0) slice_load(0);
+  if constexpr (SL) slice_load(0, 0);
   // T for the LoRA update, used only after the main loop.  With nz > 0, the
   // 16-lane row h sums quad h (4 ranks of one token) over the partials, lane
   // z loading partials z + 16 i; with nz == 0 T is final and the lanes of the
@@ -308,13 +309,16 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 
   // Stage into LDS: level table, X, block scales, B.
   build_rep_pair_table<kDecThreads>(tab, lv, tid);
-  if constexpr (SL > 0) {
-    slice_store();
+  if constexpr (SL) {
+    slice_store(0, 0);
     if (tid < kDecXZero / 16)
-      *reinterpret_cast<u32x4*>(xs + M * (KX + kDecXPad) + 8 * tid) = u32x4{0, 0, 0, 0};
-    if (tid < M)
-      *reinterpret_cast<u32x4*>(xs + tid * (KX + kDecXPad) + KX) = u32x4{0, 0, 0, 0};
-    if (tid < ROWS) csc[KXB * ROWS + tid] = 0.f;
+      *reinterpret_cast<u32x4*>(xs + NB * xcopy + 8 * tid) = u32x4{0, 0, 0, 0};
+    if (tid < NB * M)   // row padding of each copy
+      *reinterpret_cast<u32x4*>(xs + (tid / M) * xcopy + (tid % M) * (KX + kDecXPad) + KX) =
+          u32x4{0, 0, 0, 0};
+    if (tid < NB * ROWS) csc[(tid / ROWS) * ccopy + KXB * ROWS + tid % ROWS] = 0.f;
+    slice_load(1, 1);   // slices 1 and 2 in flight (sets 1 and 0)
+    slice_load(0, 2);
   } else if constexpr (XLDS) {
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // Block scales c = e . d, transposed so that the four rows of a lane's
   // outputs read 16 consecutive bytes; column KB is zero.
 #pragma unroll
-  for (int i = 0; i < (SL > 0 ? 0 : kDecEPieces); ++i) {
+  for (int i = 0; i < (SL ? 0 : kDecEPieces); ++i) {
     const int idx = tid + i * kDecThreads;
     if (8 * idx < erange) {
 #pragma unroll
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
       }
     }
   }
-  if (SL == 0 && tid < ROWS) csc[KB * ROWS + tid] = 0.f;
+  if (!SL && tid < ROWS) csc[KB * ROWS + tid] = 0.f;
   if ((tid >> 2) < r) reinterpret_cast<u32x4*>(bst)[tid] = bpiece;
 
   // Lanes past M read X from the zero bytes with stride 0.  Past K (the
@@ -359,8 +363,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // stay inside the next token row or the zero bytes, and their weights are
   // zero: their block constant is the zero column KB.
   const int xrow = KX + kDecXPad;
-  const uint16_t* xlane = li < M ? xs + li * xrow + xo0 : xs + M * xrow + xo0;
+  const uint16_t* xlane = li < M ? xs + li * xrow + xo0 : xs + NB * M * xrow + xo0;
   const int xstep = li < M ? 128 : 0;
+  const int xcstep = li < M ? xcopy : 0;   // (SL) to the second LDS copy
   // block constant of the lane's row li and block 2 c + g / 2: + 16 fragment
   const float* clane = csc + (g >> 1) * ROWS + li;
   // Table addresses: the lane's copy offset in byte 0, entry in byte 1.  The
@@ -375,20 +380,21 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // are issued before any of their products, so one LDS round trip serves
   // its MFMAs; with two fragments a wave (X from global memory) takes them
   // one after the other, which keeps the lookups of one in registers.
-  int cbase = 0;   // (SL) first chunk of the slice in LDS
+  int cbase = 0;   // (SL) first chunk of the slice
   auto compute = [&](int t, int st) {
     const int c = kw + KS * t - cbase;   // chunk, counted from the first in LDS
+    const int cp = SL ? st : 0;          // (SL) LDS copy: slice t in copy t % 2
     u32x4 xf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if constexpr (XLDS)
-        xf[i] = *reinterpret_cast<const u32x4*>(xlane + c * xstep + 8 * i);
+        xf[i] = *reinterpret_cast<const u32x4*>(xlane + cp * xcstep + c * xstep + 8 * i);
       else
         xf[i] = xv[st][i];
     }
 #pragma unroll
     for (int f = 0; f < FR; ++f) {
-      const float ch = clane[16 * frag(f) + 2 * c * ROWS];
+      const float ch = clane[cp * ccopy + 16 * frag(f) + 2 * c * ROWS];
       f32x2 v[4][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -409,26 +415,21 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     }
   };
   __syncthreads();
-  if constexpr (SL > 0) {
-    // Slice sg: its X and constants are in LDS, the next slice's in flight
-    // to registers; at the boundary, one barrier once every wave is done
-    // with the slice, the stores, and one more before the next slice is read.
-    const int tps = KX / (128 * KS);   // chunks per wave and slice
-    for (int sg = 0; sg < nslices; ++sg) {
-      if (sg > 0) {
-        __syncthreads();
-        slice_store();
-        __syncthreads();
-      }
-      cbase = sg * KS * tps;
-      slice_load(sg + 1);
-      for (int t0 = sg * tps; t0 < (sg + 1) * tps; t0 += D) {
+  if constexpr (SL) {
+    // Slice t (chunk t of every wave) is read from copy t % 2.  After the
+    // barrier that ends slice t - 1, slice t + 1 (in registers since two
+    // slices ago) is stored into the other copy, which slice t - 1 used,
+    // and slice t + 3 is loaded into the freed registers.
+    for (int sg = 0; sg < nslices; sg += 2) {
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
-          const int t = t0 + u;
-          if (t < nmine) compute(t, u);
-          load(t + D, u);
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int t = sg + u;
+        if (t > 0) __syncthreads();
+        if (t + 1 < nslices) slice_store(1 - u, 1 - u);
+        slice_load(1 - u, t + 3);
+        cbase = t * KS;
+        if (t < nmine) compute(t, u);
+        load(t + D, u);
       }
     }
   } else {
@@ -526,7 +527,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 
 namespace {
 
-template <int D, int XP, int FR, bool NODQ, int SL = 0>
+template <int D, int XP, int FR, bool NODQ, bool SL = false>
 hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w, const float* T,
                                  int nz, float* Tout, const uint16_t* B, int r, float s,
                                  uint16_t* Y, const Nf4Tables& tb, hipStream_t stream, int ldt,
@@ -536,8 +537,8 @@ hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w,
       reinterpret_cast<const void*>(&k_fwd_decode<D, XP, FR, NODQ, SL>),
       hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
   if (attr != hipSuccess) return attr;
-  if (SL > 0 && ksl != 2048 * SL) return hipErrorInvalidValue;
-  const DecLds L(M, w.K, r, XP > 0, FR, ksl);
+  if (SL && ksl != 1024) return hipErrorInvalidValue;
+  const DecLds L(M, w.K, r, XP > 0, FR, ksl, SL ? 2 : 1);
   if (L.total > kDecLdsMax || nz > 16 * dec_tq(FR, SL)) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>((w.N + kDecRows - 1) / kDecRows);
   const float inv_kb = 1.0f / static_cast<float>(w.K / kBlock);
@@ -551,11 +552,11 @@ bool decode_x_in_lds(int64_t M, int64_t K, int r) {
   return M * K * 2 <= kDecXLdsBytes && DecLds(M, K, r, true).total <= kDecLdsMax;
 }
 
-// Slice width for X in K-slices: 2048 columns when that slice of X (M rows)
-// fits the 64 KB and the layout fits the LDS (always, for M <= 16), else 0.
+// Slice width for X in K-slices: 1024 columns in two LDS copies when they
+// fit (always, for M <= 16), else 0.
 int decode_slice(int64_t M, int64_t K, int r) {
-  constexpr int ksl = 2048;
-  return M * ksl * 2 <= kDecXLdsBytes && DecLds(M, K, r, true, 1, ksl).total <= kDecLdsMax
+  constexpr int ksl = 1024;
+  return M * ksl * 2 <= kDecXLdsBytes / 2 && DecLds(M, K, r, true, 1, ksl, 2).total <= kDecLdsMax
              ? ksl : 0;
 }
 
@@ -587,8 +588,8 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
   // r <= 64; M = 4 up to K = 8192), in as few 16-byte pieces per thread as it
   // needs.  Otherwise, for more than 8 tokens, in K-slices: each wave's X
   // loads from global memory touch one cache line per token, and at M = 16
-  // the sliced form runs 41 against 46 us at 8192 x 22016; with 4 tokens it
-  // is the slower one (37 against 34 us).
+  // the sliced form runs 36 against 46 us at 8192 x 22016; with 4 tokens
+  // (single-copy 4096-column slices) it was the slower one (37 against 34 us).
   auto run = [&](auto nodq) {
     constexpr bool ND = decltype(nodq)::value;
     const int lb = static_cast<int>(ldb), ly = static_cast<int>(ldy);
@@ -604,13 +605,9 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
       return launch_decode_variant<2, kDecXPieces, 1, ND>(X, M, w, T, nz, Tout, B, r, s, Y, tb,
                                                           stream, ldt, lb, ly);
     }
-    switch (M > 8 ? decode_slice(M, w.K, r) : 0) {
-      case 2048:
-        return launch_decode_variant<2, 4, 1, ND, 1>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream,
-                                                     ldt, lb, ly, 2048);
-      default:
-        break;
-    }
+    if (M > 8 && decode_slice(M, w.K, r) == 1024)
+      return launch_decode_variant<2, 2, 1, ND, true>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream,
+                                                      ldt, lb, ly, 1024);
     // X from global memory: each wave works on both fragments, so each X
     // piece it loads serves 32 rows.
     return launch_decode_variant<2, 0, 2, ND>(X, M, w, T, nz, Tout, B, r, s, Y, tb, stream, ldt,

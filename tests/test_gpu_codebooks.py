@@ -97,8 +97,8 @@ LAYER_CASES = [
     # (M, N, K, r): streaming path (X in LDS whole or in K-slices), tiled path
     (1, 256, 1024, 16),
     (4, 200, 64 * 33, 8),    # half a 128-k chunk past K
-    (16, 200, 4096, 64),     # X in 2048-column K-slices
-    (9, 72, 64 * 197, 16),   # X in 2048-column K-slices, the last ragged
+    (16, 200, 4096, 64),     # X in 1024-column K-slices
+    (9, 72, 64 * 197, 16),   # X in 1024-column K-slices, the last ragged
     (300, 264, 448, 32),
 ]
 

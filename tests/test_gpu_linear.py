@@ -54,7 +54,7 @@ FWD_CASES = [
     (4, 1024, 1024, 16, 1.0),
     (16, 1024, 1024, 16, 1.0),
     (7, 200, 320, 8, 0.5),           # ragged N (not a multiple of 16), K = 5 * 64
-    (16, 1000, 64 * 33, 64, 0.25),   # X in two K-slices, the second half a chunk
+    (16, 1000, 64 * 33, 64, 0.25),   # X in three K-slices, the last half a chunk
     (1, 232, 64 * 33, 32, 0.5),      # K with a half chunk; X staged in LDS
     (4, 96, 16384, 64, 0.25),        # T folded, X too large for LDS (read from global memory)
     (2, 64, 16384, 8, 0.5),          # X of exactly the LDS staging limit (64 KB); 64 T partials
