@@ -77,12 +77,23 @@ def percentiles(xs):
     return [float(v) for v in np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])]
 
 
+def q4_format(form):
+    """(codebook, double_quant) of a 4-bit weight form "int4-fp32", "fp4-dq", ...,
+    or None for the NF4 entry points ("nf4") and the bf16 weight ("lora16")."""
+    if form in ("nf4", "lora16"):
+        return None
+    cb, const = form.split("-")
+    return cb, const == "dq"
+
+
 def run_training(q, torch, steps, warmup, dev, key="llama7b", M=None, form="nf4"):
     """One step = fwd + bwd of the workload's seven linears.  The 33B workload
     runs the backward as under gradient checkpointing: T is not kept, the
     backward recomputes it (and dequantizes W again, as every backward does).
     form "lora16" runs the same step with bf16 base weights on the same
-    kernels (the 16-bit LoRA comparator) instead of NF4 ones."""
+    kernels (the 16-bit LoRA comparator) instead of NF4 ones; "int4-fp32",
+    "fp4-dq" (codebook - block constants) run it on the 4-bit codebook
+    variants through the same kernels."""
     import numpy as np
 
     import workloads
@@ -90,6 +101,7 @@ def run_training(q, torch, steps, warmup, dev, key="llama7b", M=None, form="nf4"
     M, r, s = (cfg.M[0] if M is None else M), cfg.r, cfg.s
     recompute = key == "llama33b_recompute"
     dense = form == "lora16"
+    q4 = q4_format(form)
     ws_fwd = (q.lib().qlora_lora16_fwd_workspace_bytes if dense
               else q.lib().qlora_linear_fwd_workspace_bytes)
     ws_bwd = (q.lib().qlora_lora16_bwd_workspace_bytes if dense
@@ -98,7 +110,12 @@ def run_training(q, torch, steps, warmup, dev, key="llama7b", M=None, form="nf4"
     t0 = time.time()
     for lin, inp in workloads.workload_inputs(key, M=M):
         Wg = torch.from_numpy(inp.W).to(dev)
-        w = Wg.to(torch.bfloat16) if dense else q.qlora_nf4_quantize(Wg)
+        if dense:
+            w = Wg.to(torch.bfloat16)
+        elif q4 is not None:
+            w = q.qlora_q4_quantize(Wg, q4[0], q4[1])
+        else:
+            w = q.qlora_nf4_quantize(Wg)
         del Wg
         L = dict(lin=lin, w=w, X=bf16_dev(inp.X, dev), A=bf16_dev(inp.A, dev),
                  B=bf16_dev(inp.B, dev), dY=bf16_dev(inp.dY, dev))
@@ -113,8 +130,10 @@ def run_training(q, torch, steps, warmup, dev, key="llama7b", M=None, form="nf4"
     torch.cuda.synchronize()
     log(f"setup (draw + upload + {'convert' if dense else 'quantize'} {len(layers)} linears): "
         f"{time.time() - t0:.1f}s")
-    fwd = q.qlora_lora16_fwd if dense else q.qlora_linear_fwd
-    bwd = q.qlora_lora16_bwd if dense else q.qlora_linear_bwd
+    fwd = (q.qlora_lora16_fwd if dense else q.qlora_q4_linear_fwd if q4 is not None
+           else q.qlora_linear_fwd)
+    bwd = (q.qlora_lora16_bwd if dense else q.qlora_q4_linear_bwd if q4 is not None
+           else q.qlora_linear_bwd)
 
     def step():
         for L in layers:
@@ -455,30 +474,38 @@ def run_stack(q, torch, dev, steps=2, warmup=1):
                 ms_token_eager=ms_token_eager, token_gbs=alg / (ms_token * 1e-3) / 1e9)
 
 
-def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
+def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9, form="nf4", Ms=None):
     """Decode GB/s on the 65B shapes, rotating over >1 GB of weight copies.
 
     The rate is device time per call: one pass over the pool is captured as
     a graph (the calls allocate nothing and record no memsets) and replayed;
-    the eager per-call time, host launch path included, is reported too."""
+    the eager per-call time, host launch path included, is reported too.
+    form: "nf4", or a 4-bit codebook variant ("int4-fp32", "fp4-dq", ...)
+    whose weight bytes (codes and block constants) are counted as such."""
     import workloads
     cfg = workloads.WORKLOADS["decode_65b"]
     r, s = cfg.r, cfg.s
+    q4 = q4_format(form)
+    fwd_call = q.qlora_q4_linear_fwd if q4 is not None else q.qlora_linear_fwd
     g = torch.Generator(device=dev)
     g.manual_seed(2000)
     out = {}
-    for M in cfg.M:
+    for M in (cfg.M if Ms is None else Ms):
         tot_bytes, tot_ms, kern_bytes, kern_ms = 0.0, 0.0, 0.0, 0.0
         per_shape = {}
         for lin in cfg.linears:
             N, K = lin.N, lin.K
-            nf4_bytes = N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256)
+            if q4 is not None and not q4[1]:   # one fp32 constant per block
+                nf4_bytes = N * K // 2 + 4 * (N * K // 64)
+            else:
+                nf4_bytes = N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256)
             copies = max(2, int(pool_bytes // nf4_bytes) + 1)
             pool = []
             for _ in range(copies):
                 W = torch.randn((N, K), generator=g, device=dev) * 0.02
                 W = torch.where(torch.rand((N, K), generator=g, device=dev) < 0.001, W * 10, W)
-                pool.append(q.qlora_nf4_quantize(W))
+                pool.append(q.qlora_q4_quantize(W, q4[0], q4[1]) if q4 is not None
+                            else q.qlora_nf4_quantize(W))
                 del W
             X = (torch.randn((M, K), generator=g, device=dev)).to(torch.bfloat16)
             A = (torch.randn((K, r), generator=g, device=dev) / r).to(torch.bfloat16)
@@ -488,13 +515,13 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
             ws = torch.empty(q.lib().qlora_linear_fwd_workspace_bytes(M, N, K, r),
                              dtype=torch.uint8, device=dev)
             for w in pool[:2]:
-                q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
+                fwd_call(X, w, A, B, s, Y=Y, T=T, workspace=ws)
             torch.cuda.synchronize()
             # eager per-call rate (includes the Python launch path)
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ev0.record()
             for w in pool:
-                q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
+                fwd_call(X, w, A, B, s, Y=Y, T=T, workspace=ws)
             ev1.record()
             torch.cuda.synchronize()
             ms_eager = ev0.elapsed_time(ev1) / len(pool)
@@ -503,7 +530,7 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
                 for w in pool:
-                    q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
+                    fwd_call(X, w, A, B, s, Y=Y, T=T, workspace=ws)
             graph.replay()
             torch.cuda.synchronize()
             ev0.record()
@@ -515,7 +542,7 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
             calls = reps * len(pool)
             # the last call of every replay used pool[-1]: recompute it eagerly
             Y_graph = Y.clone()
-            q.qlora_linear_fwd(X, pool[-1], A, B, s, Y=Y, T=T, workspace=ws)
+            fwd_call(X, pool[-1], A, B, s, Y=Y, T=T, workspace=ws)
             torch.cuda.synchronize()
             if not torch.equal(Y_graph, Y):
                 raise RuntimeError(f"decode {N}x{K} M={M}: graph replay differs from eager call")
@@ -525,7 +552,7 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
             q.qlora_profile_enable(True)
             for _ in range(max(1, reps // 4)):
                 for w in pool:
-                    q.qlora_linear_fwd(X, w, A, B, s, Y=Y, T=T, workspace=ws)
+                    fwd_call(X, w, A, B, s, Y=Y, T=T, workspace=ws)
             torch.cuda.synchronize()
             q.qlora_profile_enable(False)
             kms, kn = q.qlora_profile_read(2)
@@ -545,7 +572,7 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9):
         out[f"M={M}"] = dict(gbs_call=tot_bytes / (tot_ms * 1e-3) / 1e9,
                              gbs_decode_kernel=kern_bytes / (kern_ms * 1e-3) / 1e9,
                              shapes=per_shape)
-        log(f"decode M={M}: {out[f'M={M}']['gbs_call']:.0f} GB/s per call, "
+        log(f"decode {form} M={M}: {out[f'M={M}']['gbs_call']:.0f} GB/s per call, "
             f"{out[f'M={M}']['gbs_decode_kernel']:.0f} GB/s decode kernel")
     return out
 
@@ -823,6 +850,8 @@ def main():
                     help="skip the adapters' AdamW step (resident and paged-out moments)")
     ap.add_argument("--no-lora16", action="store_true",
                     help="skip the 16-bit LoRA comparator steps (bf16 base weight)")
+    ap.add_argument("--no-codebooks", action="store_true",
+                    help="skip the INT4 / FP4 / fp32-constant variants (step and M=1 decode)")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the extra step with q/k/v and gate/up run as fused blocks")
     ap.add_argument("--no-shard", action="store_true",
@@ -956,6 +985,29 @@ def main():
         log(f"16-bit LoRA step as torch bf16 matmuls: {torch16['ms_per_step']:.3f} ms "
             f"({torch16['timing']}), {torch16['tflops']:.1f} TFLOP/s")
 
+    variants = None
+    if args.workload == "llama7b" and not args.no_codebooks:
+        # the codebook / constant variants through the same kernels: the
+        # training step and the M = 1 decode (weight bytes counted per format)
+        variants = {}
+        for form in ("int4-fp32", "fp4-dq"):
+            v = run_training(q, torch, args.steps, args.warmup, dev, key="llama7b", form=form)
+            vd = dict(ms_per_step=v["ms_step"],
+                      tflops=v["flops_step"] / (v["ms_step"] * 1e-3) / 1e12,
+                      time_over_nf4=v["ms_step"] / tr["ms_step"])
+            del v
+            if not args.no_decode:
+                dm = run_decode(q, torch, dev, reps=args.decode_reps, form=form, Ms=[1])["M=1"]
+                vd["decode_m1"] = dict(gbs_call=dm["gbs_call"],
+                                       gbs_decode_kernel=dm["gbs_decode_kernel"],
+                                       us_per_call={k: x["us_per_call"]
+                                                    for k, x in dm["shapes"].items()})
+            variants[form] = vd
+            log(f"{form}: step {vd['ms_per_step']:.3f} ms ({vd['tflops']:.1f} TFLOP/s, "
+                f"{vd['time_over_nf4']:.3f} of the NF4 time)"
+                + (f"; decode M=1 {vd['decode_m1']['gbs_call']:.0f} GB/s per call"
+                   if "decode_m1" in vd else ""))
+
     shard = None
     if args.workload == "llama7b" and not args.no_shard:
         # extra data point: the same step at the per-GPU share of 8-way data
@@ -1032,6 +1084,7 @@ def main():
         "lora16_step": lora16,
         "adamw": opt,
         "torch_lora16_step": torch16,
+        "codebook_variants": variants,
         "dp8_shard": shard,
         "decode": decode,
         "kernels": kernels,
