@@ -9,10 +9,44 @@
 // tables of "4-bit NormalFloat" in the same page), and with dq == 0 each
 // block keeps its fp32 absmax instead (the format double quantization
 // improves on).
+#include <cmath>
+#include <cstring>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace qnf4 {
+
+// Buckets of the quantizer's code search (k_quantize): 34 per sign.
+constexpr int kBucketsPerSign = 34;
+constexpr int kBuckets = 2 * kBucketsPerSign;
+constexpr int kBucketBias = 221;   // one below bits 30..22 of 2^-16 (222)
+struct QuantBuckets {
+  uint32_t base[kBuckets];   // thresholds below the whole bucket
+  uint32_t ta[kBuckets];     // fp32 bits of the thresholds inside it (+inf if none)
+  uint32_t tb[kBuckets];
+};
+
+// The code of a normalised weight x in [-1, 1] is #{j : x > t_j} over the
+// 15 thresholds.  Instead of 15 comparisons, x's bucket -- its sign, its
+// binary exponent and its top mantissa bit (half an octave), with every
+// |x| < 2^-16 in one bucket per sign -- selects a table entry holding the
+// count of thresholds below the whole bucket and the (at most two)
+// thresholds inside it; the code is that count plus two comparisons.  The
+// host builds the entries from the threshold table (QuantBuckets below).
+constexpr int kBucketCopies = 16;   // lane l reads copy l % 16: no bank conflicts
+
+__device__ __forceinline__ uint32_t bucket_code(const u32x4* btab, float x, int copy) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const int b = max(static_cast<int>((u >> 22) & 0x1FFu) - kBucketBias, 0);
+  const int idx = b + static_cast<int>(u >> 31) * kBucketsPerSign;
+  const u32x4 e = btab[idx * kBucketCopies + copy];
+  // (elements copied to plain values first: this compiler bit-casts element
+  // 0 when __builtin_bit_cast is given a vector element)
+  const uint32_t base = e.x, ta = e.y, tb = e.z;
+  return base + (x > __builtin_bit_cast(float, ta) ? 1u : 0u) +
+         (x > __builtin_bit_cast(float, tb) ? 1u : 0u);
+}
 
 // One workgroup per double-quantization group of 256 blocks (16384 weights).
 // 256 threads; each iteration covers 16 blocks, one block per 16 lanes, each
@@ -22,10 +56,17 @@ namespace qnf4 {
 __global__ __launch_bounds__(256) void k_quantize(
     const float* __restrict__ W, int64_t nblocks, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ absmax_q, float* __restrict__ absmax_scale,
-    Nf4Tables tb, int dq) {
+    QuantBuckets bk, int dq) {
   __shared__ float cs[kGroup];
   __shared__ float wmax[4];
+  __shared__ u32x4 btab[kBuckets * kBucketCopies];
   const int tid = threadIdx.x;
+  for (int i = tid; i < kBuckets * kBucketCopies; i += 256) {
+    const int e = i / kBucketCopies;
+    btab[i] = u32x4{bk.base[e], bk.ta[e], bk.tb[e], 0u};
+  }
+  __syncthreads();
+  const int copy = tid & (kBucketCopies - 1);
   const int64_t g = blockIdx.x;
   const int64_t b0 = g * kGroup;
   const int nblk = static_cast<int>(min<int64_t>(kGroup, nblocks - b0));
@@ -38,21 +79,18 @@ __global__ __launch_bounds__(256) void k_quantize(
       const int64_t elem = (b0 + bl) * kBlock + sub * 4;
       const float4 v = *reinterpret_cast<const float4*>(W + elem);
       float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-      m = fmaxf(m, __shfl_xor(m, 8, 16));
-      m = fmaxf(m, __shfl_xor(m, 4, 16));
-      m = fmaxf(m, __shfl_xor(m, 2, 16));
-      m = fmaxf(m, __shfl_xor(m, 1, 16));
+      // max over the block's 16 lanes (a DPP row): pairs, quads, the row's
+      // halves (half mirror), then both halves (mirror)
+      m = fmaxf(m, dpp_f32<0xB1>(m));
+      m = fmaxf(m, dpp_f32<0x4E>(m));
+      m = fmaxf(m, dpp_f32<0x141>(m));
+      m = fmaxf(m, dpp_f32<0x140>(m));
       // IEEE divide; an all-zero block divides zeros by 1 (code 7).
       const float c = m > 0.f ? m : 1.f;
       const float x[4] = {v.x / c, v.y / c, v.z / c, v.w / c};
       uint32_t packed = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t code = 0;
-#pragma unroll
-        for (int j = 0; j < 15; ++j) code += (x[i] > tb.t[j]) ? 1u : 0u;
-        packed |= code << (4 * i);
-      }
+      for (int i = 0; i < 4; ++i) packed |= bucket_code(btab, x[i], copy) << (4 * i);
       *reinterpret_cast<uint16_t*>(codes + elem / 2) = static_cast<uint16_t>(packed);
       if (sub == 0) cs[bl] = m;
     }
@@ -101,13 +139,58 @@ __global__ __launch_bounds__(256) void k_dequantize(
   }
 }
 
+// Bucket entries from the threshold table.  Bucket b of a sign holds the
+// x of that sign whose bits 30..22 (exponent, top mantissa bit) are b + 221
+// (b >= 1: |x| in [2^e (1 + m/2), 2^e (1 + (m + 1)/2)) with e >= -16), or
+// below 222 (b = 0: |x| < 2^-16, zero and subnormals included).  For the
+// bucket's least and greatest members lo <= hi, a threshold t < lo counts for
+// every member, one with t >= hi for none, and one in [lo, hi) is compared
+// (x > t); unused comparison slots hold +inf.  Returns false if a bucket
+// would need more than two comparisons (no 4-bit table here does).
+bool build_quant_buckets(const float* t, QuantBuckets& out) {
+  auto f32 = [](uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; };
+  auto bits = [](float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; };
+  for (int sign = 0; sign < 2; ++sign) {
+    for (int b = 0; b < kBucketsPerSign; ++b) {
+      uint32_t lo_u, hi_u;   // magnitudes of the bucket's extreme members
+      if (b == 0) {
+        lo_u = 0u;
+        hi_u = (static_cast<uint32_t>(kBucketBias + 1) << 22) - 1u;
+      } else {
+        lo_u = static_cast<uint32_t>(b + kBucketBias) << 22;
+        hi_u = lo_u + (1u << 22) - 1u;
+        if (hi_u > 0x3F800000u) hi_u = 0x3F800000u;   // |x| <= 1
+      }
+      const float lo = sign ? -f32(hi_u) : f32(lo_u);
+      const float hi = sign ? -f32(lo_u) : f32(hi_u);
+      uint32_t base = 0, nc = 0;
+      float cmp[2] = {INFINITY, INFINITY};
+      for (int j = 0; j < 15; ++j) {
+        if (t[j] < lo) {
+          ++base;
+        } else if (t[j] < hi) {
+          if (nc == 2) return false;
+          cmp[nc++] = t[j];
+        }
+      }
+      const int e = b + sign * kBucketsPerSign;
+      out.base[e] = base;
+      out.ta[e] = bits(cmp[0]);
+      out.tb[e] = bits(cmp[1]);
+    }
+  }
+  return true;
+}
+
 hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
                            uint8_t* absmax_q, float* absmax_scale,
                            const Nf4Tables& tb, hipStream_t stream, bool dq) {
+  QuantBuckets bk;
+  if (!build_quant_buckets(tb.t, bk)) return hipErrorInvalidValue;
   const int64_t nblocks = N * K / kBlock;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
   hipLaunchKernelGGL(k_quantize, dim3(static_cast<unsigned>(ngroups)), dim3(256), 0,
-                     stream, W, nblocks, codes, absmax_q, absmax_scale, tb, dq ? 1 : 0);
+                     stream, W, nblocks, codes, absmax_q, absmax_scale, bk, dq ? 1 : 0);
   return hipGetLastError();
 }
 
