@@ -35,13 +35,64 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+# The sources that define each kernel whose HBM traffic the bench reports: a
+# stored counter reading is used only while these files are unchanged.
+KERNEL_SOURCES = {
+    "k_fwd_gemm": ("gemm_fwd.hip", "device_common.hpp", "kernels.hpp"),
+    "k_dx_gemm": ("gemm_dx.hip", "device_common.hpp", "kernels.hpp"),
+}
+
+
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_fine_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def write_traffic(fetch_dir, write_dir, copy_mib, source_note, path=None):
+    """profiles/traffic.json from two rocprofv3 counter runs of the same
+    command (FETCH_SIZE, then WRITE_SIZE), each with a calibration copy of
+    copy_mib MiB (`--copy-calibration-mib`): per kernel, the mean counter
+    reading per dispatch in KiB, scaled by bytes moved / counter reading of
+    the copy, and the hash of the kernel's sources."""
+    import csv
+    means, scale = {}, {}
+    for counter, root in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        agg = {}
+        for path in _rocprof_csvs(root, "counter_collection.csv"):
+            for r in csv.DictReader(open(path)):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                key = ("neg" if "neg_kernel" in name else
+                       next((k for k in KERNEL_SOURCES if f"{k}<0>" in name), None))
+                if key:
+                    agg.setdefault(key, []).append(float(r["Counter_Value"]))
+        if "neg" not in agg:
+            raise SystemExit(f"{root}: no calibration copy in the {counter} run")
+        scale[counter] = copy_mib * 1024.0 / (sum(agg["neg"]) / len(agg["neg"]))
+        for k, v in agg.items():
+            if k != "neg":
+                means.setdefault(k, {})[counter] = (sum(v) / len(v), len(v))
+    out = {}
+    for k, m in sorted(means.items()):
+        fk, wk = m["FETCH_SIZE"][0], m["WRITE_SIZE"][0]
+        fb, wb = fk * 1024 * scale["FETCH_SIZE"], wk * 1024 * scale["WRITE_SIZE"]
+        out[k] = dict(bytes_per_launch=fb + wb, fetch_bytes_per_launch=fb,
+                      write_bytes_per_launch=wb, fetch_kib_raw=round(fk, 1),
+                      write_kib_raw=round(wk, 1), fetch_scale=round(scale["FETCH_SIZE"], 4),
+                      write_scale=round(scale["WRITE_SIZE"], 4),
+                      dispatches=m["FETCH_SIZE"][1], src_hash=kernel_source_hash(k),
+                      launches="mean over the dispatches of the profiled run",
+                      source=source_note)
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
 
 
 def stored_traffic(kernel, src_hash):
@@ -875,7 +926,17 @@ def main():
                     help="print a text summary of a rocprofv3 csv output folder and exit")
     ap.add_argument("--by-grid", action="store_true",
                     help="with --summarize-rocprof: counter means per kernel and grid size")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE "
+                         "rocprofv3 run (each with --copy-calibration-mib) and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        if not args.copy_calibration_mib:
+            raise SystemExit("--write-traffic needs --copy-calibration-mib (the size the runs used)")
+        out = write_traffic(*args.write_traffic, args.copy_calibration_mib,
+                            "profiles/train_step_traffic.md")
+        print(json.dumps(out, indent=1))
+        return
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof, args.copy_calibration_mib,
                                 by_grid=args.by_grid))
@@ -942,7 +1003,7 @@ def main():
         kern, kms, kn, kflops = "k_dx_gemm", dx_ms, dx_n, tr["dx_flops"]
     steps_timed = args.steps
     achieved = kflops * steps_timed / (kms * 1e-3) / 1e12
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash(kern)
     traffic = stored_traffic(kern, src_hash)
     roofline = dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic, kernel=kern,

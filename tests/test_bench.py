@@ -29,3 +29,29 @@ def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def _counter_csv(folder, counter, rows):
+    os.makedirs(folder, exist_ok=True)
+    with open(os.path.join(folder, "pmc_counter_collection.csv"), "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for name, value in rows:
+            f.write(f'"{name}",{counter},{value}\n')
+
+
+def test_traffic_record_scales_counters_by_the_calibration_copy(tmp_path):
+    """FETCH_SIZE reads half of a 1 GiB copy's bytes here (scale 2), WRITE_SIZE
+    all of them (scale 1); a GEMM reading 1000 KiB and writing 300 KiB per
+    dispatch (mean of two) then moved 2.0e6 + 0.3e6 KiB-scaled bytes, and the
+    record carries the hash of the kernel's own sources."""
+    fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel>(int)"
+    fwd = "void qnf4::k_fwd_gemm<0>(unsigned short const*, long)"
+    _counter_csv(fetch, "FETCH_SIZE", [(neg, 524288.0), (fwd, 900.0), (fwd, 1100.0)])
+    _counter_csv(write, "WRITE_SIZE", [(neg, 1048576.0), (fwd, 300.0), (fwd, 300.0)])
+    out = bench.write_traffic(fetch, write, 1024, "test", path=str(tmp_path / "t.json"))
+    rec = out["k_fwd_gemm"]
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["bytes_per_launch"] == pytest.approx(1000 * 1024 * 2 + 300 * 1024)
+    assert rec["src_hash"] == bench.kernel_source_hash("k_fwd_gemm")
+    assert bench.kernel_source_hash("k_fwd_gemm") != bench.kernel_source_hash("k_dx_gemm")

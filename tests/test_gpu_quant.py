@@ -88,19 +88,54 @@ def test_edge_blocks_bit_exact():
                                   oracle.dequantize(*ref, *W.shape))
 
 
-def test_every_float32_in_unit_interval_encodes_like_oracle():
+def _codebook_boundaries(codebook):
+    """For j = 1..15, the smallest float32 in [-1, 1] whose oracle code (the
+    nearest level of the codebook, ties to the lower index) is >= j, found by
+    bisection over the ordered float32 values (the code is a non-decreasing
+    step function of x)."""
+    if codebook == "nf4":
+        return oracle.code_boundaries()
+    from oracle import codebooks
+    lv = codebooks.levels(codebook)
+    one = int(np.array([1.0], np.float32).view(np.uint32)[0])
+
+    def f32_of(o):
+        u = np.array([abs(o)], dtype=np.uint32).view(np.float32)[0]
+        return u if o >= 0 else -u
+
+    def code(o):
+        return int(codebooks.encode_levels(np.array([f32_of(o)], np.float32), lv)[0])
+
+    out = np.empty(15, dtype=np.float32)
+    for j in range(1, 16):
+        lo, hi = -one, one
+        if code(lo) >= j:          # code j is reached at -1 already
+            out[j - 1] = np.float32(-1.0)
+            continue
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if code(mid) >= j:
+                hi = mid
+            else:
+                lo = mid
+        out[j - 1] = f32_of(hi)
+    return out
+
+
+@pytest.mark.parametrize("codebook", ["nf4", "int4", "fp4"])
+def test_every_float32_in_unit_interval_encodes_like_oracle(codebook):
     """All 2.13e9 float32 values in [-1, 1] go through the quantize kernel in
     blocks whose 64th element is +1.0 (so the block scale is exactly 1 and the
     normalised value equals the input); their codes must equal the oracle's
-    nearest-level code, given by its 15 boundaries."""
+    nearest-level code of the codebook, given by its 15 boundaries."""
     need_gpu()
-    bnd = torch.from_numpy(oracle.code_boundaries()).to(dev())
+    bnd = torch.from_numpy(_codebook_boundaries(codebook)).to(dev())
     one = int(np.array([1.0], np.float32).view(np.uint32)[0])
     per_blk = 63
     chunk_blocks = 1 << 22
     total = 0
     for sign in (0, 1):
-        say(f"exhaustive sweep sign={sign}")
+        say(f"exhaustive sweep {codebook} sign={sign}")
         start = 0
         while start <= one:
             nvals = min(per_blk * chunk_blocks, one + 1 - start)
@@ -112,7 +147,8 @@ def test_every_float32_in_unit_interval_encodes_like_oracle():
             vals = pat.to(torch.int32).view(torch.float32).view(nblk, per_blk)
             W = torch.ones((nblk, 64), dtype=torch.float32, device=dev())
             W[:, :per_blk] = vals
-            w = q.qlora_nf4_quantize(W)
+            w = (q.qlora_nf4_quantize(W) if codebook == "nf4"
+                 else q.qlora_q4_quantize(W, codebook, True))
             c = w.codes
             codes = torch.stack([c & 15, c >> 4], dim=1).view(nblk, 64)[:, :per_blk]
             expect = torch.bucketize(vals, bnd, right=True).to(torch.uint8)
