@@ -62,8 +62,8 @@ def write_traffic(fetch_dir, write_dir, copy_mib, source_note, path=None):
     means, scale = {}, {}
     for counter, root in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         agg = {}
-        for path in _rocprof_csvs(root, "counter_collection.csv"):
-            for r in csv.DictReader(open(path)):
+        for csv_path in _rocprof_csvs(root, "counter_collection.csv"):
+            for r in csv.DictReader(open(csv_path)):
                 if r["Counter_Name"] != counter:
                     continue
                 name = r["Kernel_Name"]

@@ -55,3 +55,15 @@ def test_traffic_record_scales_counters_by_the_calibration_copy(tmp_path):
     assert rec["bytes_per_launch"] == pytest.approx(1000 * 1024 * 2 + 300 * 1024)
     assert rec["src_hash"] == bench.kernel_source_hash("k_fwd_gemm")
     assert bench.kernel_source_hash("k_fwd_gemm") != bench.kernel_source_hash("k_dx_gemm")
+
+
+def test_traffic_record_leaves_the_counter_files_alone(tmp_path):
+    fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
+    neg = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel>(int)"
+    dx = "void qnf4::k_dx_gemm<0>(unsigned short const*, long)"
+    _counter_csv(fetch, "FETCH_SIZE", [(neg, 524288.0), (dx, 10.0)])
+    _counter_csv(write, "WRITE_SIZE", [(neg, 1048576.0), (dx, 5.0)])
+    before = open(os.path.join(write, "pmc_counter_collection.csv")).read()
+    bench.write_traffic(fetch, write, 1024, "test", path=str(tmp_path / "t.json"))
+    assert open(os.path.join(write, "pmc_counter_collection.csv")).read() == before
+    assert set(bench.json.load(open(tmp_path / "t.json"))) == {"k_dx_gemm"}
