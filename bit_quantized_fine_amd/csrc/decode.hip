@@ -73,6 +73,14 @@ constexpr int kDecXPad = 8;                    // X rows in LDS are K + 8 elemen
 // LoRA waves use the first two loads for their 8 values.
 constexpr int dec_tq(int fr, int sl = 0) { return fr == 1 && sl == 0 ? 4 : 2; }
 constexpr int kDecTSumMaxMR = 4 * (kDecThreads / 16);
+// More T values than that (up to one per thread: M r <= kDecTFinMaxMR) are
+// summed after the main loop instead, one value per thread over the
+// partials in order, without registers held through the loop.
+constexpr int kDecTFinMaxMR = kDecThreads;
+int dec_tfin_floats(int64_t M, int r) {
+  return M * r > kDecTSumMaxMR && M * r <= kDecTFinMaxMR ? static_cast<int>(M * r)
+                                                         : kDecTSumMaxMR;
+}
 static_assert(kMaxDownPartials <= dec_tq(1) * 16, "partials per lane of a 16-lane row");
 static_assert(kMaxDownPartials / 2 <= dec_tq(2) * 16, "partials per lane of a 16-lane row");
 // Block constants of the workgroup's rows, read as 8-byte pieces.
@@ -94,7 +102,7 @@ struct DecLds {
     const int64_t kb = kx / kBlock;
     boff = kRepTabBytes;
     toff = boff + round16(int64_t(64) * r);
-    coff = toff + kDecTSumMaxMR * 4;
+    coff = toff + round16(int64_t(4) * dec_tfin_floats(M, r));
     xoff = coff + nbuf * round16(kDecRows * (kb + 1) * 4);
     const int end = xoff + (xlds ? nbuf * round16(M * (kx + kDecXPad) * 2) + kDecXZero : 0);
     total = end > coff + kDecThreads * 16 * fr ? end : coff + kDecThreads * 16 * fr;
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   char* tab = reinterpret_cast<char*>(dyn);                          // fp32 level pairs
   uint16_t* bst = reinterpret_cast<uint16_t*>(dyn + boff);           // B columns [r][ROWS]
-  f32x4* tfin = reinterpret_cast<f32x4*>(dyn + toff);                // [kDecTSumMaxMR / 4]
+  f32x4* tfin = reinterpret_cast<f32x4*>(dyn + toff);   // the summed T [M r / 4]
   float* csc = reinterpret_cast<float*>(dyn + coff);                 // [KB + 1][ROWS]
   f32x4* red = reinterpret_cast<f32x4*>(dyn + coff);                 // after the main loop
   uint16_t* xs = reinterpret_cast<uint16_t*>(dyn + xoff);            // [M][K + pad], zeros
@@ -249,6 +257,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // LoRA waves load their own 8 values of it (the first two loads).
   const int nsteps = (r + 31) / 32;
   const int nq = M * r / 4;
+  const bool late_fold = nz > 0 && M * r > kDecTSumMaxMR;   // summed after the main loop
   const int hr = tid >> 4, hl = tid & 15;
   constexpr int TQ = dec_tq(FR, SL);
   f32x4 tq[TQ];
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
       const int z = hl + 16 * i;
-      const bool ok = nz > 0 ? (hr < nq && z < nz) : (lora_lane && i < 2);
+      const bool ok = nz > 0 ? (!late_fold && hr < nq && z < nz) : (lora_lane && i < 2);
       const int idx = nz > 0 ? z * M * r + 4 * hr : li * ldt + j + 4 * i;
       tq[i] = __builtin_bit_cast(
           f32x4, buf_load16(rt, ok ? static_cast<uint32_t>(idx * 4) : kDecOffNone));
@@ -463,7 +472,19 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // the lane's four partials, then a butterfly over its 16-lane row with DPP
   // moves (xor 1, xor 2, rotate 4, rotate 8), in a fixed order
   // (deterministic).
-  if (nz > 0) {
+  if (late_fold) {
+    // one T value per thread, its nz partials added in partial order
+    // (deterministic)
+    const int mr = M * r;
+    const BufRes rt = make_bufres(T, static_cast<uint32_t>(nz * mr) * 4u);
+    if (tid < mr) {
+      float t = 0.f;
+#pragma unroll 8
+      for (int z = 0; z < nz; ++z) t += buf_load_f32(rt, static_cast<uint32_t>(z * mr + tid) * 4u);
+      reinterpret_cast<float*>(tfin)[tid] = t;
+      if (blockIdx.x == 0) Tout[tid] = t;   // [M][r]
+    }
+  } else if (nz > 0) {
     f32x4 v = tq[0] + tq[1];
     if constexpr (TQ == 4) v = (tq[0] + tq[1]) + (tq[2] + tq[3]);
 #pragma unroll
@@ -571,7 +592,7 @@ int decode_max_t_partials(int64_t M, int64_t K, int r) {
 }
 
 bool decode_folds_t(int64_t M, int r) {
-  return r > 0 && M <= 4 && M * r <= kDecTSumMaxMR;
+  return r > 0 && M * r <= kDecTFinMaxMR;
 }
 
 hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
@@ -619,7 +640,7 @@ hipError_t launch_fwd_decode(const uint16_t* X, int64_t M, const Nf4View& w,
   return e;
 }
 
-static_assert(kRepTabBytes + 64 * kDecMaxR + kDecTSumMaxMR * 4 +
+static_assert(kRepTabBytes + 64 * kDecMaxR + kDecTFinMaxMR * 4 +
                       kDecRows * (kDecMaxK / kBlock + 1) * 4 <= kDecLdsMax,
               "block scales of the largest K fit next to the table without X");
 
