@@ -38,7 +38,10 @@ constexpr int kBucketCopies = 16;   // lane l reads copy l % 16: no bank conflic
 
 __device__ __forceinline__ uint32_t bucket_code(const u32x4* btab, float x, int copy) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const int b = max(static_cast<int>((u >> 22) & 0x1FFu) - kBucketBias, 0);
+  // (clamped at both ends: a weight that is not finite, which the format
+  // excludes, still reads inside the table)
+  const int b =
+      min(max(static_cast<int>((u >> 22) & 0x1FFu) - kBucketBias, 0), kBucketsPerSign - 1);
   const int idx = b + static_cast<int>(u >> 31) * kBucketsPerSign;
   const u32x4 e = btab[idx * kBucketCopies + copy];
   // (elements copied to plain values first: this compiler bit-casts element
