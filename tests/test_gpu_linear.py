@@ -62,7 +62,9 @@ FWD_CASES = [
     (1, 64, 32768, 64, 0.5),         # one token, X from global memory: at most 32 partials
     (8, 264, 64 * 133, 16, 0.5),     # 8 tokens, X from global memory, ragged rows
     (12, 264, 64 * 133, 16, 0.5),    # X in K-slices, the last ragged (half a chunk), ragged rows
-    (4, 96, 1024, 256, 0.25),        # M * r too large to fold T into the decode kernel
+    (4, 96, 1024, 256, 0.25),        # M r = 1024: the most T values added after the main loop
+    (5, 96, 1024, 256, 0.25),        # M r = 1280: T reduced by a launch of its own
+    (8, 96, 16384, 64, 0.25),        # T added after the main loop, X read from global memory
     (2, 64, 32768 + 64, 8, 0.5),     # K beyond the decode kernel: GEMM path at M = 2
     (17, 1024, 1024, 16, 1.0),       # first GEMM size
     (300, 520, 448, 64, 0.25),       # ragged M, N, K over several tiles
@@ -70,7 +72,7 @@ FWD_CASES = [
     (129, 136, 64, 8, 2.0),          # single reduction tile
     (520, 264, 192, 40, 0.5),        # rank not a multiple of 32, three token tiles
     (1, 8, 64, 8, 1.0),              # smallest decode: 8 rows, one block (half a 128-k chunk)
-    (3, 8, 64, 256, 0.5),            # rank above K, decode with a separate T reduction
+    (3, 8, 64, 256, 0.5),            # rank above K, T added after the main loop (M r = 768)
     (2048, 8, 64, 8, 1.0),           # GEMM with one 8-row tile and eight token tiles
     (40, 4104, 128, 16, 0.25),       # N a multiple of 8 only (513 x 8)
 ]
