@@ -525,14 +525,16 @@ def run_stack(q, torch, dev, steps=2, warmup=1):
                 ms_token_eager=ms_token_eager, token_gbs=alg / (ms_token * 1e-3) / 1e9)
 
 
-def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9, form="nf4", Ms=None):
+def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9, form="nf4", Ms=None, shapes=None):
     """Decode GB/s on the 65B shapes, rotating over >1 GB of weight copies.
 
     The rate is device time per call: one pass over the pool is captured as
     a graph (the calls allocate nothing and record no memsets) and replayed;
     the eager per-call time, host launch path included, is reported too.
     form: "nf4", or a 4-bit codebook variant ("int4-fp32", "fp4-dq", ...)
-    whose weight bytes (codes and block constants) are counted as such."""
+    whose weight bytes (codes and block constants) are counted as such.
+    Ms and shapes ("NxK" strings) restrict the sweep, e.g. to tell one
+    shape's counters apart from another's with the same kernel and grid."""
     import workloads
     cfg = workloads.WORKLOADS["decode_65b"]
     r, s = cfg.r, cfg.s
@@ -546,6 +548,8 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9, form="nf4", Ms=None):
         per_shape = {}
         for lin in cfg.linears:
             N, K = lin.N, lin.K
+            if shapes is not None and f"{N}x{K}" not in shapes:
+                continue
             if q4 is not None and not q4[1]:   # one fp32 constant per block
                 nf4_bytes = N * K // 2 + 4 * (N * K // 64)
             else:
@@ -620,6 +624,8 @@ def run_decode(q, torch, dev, reps=20, pool_bytes=1.1e9, form="nf4", Ms=None):
             kern_ms += kms
             del pool
             torch.cuda.empty_cache()
+        if not per_shape:
+            continue
         out[f"M={M}"] = dict(gbs_call=tot_bytes / (tot_ms * 1e-3) / 1e9,
                              gbs_decode_kernel=kern_bytes / (kern_ms * 1e-3) / 1e9,
                              shapes=per_shape)
@@ -888,6 +894,24 @@ def summarize_rocprof(root, copy_mib, top=16, by_grid=False):
     return "\n".join(lines)
 
 
+def _int_list(text):
+    """"1,16" -> [1, 16]: token counts of the decode path (1 <= M <= 16)."""
+    vals = [int(v) for v in text.split(",") if v.strip()]
+    if not vals or any(not 1 <= v <= 16 for v in vals):
+        raise argparse.ArgumentTypeError(f"token counts between 1 and 16 expected, got {text!r}")
+    return vals
+
+
+def _shape_list(text):
+    """"8192x8192,22016x8192" -> the same names, checked against the decode sweep's shapes."""
+    import workloads
+    known = tuple(f"{lin.N}x{lin.K}" for lin in workloads.WORKLOADS["decode_65b"].linears)
+    vals = [v.strip() for v in text.split(",") if v.strip()]
+    if not vals or any(v not in known for v in vals):
+        raise argparse.ArgumentTypeError(f"shapes among {', '.join(known)} expected, got {text!r}")
+    return vals
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -913,6 +937,11 @@ def main():
                          "numbers (for profiling it on its own)")
     ap.add_argument("--decode-reps", type=int, default=20,
                     help="graph replays per shape in the decode leg")
+    ap.add_argument("--decode-m", type=_int_list, default=None, metavar="M[,M...]",
+                    help="with --decode-only: only these token counts (of 1, 4, 16)")
+    ap.add_argument("--decode-shapes", type=_shape_list, default=None, metavar="NxK[,NxK...]",
+                    help="with --decode-only: only these weight shapes (of 8192x8192, "
+                         "22016x8192, 8192x22016)")
     ap.add_argument("--workload", default="llama7b",
                     choices=("llama7b", "llama33b_recompute", "stack_65b"),
                     help="llama7b: the headline (LLaMA-7B linears, M=2048); "
@@ -930,6 +959,8 @@ def main():
                     help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE "
                          "rocprofv3 run (each with --copy-calibration-mib) and exit")
     args = ap.parse_args()
+    if (args.decode_m or args.decode_shapes) and not args.decode_only:
+        ap.error("--decode-m and --decode-shapes go with --decode-only")
     if args.write_traffic:
         if not args.copy_calibration_mib:
             raise SystemExit("--write-traffic needs --copy-calibration-mib (the size the runs used)")
@@ -964,9 +995,11 @@ def main():
         del src, dst
 
     if args.decode_only:
-        dec = run_decode(q, torch, dev, reps=args.decode_reps)
-        print(json.dumps({"metric": "QLoRA decode (M=1) effective HBM GB/s, 65B shapes",
-                          "value": dec["M=1"]["gbs_call"], "unit": "GB/s", "n_gpus": 1,
+        dec = run_decode(q, torch, dev, reps=args.decode_reps, Ms=args.decode_m,
+                         shapes=args.decode_shapes)
+        first = "M=1" if "M=1" in dec else next(iter(dec))
+        print(json.dumps({"metric": f"QLoRA decode ({first}) effective HBM GB/s, 65B shapes",
+                          "value": dec[first]["gbs_call"], "unit": "GB/s", "n_gpus": 1,
                           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
                           "decode": dec}), flush=True)
         return

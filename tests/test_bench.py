@@ -67,3 +67,21 @@ def test_traffic_record_leaves_the_counter_files_alone(tmp_path):
     bench.write_traffic(fetch, write, 1024, "test", path=str(tmp_path / "t.json"))
     assert open(os.path.join(write, "pmc_counter_collection.csv")).read() == before
     assert set(bench.json.load(open(tmp_path / "t.json"))) == {"k_dx_gemm"}
+
+
+def test_decode_filters_parse_and_reject_what_the_sweep_lacks():
+    assert bench._int_list("1,16") == [1, 16]
+    assert bench._shape_list("22016x8192") == ["22016x8192"]
+    for bad in ("0", "17", "", "1,32"):
+        with pytest.raises(bench.argparse.ArgumentTypeError):
+            bench._int_list(bad)
+    for bad in ("4096x4096", "8192x8192,1x1", ""):
+        with pytest.raises(bench.argparse.ArgumentTypeError):
+            bench._shape_list(bad)
+
+
+def test_decode_filters_need_decode_only():
+    import subprocess
+    p = subprocess.run([sys.executable, bench.__file__, "--decode-m", "1"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode != 0 and "--decode-only" in p.stderr
