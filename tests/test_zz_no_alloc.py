@@ -28,6 +28,7 @@ def _case(M, N, K, r, s, seed):
     ((256, 4096, 4096, 64, 0.25), (4, 512, 2048, 64, 0.25)),     # GEMM split (32 MiB), then decode
     ((300, 520, 448, 64, 0.25), (16, 256, 1024, 16, 1.0)),       # GEMM + T split, then decode
     ((2048, 1024, 1024, 0, 1.0), (64, 128, 256, 8, 0.5)),        # base only, then a small GEMM
+    ((16, 1024, 4096, 64, 0.25), (8, 256, 1024, 64, 0.5)),       # decode, T added after the main loop
 ])
 def test_noalloc_matches_workspace_forward(shapes):
     need_gpu()
