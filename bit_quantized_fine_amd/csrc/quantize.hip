@@ -88,9 +88,38 @@ __global__ __launch_bounds__(256) void k_quantize(
       m = fmaxf(m, dpp_f32<0x4E>(m));
       m = fmaxf(m, dpp_f32<0x141>(m));
       m = fmaxf(m, dpp_f32<0x140>(m));
-      // IEEE divide; an all-zero block divides zeros by 1 (code 7).
+      // x = fl32(w / c); an all-zero block divides zeros by 1 (code 7).
       const float c = m > 0.f ? m : 1.f;
-      const float x[4] = {v.x / c, v.y / c, v.z / c, v.w / c};
+      float x[4];
+      if (c >= 0x1p-96f && c <= 0x1p125f) {
+        // Markstein's quotient: with y = RN(1/c) and q = RN(w y), the
+        // remainder r = w - q c is a float that an fma forms exactly, and
+        // RN(q + r y) = RN(w / c).  The range of c keeps y normal and keeps
+        // r clear of the subnormal range for |q| >= 2^-6, below the
+        // smallest nonzero threshold of the three tables (NF4's, 0.021).
+        // Between 2^-120 and 2^-6 only the sign of x decides the code, and
+        // q has the quotient's sign; below 2^-120 the quotient may round to
+        // zero, which decides the code where a table has a threshold at
+        // zero (INT4, FP4), so those weights take the IEEE divide.
+        const float y = 1.0f / c;
+        const float w[4] = {v.x, v.y, v.z, v.w};
+        float qmin = 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float q = w[i] * y;
+          x[i] = __builtin_fmaf(__builtin_fmaf(-q, c, w[i]), y, q);
+          qmin = fminf(qmin, fabsf(q));
+        }
+        if (qmin < 0x1p-120f) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = w[i] / c;
+        }
+      } else {   // IEEE divide
+        x[0] = v.x / c;
+        x[1] = v.y / c;
+        x[2] = v.z / c;
+        x[3] = v.w / c;
+      }
       uint32_t packed = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) packed |= bucket_code(btab, x[i], copy) << (4 * i);

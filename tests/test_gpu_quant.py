@@ -162,28 +162,34 @@ def test_every_float32_in_unit_interval_encodes_like_oracle(codebook):
 
 
 # Block constants for the quotient sweep: weight-like scales, values next to
-# a power of two, a tiny and a large one.
-_SWEEP_CONSTANTS = [0.0213, 0.37, float(np.nextafter(np.float32(1), np.float32(0))), 1.5,
-                    3.0e-5, 2.0 ** -60, 2.0 ** 20]
+# a power of two, tiny and large ones (2^-100 and 2^126 lie outside the range
+# where the kernel forms the quotient from the reciprocal), and, for the
+# tables with a threshold at zero (INT4, FP4), constants above 1, whose
+# quotients of subnormal weights round to zero or not.
+_SWEEP_CASES = [("nf4", c) for c in (
+    0.0213, 0.37, float(np.nextafter(np.float32(1), np.float32(0))), 1.5, 3.0, 3.0e-5,
+    2.0 ** -60, 2.0 ** 20, 2.0 ** -100, 2.0 ** 126)] + [
+    ("int4", 3.0), ("int4", 2.0 ** 20), ("int4", 2.0 ** -100),
+    ("fp4", 1.5), ("fp4", 2.0 ** -60), ("fp4", 2.0 ** 126)]
 
 
-@pytest.mark.parametrize("cval", _SWEEP_CONSTANTS)
-def test_every_quotient_by_a_block_constant_encodes_like_oracle(cval):
+@pytest.mark.parametrize("codebook,cval", _SWEEP_CASES)
+def test_every_quotient_by_a_block_constant_encodes_like_oracle(codebook, cval):
     """Every float32 w with |w| <= c goes through the quantize kernel in blocks
     whose 64th element is c, so the block constant is exactly c and every
-    code is the nearest NF4 level of fl32(w / c).  The reference quotient is
-    taken in float64 and rounded once to float32, which is the correctly
+    code is the oracle's nearest level of fl32(w / c).  The reference quotient
+    is taken in float64 and rounded once to float32, which is the correctly
     rounded float32 quotient (53 >= 2 * 24 + 2 bits), then encoded with the
-    oracle's 15 boundaries."""
+    codebook's 15 boundaries."""
     need_gpu()
     c32 = np.float32(cval)
     cbits = int(np.array([c32], np.float32).view(np.uint32)[0])
-    bnd = torch.from_numpy(oracle.code_boundaries()).to(dev())
+    bnd = torch.from_numpy(_codebook_boundaries(codebook)).to(dev())
     per_blk = 63
     chunk_blocks = 1 << 22
     total = 0
     for sign in (0, 1):
-        say(f"quotient sweep c={float(c32):.6g} sign={sign}")
+        say(f"quotient sweep {codebook} c={float(c32):.6g} sign={sign}")
         start = 0
         while start <= cbits:
             nvals = min(per_blk * chunk_blocks, cbits + 1 - start)
@@ -195,7 +201,8 @@ def test_every_quotient_by_a_block_constant_encodes_like_oracle(cval):
             vals = pat.to(torch.int32).view(torch.float32).view(nblk, per_blk)
             W = torch.full((nblk, 64), float(c32), dtype=torch.float32, device=dev())
             W[:, :per_blk] = vals
-            w = q.qlora_nf4_quantize(W)
+            w = (q.qlora_nf4_quantize(W) if codebook == "nf4"
+                 else q.qlora_q4_quantize(W, codebook, True))
             cc = w.codes
             codes = torch.stack([cc & 15, cc >> 4], dim=1).view(nblk, 64)[:, :per_blk]
             x = (vals.double() / float(c32)).float()
