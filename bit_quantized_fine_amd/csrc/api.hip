@@ -235,8 +235,7 @@ int fwd_impl(const uint16_t* X, int64_t M, const Nf4View& v, const Nf4Tables& tb
     // T's partial sums are added up inside the decode kernel (no reduction
     // launch); its workgroup 0 writes T.
     int nz = 0;
-    e = launch_lora_down_partials(X, M, v.K, A, r, decode_max_t_partials(M, v.K, r), ws, &nz,
-                                  hs);
+    e = launch_lora_down_partials(X, M, v.K, A, r, kMaxDownPartials, ws, &nz, hs);
     if (e == hipSuccess) e = launch_fwd_decode(X, M, v, ws, nz, T, B, r, s, Y, tb, hs);
     return hip_status(e);
   }

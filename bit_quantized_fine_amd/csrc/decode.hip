@@ -68,14 +68,15 @@ constexpr int kDecXPad = 8;                    // X rows in LDS are K + 8 elemen
 // T partial sums are added up by rows of 16 lanes: row h takes the quad (4
 // ranks of one token) h, its lane z the partials z + 16 i, i < TQ.  M r <=
 // kDecTSumMaxMR keeps that within one quad per row.  A kernel with X in LDS
-// takes up to 64 partials (TQ = 4); the one reading X from global memory, 32
-// (TQ = 2, registers are short there).  With a final T, the lanes of the
-// LoRA waves use the first two loads for their 8 values.
+// holds up to 64 partials so (TQ = 4); the others, 32 (TQ = 2, registers are
+// short there).  With a final T, the lanes of the LoRA waves use the first
+// two loads for their 8 values.
 constexpr int dec_tq(int fr, int sl = 0) { return fr == 1 && sl == 0 ? 4 : 2; }
 constexpr int kDecTSumMaxMR = 4 * (kDecThreads / 16);
-// More T values than that (up to one per thread: M r <= kDecTFinMaxMR) are
-// summed after the main loop instead, one value per thread over the
-// partials in order, without registers held through the loop.
+// More T values than that (up to one per thread: M r <= kDecTFinMaxMR), or
+// more partials than the registers hold, are summed after the main loop
+// instead, one value per thread over the partials in order, without
+// registers held through the loop.
 constexpr int kDecTFinMaxMR = kDecThreads;
 int dec_tfin_floats(int64_t M, int r) {
   return M * r > kDecTSumMaxMR && M * r <= kDecTFinMaxMR ? static_cast<int>(M * r)
@@ -257,7 +258,9 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
   // LoRA waves load their own 8 values of it (the first two loads).
   const int nsteps = (r + 31) / 32;
   const int nq = M * r / 4;
-  const bool late_fold = nz > 0 && M * r > kDecTSumMaxMR;   // summed after the main loop
+  // summed after the main loop: more T values than the 16-lane rows take,
+  // or more partials than their registers hold
+  const bool late_fold = nz > 0 && (M * r > kDecTSumMaxMR || nz > 16 * dec_tq(FR, SL));
   const int hr = tid >> 4, hl = tid & 15;
   constexpr int TQ = dec_tq(FR, SL);
   f32x4 tq[TQ];
@@ -478,9 +481,18 @@ __global__ __launch_bounds__(kDecThreads) void k_fwd_decode(
     const int mr = M * r;
     const BufRes rt = make_bufres(T, static_cast<uint32_t>(nz * mr) * 4u);
     if (tid < mr) {
+      // 16 loads in flight at a time; partials past nz read as zero, and
+      // adding zero leaves the sum (never -0 here) as it was
       float t = 0.f;
-#pragma unroll 8
-      for (int z = 0; z < nz; ++z) t += buf_load_f32(rt, static_cast<uint32_t>(z * mr + tid) * 4u);
+      for (int z0 = 0; z0 < nz; z0 += 16) {
+        float pz[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          pz[i] = buf_load_f32(rt, z0 + i < nz ? static_cast<uint32_t>((z0 + i) * mr + tid) * 4u
+                                               : kDecOffNone);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) t += pz[i];
+      }
       reinterpret_cast<float*>(tfin)[tid] = t;
       if (blockIdx.x == 0) Tout[tid] = t;   // [M][r]
     }
@@ -560,7 +572,7 @@ hipError_t launch_decode_variant(const uint16_t* X, int64_t M, const Nf4View& w,
   if (attr != hipSuccess) return attr;
   if (SL && ksl != 1024) return hipErrorInvalidValue;
   const DecLds L(M, w.K, r, XP > 0, FR, ksl, SL ? 2 : 1);
-  if (L.total > kDecLdsMax || nz > 16 * dec_tq(FR, SL)) return hipErrorInvalidValue;
+  if (L.total > kDecLdsMax || nz > kMaxDownPartials) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>((w.N + kDecRows - 1) / kDecRows);
   const float inv_kb = 1.0f / static_cast<float>(w.K / kBlock);
   hipLaunchKernelGGL((k_fwd_decode<D, XP, FR, NODQ, SL>), dim3(grid), dim3(kDecThreads), L.total,
@@ -584,12 +596,6 @@ int decode_slice(int64_t M, int64_t K, int r) {
 }  // namespace
 
 bool decode_fits(int64_t M, int64_t K) { return M <= 16 && K <= kDecMaxK; }
-
-// Up to 64 partials when one token's T is at most 64 values and X sits in LDS
-// (each workgroup reads all nz M r of them), else 32.
-int decode_max_t_partials(int64_t M, int64_t K, int r) {
-  return M * r <= 64 && decode_x_in_lds(M, K, r) ? kMaxDownPartials : kMaxDownPartials / 2;
-}
 
 bool decode_folds_t(int64_t M, int r) {
   return r > 0 && M * r <= kDecTFinMaxMR;

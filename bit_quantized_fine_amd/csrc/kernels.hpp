@@ -93,8 +93,6 @@ constexpr int kMaxDownPartials = 64;
 int lora_down_partial_count(int64_t K, int maxp);
 hipError_t launch_lora_down_partials(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A,
                                      int r, int maxp, float* ws, int* nz, hipStream_t stream);
-// The most T partial sums the decode kernel chosen for (M, K, r) adds up.
-int decode_max_t_partials(int64_t M, int64_t K, int r);
 
 // T[M,r] = X . A (fp32 out).
 hipError_t launch_lora_down(const uint16_t* X, int64_t M, int64_t K,

@@ -59,7 +59,7 @@ FWD_CASES = [
     (4, 96, 16384, 64, 0.25),        # T folded, X too large for LDS (read from global memory)
     (2, 64, 16384, 8, 0.5),          # X of exactly the LDS staging limit (64 KB); 64 T partials
     (1, 96, 16384 + 64 * 5, 64, 0.25),   # 33 T partial sums, ragged last 256-k slice
-    (1, 64, 32768, 64, 0.5),         # one token, X from global memory: at most 32 partials
+    (1, 64, 32768, 64, 0.5),         # one token, X from global memory: 64 partials added late
     (8, 264, 64 * 133, 16, 0.5),     # 8 tokens, X from global memory, ragged rows
     (12, 264, 64 * 133, 16, 0.5),    # X in K-slices, the last ragged (half a chunk), ragged rows
     (4, 96, 1024, 256, 0.25),        # M r = 1024: the most T values added after the main loop
