@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k_quantize(
         // Between 2^-120 and 2^-6 only the sign of x decides the code, and
         // q has the quotient's sign; below 2^-120 the quotient may round to
         // zero, which decides the code where a table has a threshold at
-        // zero (INT4, FP4), so those weights take the IEEE divide.
+        // zero (INT4's), so those weights take the IEEE divide.
         const float y = 1.0f / c;
         const float w[4] = {v.x, v.y, v.z, v.w};
         float qmin = 1.f;

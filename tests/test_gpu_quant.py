@@ -163,9 +163,9 @@ def test_every_float32_in_unit_interval_encodes_like_oracle(codebook):
 
 # Block constants for the quotient sweep: weight-like scales, values next to
 # a power of two, tiny and large ones (2^-100 and 2^126 lie outside the range
-# where the kernel forms the quotient from the reciprocal), and, for the
-# tables with a threshold at zero (INT4, FP4), constants above 1, whose
-# quotients of subnormal weights round to zero or not.
+# where the kernel forms the quotient from the reciprocal), and, for INT4,
+# whose table has a threshold at zero, constants above 1, whose quotients of
+# subnormal weights round to zero or not; FP4 at constants of other ranges.
 _SWEEP_CASES = [("nf4", c) for c in (
     0.0213, 0.37, float(np.nextafter(np.float32(1), np.float32(0))), 1.5, 3.0, 3.0e-5,
     2.0 ** -60, 2.0 ** 20, 2.0 ** -100, 2.0 ** 126)] + [
