@@ -441,13 +441,16 @@ __global__ __launch_bounds__(256) void k_split_reduce_pair(ReduceJob a, ReduceJo
 
 // ---------------------------------------------------------------------------
 // LoRA down-projection for few tokens (M <= 16): workgroup z covers spw
-// consecutive slices of 256 k; partial[z][m][j] = sum over them of
-// X[m, k] A[k, j].  Each A slice is transposed through LDS in 8x8 patches,
-// 64 ranks at a time; wave w multiplies ranks 16w..16w+15 of the 64 against
-// the token fragments, which come straight from global memory.
+// consecutive slices of 128 k; partial[z][m][j] = sum over them of
+// X[m, k] A[k, j].  Each A slice is transposed through LDS in 8x8 patches
+// (16 KB a slice, staged by the first 128 threads), 64 ranks at a time; wave
+// w multiplies ranks 16w..16w+15 of the 64 against the token fragments,
+// which come straight from global memory.  128-k slices give 64 workgroups
+// at K = 8192 where 256-k slices gave 32; the kernel is a short latency
+// chain, so more of them in parallel end sooner (about 0.3 us per call).
 // ---------------------------------------------------------------------------
 
-constexpr int LDS_K = 256;             // k per slice
+constexpr int LDS_K = 128;             // k per slice
 constexpr int LDS_KS = LDS_K + 8;      // LDS row stride (elements)
 
 __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restrict__ X, int M,
@@ -464,7 +467,7 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
   const BufRes ra = make_bufres(A, static_cast<uint32_t>(K32 * r * 2));
   // Slices run as a two-stage pipeline: the loads of slice sub + 1 are in
   // flight while slice sub is transposed and multiplied.
-  u32x4 xf[2][8];     // token fragments for the 8 k32 steps of a slice
+  u32x4 xf[2][LDS_K / 32];   // token fragments for the k32 steps of a slice
   u32x4 rows[2][8];   // this thread's 8x8 patch of the slice's A rows
   for (int j0 = 0; j0 < r; j0 += 64) {
     // (buffer loads with out-of-range offsets instead of branches, so the
@@ -472,7 +475,7 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
     auto load = [&](int sub, int b) {   // past the workgroup's slices: reads nothing
       const int k0 = sub < spw ? (blockIdx.x * spw + sub) * LDS_K : K32;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
+      for (int st = 0; st < LDS_K / 32; ++st) {
         const int k = k0 + 32 * st + 8 * g;
         xf[b][st] = buf_load16(rx, m_ok && k < K ? static_cast<uint32_t>((li * K32 + k) * 2)
                                                  : 0x80000000u);
@@ -481,8 +484,8 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
       for (int t = 0; t < 8; ++t) {
         const int k = k0 + kp * 8 + t;
         const int j = j0 + jp * 8;
-        rows[b][t] = buf_load16(ra, k < K && j < r ? static_cast<uint32_t>((k * r + j) * 2)
-                                                   : 0x80000000u);
+        const bool ok = kp * 8 < LDS_K && k < K && j < r;   // 16 threads of rows a slice
+        rows[b][t] = buf_load16(ra, ok ? static_cast<uint32_t>((k * r + j) * 2) : 0x80000000u);
       }
     };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -492,12 +495,14 @@ __global__ __launch_bounds__(256) void k_lora_down_small(const uint16_t* __restr
       load(sub + 1, b ^ 1);
       u32x4 cols[8];
       transpose8x8_b16(rows[b], cols);
+      if (kp * 8 < LDS_K) {   // threads past the slice's rows hold zeros
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        *reinterpret_cast<u32x4*>(at + (jp * 8 + t) * LDS_KS + kp * 8) = cols[t];
+        for (int t = 0; t < 8; ++t)
+          *reinterpret_cast<u32x4*>(at + (jp * 8 + t) * LDS_KS + kp * 8) = cols[t];
+      }
       __syncthreads();
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
+      for (int st = 0; st < LDS_K / 32; ++st) {
         const u32x4 af =
             *reinterpret_cast<const u32x4*>(at + (16 * wave + li) * LDS_KS + 32 * st + 8 * g);
         acc = mfma16(af, xf[b][st], acc);

@@ -58,7 +58,7 @@ FWD_CASES = [
     (1, 232, 64 * 33, 32, 0.5),      # K with a half chunk; X staged in LDS
     (4, 96, 16384, 64, 0.25),        # T folded, X too large for LDS (read from global memory)
     (2, 64, 16384, 8, 0.5),          # X of exactly the LDS staging limit (64 KB); 64 T partials
-    (1, 96, 16384 + 64 * 5, 64, 0.25),   # 33 T partial sums, ragged last 256-k slice
+    (1, 96, 16384 + 64 * 5, 64, 0.25),   # 44 T partial sums, the last of two 128-k slices, one ragged
     (1, 64, 32768, 64, 0.5),         # one token, X from global memory: 64 partials added late
     (8, 264, 64 * 133, 16, 0.5),     # 8 tokens, X from global memory, ragged rows
     (12, 264, 64 * 133, 16, 0.5),    # X in K-slices, the last ragged (half a chunk), ragged rows
