@@ -8,7 +8,8 @@
 // dequantize the tile's 128 x 64 weights once into one of two LDS buffers,
 // while the waves multiply the other buffer.  Wave w owns tokens
 // 64 (w % 4) .. +63 and all 128 rows, and the 32-k half (w / 4) of every
-// chunk; the two halves' accumulators are added through LDS at the end.
+// chunk; the two halves' accumulators are added through LDS at the end, each
+// half receiving and storing four of the eight row subtiles.
 // Splitting the chunk's two 32-k steps between two waves puts two waves on
 // every SIMD (128 accumulator registers each).
 //
@@ -267,6 +268,20 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
     const float* Tt = T + (p0 / seg_rows) * r;
     uint16_t* bt = As;
     for (int j0 = 0; j0 < r; j0 += 64) {
+      // this wave's s.T operands, loaded before the B^T staging so that the
+      // two loads' latencies overlap
+      const int jt = j0 + 32 * ks + 8 * g;
+      f32x4 traw[GTB][2];
+      bool tok[GTB];
+#pragma unroll
+      for (int b = 0; b < GTB; ++b) {
+        const int64_t m = q0 + 64 * wt + 16 * b + li;
+        const bool ok = m < M && jt < r;
+        tok[b] = ok;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        traw[b][0] = ok ? *reinterpret_cast<const f32x4*>(Tt + m * ldt + jt) : zero;
+        traw[b][1] = ok ? *reinterpret_cast<const f32x4*>(Tt + m * ldt + jt + 4) : zero;
+      }
       if (tid < GP) {   // patch tid: rows 8 (tid % 16) .., ranks j0 + 8 (tid / 16) ..
         const int rp = tid % (GP / 8), kp = tid / (GP / 8);
         const int64_t n = p0 + rp * 8;
@@ -286,15 +301,12 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
       {
         const int i = ks;
         {
-          const int j = j0 + 32 * i + 8 * g;
           u32x4 th[GTB], tl[GTB];
 #pragma unroll
           for (int b = 0; b < GTB; ++b) {
-            const int64_t m = q0 + 64 * wt + 16 * b + li;
             uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
-            if (m < M && j < r) {
-              const f32x4 t0 = *reinterpret_cast<const f32x4*>(Tt + m * ldt + j);
-              const f32x4 t1 = *reinterpret_cast<const f32x4*>(Tt + m * ldt + j + 4);
+            if (tok[b]) {
+              const f32x4 t0 = traw[b][0], t1 = traw[b][1];
               const float v[8] = {t0.x * s, t0.y * s, t0.z * s, t0.w * s,
                                   t1.x * s, t1.y * s, t1.z * s, t1.w * s};
 #pragma unroll
@@ -319,34 +331,42 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
     }
   }
 
-  // Add the second k half into the first: waves ks = 1 hand their
-  // accumulators over through LDS, half of the row subtiles at a time.
-  f32x4* xch = reinterpret_cast<f32x4*>(dyn);   // [GWT][GTA/2][GTB][64]
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (ks == 1) {
-#pragma unroll
-      for (int a = 0; a < GTA / 2; ++a)
-#pragma unroll
-        for (int b = 0; b < GTB; ++b)
-          xch[((wt * (GTA / 2) + a) * GTB + b) * 64 + lane] = acc[h * (GTA / 2) + a][b];
-    }
-    __syncthreads();
-    if (ks == 0) {
+  // Add the two k halves: wave ks keeps row subtiles 4 ks .. 4 ks + 3 and
+  // receives them from its partner (the other ks, same token group) through
+  // LDS, in one round; each half then stores its own row subtiles.
+  f32x4* xch = reinterpret_cast<f32x4*>(dyn);   // [2][GWT][GTA/2][GTB][64]
+  {
+    // (compile-time accumulator indices on both sides of a scalar branch)
+    auto hand = [&](auto kc) {
+      constexpr int K0 = decltype(kc)::value, GIVE = 1 - K0;
 #pragma unroll
       for (int a = 0; a < GTA / 2; ++a)
 #pragma unroll
         for (int b = 0; b < GTB; ++b)
-          acc[h * (GTA / 2) + a][b] += xch[((wt * (GTA / 2) + a) * GTB + b) * 64 + lane];
-    }
+          xch[(((GIVE * GWT + wt) * (GTA / 2) + a) * GTB + b) * 64 + lane] =
+              acc[GIVE * (GTA / 2) + a][b];
+    };
+    auto take = [&](auto kc) {
+      constexpr int K0 = decltype(kc)::value;
+#pragma unroll
+      for (int a = 0; a < GTA / 2; ++a)
+#pragma unroll
+        for (int b = 0; b < GTB; ++b)
+          acc[K0 * (GTA / 2) + a][b] +=
+              xch[(((K0 * GWT + wt) * (GTA / 2) + a) * GTB + b) * 64 + lane];
+    };
+    if (ks == 0) hand(std::integral_constant<int, 0>{}); else hand(std::integral_constant<int, 1>{});
     __syncthreads();
+    if (ks == 0) take(std::integral_constant<int, 0>{}); else take(std::integral_constant<int, 1>{});
   }
 
   // Y[m, n..n+3] for the lane's 4 consecutive rows n of each subtile (bf16),
   // or this split's fp32 partial sums part[z][m][n..n+3]
-  if (ks == 0) {
+  auto store = [&](auto kc) {
+    constexpr int K0 = decltype(kc)::value;
 #pragma unroll
-    for (int a = 0; a < GTA; ++a) {
+    for (int a0 = 0; a0 < GTA / 2; ++a0) {
+      const int a = K0 * (GTA / 2) + a0;
       const int64_t n = p0 + 16 * a + 4 * g;
 #pragma unroll
       for (int b = 0; b < GTB; ++b) {
@@ -362,7 +382,8 @@ __global__ __launch_bounds__(GT) void k_fwd_gemm(
         }
       }
     }
-  }
+  };
+  if (ks == 0) store(std::integral_constant<int, 0>{}); else store(std::integral_constant<int, 1>{});
 }
 
 GemmSplit fwd_gemm_split(int64_t M, int64_t N, int64_t K) {
